@@ -1,0 +1,379 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Every check takes the oracle namespace `O` as an argument, so that the mutant
+tests can run the same checks against oracles with a planted mistake and
+confirm that each mistake is caught. Sources of truth used here:
+
+  * hand-derived fixtures under tests/golden/ (each cites its passage);
+  * brute-force enumeration written independently of the oracle's index math;
+  * closed forms (Q = 0, one-hot values, two-key softmax);
+  * library routines (torch scaled_dot_product_attention / logsumexp on CPU,
+    numpy float64 dot products);
+  * the pages' relations: the Z / Z_hat renormalisation of kept keys and the
+    log-sum-exp potential (Theoretical Rationale 1, "Softmax Geometry"), the
+    Bhatia-Davis bound (Theoretical Rationale 2, "Tile Statistics").
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _bf16_vals(rng, shape, scale=1.0):
+    """Random bf16-representable float32 values (truncation of random floats)."""
+    x = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+
+
+# ------------------------------------------------------------------ O1 / O7
+
+def brute_force_positions(grid, tile):
+    """Enumerate boxes in raster order of box coordinates and slots in raster
+    order inside each box, handing out consecutive tiled positions; record
+    which raster token (if any) sits at each position."""
+    T, H, W = grid
+    pt, ph, pw = tile
+    nTt, nTh, nTw = -(-T // pt), -(-H // ph), -(-W // pw)
+    pos = {}
+    p = 0
+    for bt in range(nTt):
+        for by in range(nTh):
+            for bx in range(nTw):
+                for st in range(pt):
+                    for sy in range(ph):
+                        for sx in range(pw):
+                            t, y, x = bt * pt + st, by * ph + sy, bx * pw + sx
+                            if t < T and y < H and x < W:
+                                pos[(t * H + y) * W + x] = p
+                            p += 1
+    return np.array([pos[n] for n in range(T * H * W)]), p
+
+
+def check_permutation_golden(O):
+    g = _golden("permutation_grid2x3x4_tile1x2x2.json")
+    grid, tile = tuple(g["grid"]), tuple(g["tile"])
+    assert O.num_tiles(grid, tile) == g["num_tiles"]
+    assert list(O.tiled_position(grid, tile)) == g["tiled_position_of_raster_token"]
+    x = np.arange(1, 25, dtype=np.float32)[:, None]
+    xt, valid = O.tile_permute(x, grid, tile)
+    assert sorted(np.flatnonzero(~valid).tolist()) == g["pad_slots"]
+    assert np.all(xt[~valid] == 0)
+
+
+def check_permutation_bruteforce(O, shapes):
+    for grid, tile in shapes:
+        want, total = brute_force_positions(grid, tile)
+        got = O.tiled_position(grid, tile)
+        assert O.num_tiles(grid, tile) * tile[0] * tile[1] * tile[2] == total
+        assert np.array_equal(got, want), (grid, tile)
+        # bijection onto the valid slots, inverse, pad count
+        N = grid[0] * grid[1] * grid[2]
+        x = np.arange(N, dtype=np.int64)[:, None] + 1
+        xt, valid = O.tile_permute(x, grid, tile)
+        assert valid.sum() == N and len(np.unique(got)) == N
+        assert (~valid).sum() == total - N
+        assert np.array_equal(O.tile_unpermute(xt, grid, tile), x)
+
+
+# ------------------------------------------------------------------ O2
+
+def check_trippool_golden(O):
+    g = _golden("trippool_slot_order.json")
+    for case in g["cases"]:
+        vals = np.array(case["values"], dtype=np.float32)
+        n = len(vals)
+        vol = 8                                   # pad the box: only n slots are real
+        xt = np.zeros((vol, 1), dtype=np.float32)
+        xt[:n, 0] = vals
+        valid = np.zeros(vol, dtype=bool)
+        valid[:n] = True
+        st = O.trippool(xt, valid, vol)[0]
+        for got, key in zip(st, ("avg", "max", "min")):
+            want = np.float32(case[key])
+            assert got == want and np.signbit(got) == np.signbit(want), (case["comment"], key, got, want)
+
+
+def check_trippool_bruteforce(O, grid, tile, d=6, seed=0):
+    """Gather each box's real tokens straight from raster coordinates and check
+    the statistics against their definitions."""
+    rng = np.random.default_rng(seed)
+    T, H, W = grid
+    pt, ph, pw = tile
+    vol = pt * ph * pw
+    x = _bf16_vals(rng, (T * H * W, d), 2.0)
+    xt, valid = O.tile_permute(x, grid, tile)
+    st = O.trippool(xt, valid, vol)
+    nTt, nTh, nTw = -(-T // pt), -(-H // ph), -(-W // pw)
+    tau = 0
+    for bt in range(nTt):
+        for by in range(nTh):
+            for bx in range(nTw):
+                rows = []
+                for t in range(bt * pt, min(T, bt * pt + pt)):
+                    for y in range(by * ph, min(H, by * ph + ph)):
+                        for xx in range(bx * pw, min(W, bx * pw + pw)):
+                            rows.append(x[(t * H + y) * W + xx])
+                g = np.array(rows, dtype=np.float64)
+                mean = g.mean(axis=0)
+                M, m = g.max(axis=0), g.min(axis=0)
+                avg, mx, mn = st[tau, :d], st[tau, d:2 * d], st[tau, 2 * d:]
+                assert np.array_equal(mx, M.astype(np.float32)) and np.array_equal(mn, m.astype(np.float32))
+                assert np.all(mn <= avg) and np.all(avg <= mx)
+                # float32 sum error + one bf16 rounding (relative 2^-8)
+                err = 1.01 * len(rows) * 2.0 ** -24 * np.abs(g).sum(axis=0) / len(rows)
+                assert np.all(np.abs(avg - mean) <= err + np.abs(mean) * 2.0 ** -8 + 1e-30)
+                # Bhatia-Davis (Tile Statistics): var <= (M - mu)(mu - m)
+                var = g.var(axis=0)
+                assert np.all(var <= (M - mean) * (mean - m) * (1 + 1e-12) + 1e-12)
+                tau += 1
+
+
+def check_trippool_constant(O):
+    xt = np.full((16, 3), np.float32(0.375))
+    valid = np.ones(16, dtype=bool)
+    valid[11:] = False
+    xt[11:] = 0
+    st = O.trippool(xt, valid, 16)[0]
+    assert np.all(st == np.float32(0.375))
+
+
+# ------------------------------------------------------------------ O3 / O4
+
+def check_dot_golden(O):
+    g = _golden("fp32_dot_order.json")
+    for case in g["cases"]:
+        a = np.array([case["a"]], dtype=np.float32)
+        b = np.array(case["b"], dtype=np.float32)[:, None]
+        got = O.fp32_dot_rows(a, b)[0, 0]
+        assert got == np.float32(case["result"]), case["comment"]
+
+
+def check_dot_error_bound(O, seed=1):
+    """|fl32 sum - exact| <= gamma_n * sum |a_c b_c| (Higham's bound for a
+    recursive sum of exact products), against a float64 (exact here) dot."""
+    rng = np.random.default_rng(seed)
+    for n in (1, 7, 64, 384):
+        a = _bf16_vals(rng, (9, n), 3.0)
+        b = _bf16_vals(rng, (n, 5), 0.05)
+        got = O.fp32_dot_rows(a, b).astype(np.float64)
+        exact = a.astype(np.float64) @ b.astype(np.float64)
+        u = 2.0 ** -24
+        gam = n * u / (1 - n * u)
+        bound = gam * (np.abs(a).astype(np.float64) @ np.abs(b).astype(np.float64))
+        assert np.all(np.abs(got - exact) <= bound)
+
+
+def check_projection_rounds_to_bf16(O, seed=2):
+    rng = np.random.default_rng(seed)
+    st = _bf16_vals(rng, (11, 24))
+    w = _bf16_vals(rng, (24, 8), 0.2)
+    p = O.project(st, w)
+    assert np.all((p.view(np.uint32) & np.uint32(0xFFFF)) == 0)
+    exact = st.astype(np.float64) @ w.astype(np.float64)
+    assert np.all(np.abs(p - exact) <= np.abs(exact) * 2.0 ** -8 + 24 * 2.0 ** -24 * (np.abs(st) @ np.abs(w)) * 2)
+
+
+def check_average_pooling_special_case(O, seed=3):
+    """With W = [I_r; 0; 0] the estimator reduces to the average-pooling score
+    (the mean-only baseline the pages compare against), a plain dot product
+    of the tile means."""
+    rng = np.random.default_rng(seed)
+    grid, tile, d, r = (2, 4, 8), (1, 2, 4), 8, 4
+    vol = 8
+    q = _bf16_vals(rng, (64, d))
+    k = _bf16_vals(rng, (64, d))
+    qt, valid = O.tile_permute(q, grid, tile)
+    kt, _ = O.tile_permute(k, grid, tile)
+    W = np.zeros((3 * d, r), dtype=np.float32)
+    W[np.arange(r), np.arange(r)] = 1.0
+    S = O.tile_scores(O.project(O.trippool(qt, valid, vol), W), O.project(O.trippool(kt, valid, vol), W))
+    mq = qt.reshape(-1, vol, d).astype(np.float64).mean(axis=1)[:, :r]
+    mk = kt.reshape(-1, vol, d).astype(np.float64).mean(axis=1)[:, :r]
+    want = mq @ mk.T
+    # two bf16 roundings of the means (2^-8 relative each) and a float32 dot
+    tol = 3 * 2.0 ** -8 * (np.abs(mq) @ np.abs(mk).T) + 1e-6
+    assert np.all(np.abs(S - want) <= tol)
+
+
+# ------------------------------------------------------------------ O5
+
+def check_topk_golden(O):
+    g = _golden("topk_ties.json")
+    S = np.array([g["scores"]], dtype=np.float32)
+    for case in g["cases"]:
+        idx = O.topk(S, case["k"])
+        assert idx[0].tolist() == case["idx"], case
+        assert O.bitmask(idx, S.shape[1])[0].tolist() == case["bitmask"], case
+        assert O.topk_row_bruteforce(S[0], case["k"]) == case["idx"]
+
+
+def check_topk_bruteforce(O, seed=4):
+    rng = np.random.default_rng(seed)
+    for n, k in ((1, 1), (5, 3), (33, 7), (70, 70), (129, 10)):
+        S = rng.integers(-3, 4, size=(6, n)).astype(np.float32) * np.float32(0.5)
+        S[S == 0] = np.where(rng.random((S == 0).sum()) < 0.5, np.float32(-0.0), np.float32(0.0))
+        S[-1] = rng.standard_normal(n).astype(np.float32)
+        idx = O.topk(S, k)
+        for r in range(S.shape[0]):
+            row = [float(v) for v in S[r]]
+            # independent brute force: repeatedly take the best remaining
+            left = list(range(n))
+            keep = []
+            for _ in range(k):
+                best = left[0]
+                for j in left[1:]:
+                    if row[j] > row[best]:
+                        best = j
+                keep.append(best)
+                left.remove(best)
+            assert idx[r].tolist() == sorted(keep), (n, k, r)
+        if k < n:
+            small = O.topk(S, k - 1) if k > 1 else np.zeros((S.shape[0], 0), dtype=np.int64)
+            for r in range(S.shape[0]):
+                assert set(small[r].tolist()) <= set(idx[r].tolist())
+
+
+# ------------------------------------------------------------------ O6
+
+def check_attention_two_keys(O):
+    """Closed form: logits (0, 2) give p = (1/(1+e^2), e^2/(1+e^2)) and
+    LSE = log(1 + e^2)."""
+    grid, tile = (1, 1, 4), (1, 1, 2)
+    q = np.zeros((4, 4))
+    q[:, 0] = 2.0                                   # scale 1/sqrt(4): u = q.k / 2
+    k = np.array([[0, 0, 0, 0], [1, 0, 0, 0], [0, 1, 0, 0], [2, 0, 0, 0]], dtype=np.float64)
+    v = np.array([[5, 5, 5, 5], [7, 7, 7, 7], [1, 0, 0, 0], [0, 1, 0, 0]], dtype=np.float64)
+    sel = np.array([[1], [1]])
+    o, lse = O.sparse_attention(q, k, v, grid, tile, sel, 0.5)
+    p0 = 1.0 / (1.0 + math.exp(2.0))
+    want = np.array([p0, 1 - p0, 0, 0])
+    assert np.allclose(o, want[None, :], rtol=0, atol=1e-14)
+    assert np.allclose(lse, math.log(1 + math.exp(2.0)), rtol=0, atol=1e-14)
+
+
+def check_attention_dense_matches_sdpa(O, seed=5):
+    """Keeping every tile gives plain softmax attention; compare with torch's
+    scaled_dot_product_attention and logsumexp in float64 on the CPU."""
+    import torch
+    rng = np.random.default_rng(seed)
+    grid, tile, d = (2, 3, 8), (1, 2, 4), 16          # padded: 8 boxes of 8, 48 tokens
+    N = 48
+    q, k, v = (_bf16_vals(rng, (N, d)) for _ in range(3))
+    nT = O.num_tiles(grid, tile)
+    sel = np.tile(np.arange(nT), (nT, 1))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = O.sparse_attention(q, k, v, grid, tile, sel, scale)
+    tq, tk, tv = (torch.from_numpy(a.astype(np.float64))[None, None] for a in (q, k, v))
+    want = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)[0, 0].numpy()
+    want_lse = torch.logsumexp((tq @ tk.transpose(-1, -2))[0, 0] * scale, dim=-1).numpy()
+    assert np.max(np.abs(o - want)) < 1e-12
+    assert np.max(np.abs(lse - want_lse)) < 1e-12
+    od, lsed = O.dense_attention(q, k, v, scale)
+    assert np.max(np.abs(od - want)) < 1e-12 and np.max(np.abs(lsed - want_lse)) < 1e-12
+
+
+def _random_sel(rng, nT, k):
+    return np.sort(np.stack([rng.choice(nT, size=k, replace=False) for _ in range(nT)]), axis=1)
+
+
+def check_attention_renormalisation(O, seed=6):
+    """With V = identity the output row is the probability row itself. Kept
+    keys then satisfy P_sparse = P_dense * Z / Z_hat, and Z / Z_hat =
+    exp(LSE_dense - LSE_sparse) >= 1 (Softmax Geometry)."""
+    rng = np.random.default_rng(seed)
+    grid, tile = (2, 2, 6), (1, 2, 2)                  # 24 tokens, 6 boxes of 4
+    N, d = 24, 8
+    q = _bf16_vals(rng, (N, d))
+    k = _bf16_vals(rng, (N, d))
+    v = np.eye(N)
+    nT = O.num_tiles(grid, tile)
+    scale = 1.0 / math.sqrt(d)
+    sel = _random_sel(rng, nT, 2)
+    ps, lses = O.sparse_attention(q, k, v, grid, tile, sel, scale)
+    pd, lsed = O.dense_attention(q, k, v, scale)
+    assert np.allclose(ps.sum(axis=1), 1.0, atol=1e-12)
+    ratio = np.exp(lsed - lses)
+    assert np.all(ratio >= 1.0 - 1e-12) and np.all(lses <= lsed + 1e-12)
+    tile_of = O.tiled_position(grid, tile) // 4
+    for n in range(N):
+        kept = np.isin(tile_of, sel[tile_of[n]])
+        assert np.allclose(ps[n, kept], pd[n, kept] * ratio[n], rtol=1e-10, atol=1e-15)
+        assert np.all(ps[n, ~kept] == 0)
+
+
+def check_attention_zero_query(O, seed=7):
+    """Q = 0 makes every logit 0, so each output is the plain mean of the real
+    value rows in the selected tiles (pad slots must not count)."""
+    rng = np.random.default_rng(seed)
+    grid, tile = (3, 3, 5), (2, 2, 2)                  # heavily padded
+    N, d = 45, 4
+    q = np.zeros((N, d))
+    k = _bf16_vals(rng, (N, d))
+    v = _bf16_vals(rng, (N, d))
+    nT = O.num_tiles(grid, tile)
+    sel = _random_sel(rng, nT, 3)
+    o, lse = O.sparse_attention(q, k, v, grid, tile, sel, 0.5)
+    T, H, W = grid
+    for n in range(N):
+        t, y, x = n // (H * W), (n // W) % H, n % W
+        my = ((t // 2) * 2 + y // 2) * 3 + x // 2         # box of token n, computed directly
+        rows = []
+        for m in range(N):
+            tm, ym, xm = m // (H * W), (m // W) % H, m % W
+            if ((tm // 2) * 2 + ym // 2) * 3 + xm // 2 in sel[my]:
+                rows.append(v[m])
+        assert np.allclose(o[n], np.mean(rows, axis=0), atol=1e-12)
+        assert abs(lse[n] - math.log(len(rows))) < 1e-12
+
+
+def check_attention_monotone_and_bounded(O, seed=8):
+    rng = np.random.default_rng(seed)
+    grid, tile = (2, 4, 4), (1, 2, 4)                 # 4 boxes of 8
+    N, d = 32, 8
+    q, k, v = (_bf16_vals(rng, (N, d), 2.0) for _ in range(3))
+    nT = O.num_tiles(grid, tile)
+    S = rng.standard_normal((nT, nT)).astype(np.float32)
+    prev = None
+    for kk in range(1, nT + 1):
+        sel = O.topk(S, kk)
+        o, lse = O.sparse_attention(q, k, v, grid, tile, sel, 0.3)
+        if prev is not None:
+            assert np.all(lse >= prev - 1e-12)
+        prev = lse
+        tile_of = O.tiled_position(grid, tile) // 8
+        for n in range(N):
+            rows = v[np.isin(tile_of, sel[tile_of[n]])]
+            assert np.all(o[n] <= rows.max(axis=0) + 1e-12) and np.all(o[n] >= rows.min(axis=0) - 1e-12)
+
+
+ALL_SMALL_CHECKS = [
+    check_permutation_golden,
+    lambda O: check_permutation_bruteforce(O, [((2, 3, 4), (1, 2, 2)), ((4, 16, 16), (2, 8, 8)),
+                                               ((5, 7, 9), (2, 2, 4)), ((3, 9, 17), (1, 8, 16)),
+                                               ((9, 5, 5), (8, 4, 4))]),
+    check_trippool_golden,
+    lambda O: check_trippool_bruteforce(O, (3, 5, 6), (2, 2, 4)),
+    check_trippool_constant,
+    check_dot_golden,
+    check_dot_error_bound,
+    check_projection_rounds_to_bf16,
+    check_average_pooling_special_case,
+    check_topk_golden,
+    check_topk_bruteforce,
+    check_attention_two_keys,
+    check_attention_dense_matches_sdpa,
+    check_attention_renormalisation,
+    check_attention_zero_query,
+    check_attention_monotone_and_bounded,
+]
