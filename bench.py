@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of one Veda tile-sparse attention layer on one MI355X.
+
+A step is the whole layer on one batch of seeded synthetic input already
+resident in HBM: tile permute of Q, K and V; TripPool estimator (stats,
+projections, tile scores); head-aware Top-k; tile-skipping attention forward;
+tile unpermute of O. Default workload: 245,760 tokens (64x48x80 latents),
+40 heads, d = 128, tile (4,4,8) -> 1920 tiles, k = 96 (95% sparse).
+
+Prints one JSON line: ms per layer (the value), the attention kernel's
+effective TFLOP/s against the bf16 MFMA peak (roofline), per-stage times
+from HIP events on the launch stream, and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attention_flops(w) -> float:
+    """Whole 128x128 tile pairs on the selected tiles, QK^T and PV, 2 flop per MAC."""
+    pairs = sum(n * k for n, k in zip(w.tiles_per_head(), w.k_per_head())) * w.B
+    return 4.0 * w.d * 128 * 128 * pairs
+
+
+def stage_bytes(w) -> dict:
+    """Algorithmic HBM bytes per stage (each input read once, each output written once)."""
+    N, Hh, d, B = w.tokens, w.heads, w.d, w.B
+    nT = max(w.tiles_per_head())
+    raster = B * N * Hh * d * 2
+    tiled = B * Hh * nT * 128 * d * 2
+    stats = B * Hh * nT * 3 * d * 2
+    feats = B * Hh * nT * w.r * 2
+    scores = B * Hh * nT * nT * 4
+    kmax = max(w.k_per_head())
+    idx = B * Hh * nT * kmax * 4 + B * Hh * nT * ((nT + 31) // 32) * 4
+    return {
+        "permute_x3": 3 * (raster + tiled),
+        "trippool_score": 2 * tiled + 2 * stats + 2 * feats + scores + 2 * Hh * 3 * d * w.r * 2,
+        "topk": scores + idx,
+        "unpermute": tiled + raster,
+    }
+
+
+def cpu_baseline(w, data, sample_tiles: int, seconds_hint: float = 20.0):
+    """The oracle as it stands, timed on this host: head 0's mask preparation
+    in full plus attention for `sample_tiles` query tiles of head 0, scaled
+    to a whole layer (all query tiles, all heads)."""
+    import numpy as np
+    import oracle as O
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        threads = 1
+    hd = 0
+    tile = w.head_tiles()[hd]
+    nT = w.tiles_per_head()[hd]
+    k = w.k_per_head()[hd]
+    q, kk, v = (O.bf16_bits_to_float(data[n][0, :, hd, :]) for n in ("q", "k", "v"))
+    wq, wk = (O.bf16_bits_to_float(data[n][hd]) for n in ("wq", "wk"))
+    t0 = time.perf_counter()
+    qt, valid = O.tile_permute(q, w.grid, tile)
+    kt, _ = O.tile_permute(kk, w.grid, tile)
+    vt, _ = O.tile_permute(v, w.grid, tile)
+    fq = O.project(O.trippool(qt, valid), wq)
+    fk = O.project(O.trippool(kt, valid), wk)
+    S = O.tile_scores(fq, fk)
+    idx = O.topk(S, k)
+    t_prep = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    tiles = sorted(rng.choice(nT, size=min(nT, sample_tiles), replace=False).tolist())
+    t0 = time.perf_counter()
+    o, lse = O.sparse_attention(q, kk, v, w.grid, tile, idx, 1.0 / math.sqrt(w.d), query_tiles=tiles)
+    t_attn = time.perf_counter() - t0
+    ms_layer = (t_prep + t_attn / len(tiles) * nT) * w.heads * w.B * 1e3
+    return {
+        "value": round(ms_layer, 1), "unit": "ms/layer", "cores": int(threads), "kind": "oracle",
+        "sample": (f"head 0 of {w.heads}: full mask preparation ({t_prep:.1f} s) + attention of "
+                   f"{len(tiles)} of {nT} query tiles ({t_attn:.1f} s), scaled to {nT} tiles x {w.heads} heads"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long")
+    ap.add_argument("--heads", type=int, default=0, help="run only the first N heads (0 = all)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tiles", type=int, default=24)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the layer shards by head with no communication, "
+              "and multi-GPU runs are not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_13_amd as V
+    import datagen
+
+    w = datagen.WORKLOADS[args.workload]
+    if args.heads:
+        w = w.with_heads(args.heads)
+    log(f"[bench] workload {w.name}: {w.description}")
+    t0 = time.perf_counter()
+    data = datagen.generate(w)
+    log(f"[bench] generated inputs in {time.perf_counter() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(dev)
+    q, k, v, wq, wk = (to(data[n]) for n in ("q", "k", "v", "wq", "wk"))
+    geom = V.Geometry(w.B, w.heads, w.d, w.grid, w.head_tiles())
+    ks = w.k_per_head()
+    stream = torch.cuda.current_stream(dev)
+
+    bufs = V.layer_forward(q, k, v, wq, wk, geom, ks)  # allocates every buffer once
+    torch.cuda.synchronize()
+    log("[bench] first layer done")
+
+    stages = ["permute_x3", "trippool_score", "topk", "sparse_attn", "unpermute"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        V.tile_permute(q, geom, bufs["q_t"])
+        V.tile_permute(k, geom, bufs["k_t"])
+        V.tile_permute(v, geom, bufs["v_t"])
+        if ev is not None:
+            ev[1].record(stream)
+        V.trippool_score(bufs["q_t"], bufs["k_t"], wq, wk, geom,
+                         {n: bufs[n] for n in ("stats_q", "stats_k", "feat_q", "feat_k", "scores")})
+        if ev is not None:
+            ev[2].record(stream)
+        V.topk_mask(bufs["scores"], geom, ks, idx=bufs["idx"], bitmask=bufs["bitmask"])
+        if ev is not None:
+            ev[3].record(stream)
+        V.sparse_attn_fwd(bufs["q_t"], bufs["k_t"], bufs["v_t"], bufs["idx"], geom, ks,
+                          o_t=bufs["o_t"], lse=bufs["lse"])
+        if ev is not None:
+            ev[4].record(stream)
+        V.tile_unpermute(bufs["o_t"], geom, bufs["o"])
+        if ev is not None:
+            ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per_stage = {name: [] for name in stages}
+    total = []
+    for ev in events:
+        for i, name in enumerate(stages):
+            per_stage[name].append(ev[i].elapsed_time(ev[i + 1]))
+        total.append(ev[0].elapsed_time(ev[5]))
+    ms_step = float(np.mean(total))
+    stage_ms = {n: round(float(np.mean(v)), 4) for n, v in per_stage.items()}
+    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/layer (wall {wall / args.steps * 1e3:.3f} ms); {stage_ms}")
+
+    f_attn = attention_flops(w)
+    t_attn = stage_ms["sparse_attn"] * 1e-3
+    achieved = f_attn / t_attn / 1e12
+    sb = stage_bytes(w)
+    hbm = {n: round(sb[n] / (stage_ms[n] * 1e-3) / 1e9, 1) for n in sb}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(w, data, args.cpu_sample_tiles)
+        log(f"[bench] cpu baseline: {cpu}")
+
+    line = {
+        "metric": "ms/layer + effective sparse-attn TFLOP/s (% bf16 MFMA peak) at 245K tok, 95% sparse",
+        "value": round(ms_step, 3),
+        "unit": "ms/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded low-frequency 3D field + N(0,1) noise, random-init projections)",
+        "config": {"workload": w.description, "tokens": w.tokens, "heads": w.heads, "head_dim": w.d,
+                   "tiles_per_head": max(w.tiles_per_head()), "k": max(w.k_per_head()), "rank": w.r},
+        "attn_tflops": round(achieved, 1),
+        "attn_frac_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "stage_ms": stage_ms,
+        "stage_hbm_gbs": hbm,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "sparse_attn_fwd_kernel<128>", "flops_per_launch": f_attn},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

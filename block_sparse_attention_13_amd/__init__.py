@@ -1,0 +1,228 @@
+"""Veda tile-sparse self-attention forward on AMD MI355X (gfx950).
+
+Python face of libveda.so. Each function allocates its outputs with torch on
+the inputs' device, passes raw pointers and torch's current HIP stream to the
+C ABI, and raises VedaError on a non-zero status. No computation happens in
+Python: the five steps of the layer are HIP kernels.
+
+  tile_permute     raster [B, N, heads, d] -> tiled [B, heads, nT_max, 128, d]
+  trippool_score   tiled Q, K + W_q, W_k  -> stats, features, tile scores
+  topk_mask        scores -> ascending index lists (+ bitmask) per query tile
+  sparse_attn_fwd  tiled Q, K, V + index lists -> tiled O (+ LSE)
+  tile_unpermute   tiled -> raster
+  layer_forward    the five calls in order
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import VedaError
+
+__all__ = ["Geometry", "VedaError", "tile_permute", "tile_unpermute", "trippool_score", "topk_mask",
+           "sparse_attn_fwd", "layer_forward", "TILE_TOKENS"]
+
+TILE_TOKENS = _lib.VEDA_TILE_TOKENS
+
+
+@dataclasses.dataclass
+class Geometry:
+    """Batch, heads, head dim, latent grid (T, H, W) and one tile shape per head."""
+    B: int
+    n_heads: int
+    head_dim: int
+    grid: Tuple[int, int, int]
+    head_tiles: Sequence[Tuple[int, int, int]]
+
+    def __post_init__(self):
+        if len(self.head_tiles) != self.n_heads:
+            raise ValueError("need one tile shape per head")
+        self._tiles = (_lib.VedaTile * self.n_heads)(*[_lib.VedaTile(*map(int, t)) for t in self.head_tiles])
+        self._c = _lib.VedaGeom(int(self.B), int(self.n_heads), int(self.head_dim), _lib.VedaGrid(*map(int, self.grid)),
+                                self._tiles)
+
+    @property
+    def c(self):
+        return self._c
+
+    @property
+    def tokens(self) -> int:
+        T, H, W = self.grid
+        return T * H * W
+
+    def num_tiles(self, head: int) -> int:
+        return _lib.check(_lib.lib.veda_num_tiles(self._c, int(head)), "veda_num_tiles")
+
+    def max_tiles(self) -> int:
+        return _lib.check(_lib.lib.veda_max_tiles(self._c), "veda_max_tiles")
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, dtype, shape=None, name="tensor"):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _raster_strides(x: torch.Tensor, geom: Geometry, name: str):
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be a bf16 device tensor")
+    if tuple(x.shape) != (geom.B, geom.tokens, geom.n_heads, geom.head_dim):
+        raise ValueError(f"{name} must have shape [B, N, heads, d] = "
+                         f"{(geom.B, geom.tokens, geom.n_heads, geom.head_dim)}, got {tuple(x.shape)}")
+    if x.stride(3) != 1:
+        raise ValueError(f"{name} must have unit channel stride")
+    return _lib.VedaRasterStrides(x.stride(0), x.stride(1), x.stride(2))
+
+
+def _tiled_shape(geom: Geometry, last: int):
+    return (geom.B, geom.n_heads, geom.max_tiles(), TILE_TOKENS, last)
+
+
+def tile_permute(x: torch.Tensor, geom: Geometry, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gather a raster tensor [B, N, heads, d] (bf16, any strides with unit
+    channel stride) into head-tiled order [B, heads, nT_max, 128, d]."""
+    s = _raster_strides(x, geom, "x")
+    shape = _tiled_shape(geom, geom.head_dim)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, shape, "out")
+    _lib.check(_lib.lib.veda_tile_permute(geom.c, x.data_ptr(), s, out.data_ptr(), _stream(x)), "veda_tile_permute")
+    return out
+
+
+def tile_unpermute(xt: torch.Tensor, geom: Geometry, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Scatter a tiled tensor back to raster order [B, N, heads, d]."""
+    _need(xt, torch.bfloat16, _tiled_shape(geom, geom.head_dim), "x_tiled")
+    if out is None:
+        out = torch.empty((geom.B, geom.tokens, geom.n_heads, geom.head_dim), dtype=torch.bfloat16, device=xt.device)
+    s = _raster_strides(out, geom, "out")
+    _lib.check(_lib.lib.veda_tile_unpermute(geom.c, xt.data_ptr(), out.data_ptr(), s, _stream(xt)),
+               "veda_tile_unpermute")
+    return out
+
+
+def trippool_score(q_t: torch.Tensor, k_t: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor, geom: Geometry,
+                   out: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    """TripPool statistics, head-specific projections and tile scores.
+    Returns stats_q, stats_k [B, heads, nT_max, 3d], feat_q, feat_k
+    [B, heads, nT_max, r] (bf16) and scores [B, heads, nT_max, nT_max] (fp32)."""
+    d, nT = geom.head_dim, geom.max_tiles()
+    tshape = _tiled_shape(geom, d)
+    _need(q_t, torch.bfloat16, tshape, "q_tiled")
+    _need(k_t, torch.bfloat16, tshape, "k_tiled")
+    if w_q.dim() != 3:
+        raise ValueError("w_q must be [heads, 3d, r]")
+    r = w_q.shape[2]
+    _need(w_q, torch.bfloat16, (geom.n_heads, 3 * d, r), "w_q")
+    _need(w_k, torch.bfloat16, (geom.n_heads, 3 * d, r), "w_k")
+    dev = q_t.device
+    B, Hh = geom.B, geom.n_heads
+    if out is None:
+        out = {
+            "stats_q": torch.empty((B, Hh, nT, 3 * d), dtype=torch.bfloat16, device=dev),
+            "stats_k": torch.empty((B, Hh, nT, 3 * d), dtype=torch.bfloat16, device=dev),
+            "feat_q": torch.empty((B, Hh, nT, r), dtype=torch.bfloat16, device=dev),
+            "feat_k": torch.empty((B, Hh, nT, r), dtype=torch.bfloat16, device=dev),
+            "scores": torch.empty((B, Hh, nT, nT), dtype=torch.float32, device=dev),
+        }
+    for name, shape, dt in (("stats_q", (B, Hh, nT, 3 * d), torch.bfloat16), ("stats_k", (B, Hh, nT, 3 * d), torch.bfloat16),
+                            ("feat_q", (B, Hh, nT, r), torch.bfloat16), ("feat_k", (B, Hh, nT, r), torch.bfloat16),
+                            ("scores", (B, Hh, nT, nT), torch.float32)):
+        _need(out[name], dt, shape, name)
+    _lib.check(_lib.lib.veda_trippool_score(
+        geom.c, q_t.data_ptr(), k_t.data_ptr(), w_q.data_ptr(), w_k.data_ptr(), int(r),
+        out["stats_q"].data_ptr(), out["stats_k"].data_ptr(), out["feat_q"].data_ptr(), out["feat_k"].data_ptr(),
+        out["scores"].data_ptr(), _stream(q_t)), "veda_trippool_score")
+    return out
+
+
+def topk_mask(scores: torch.Tensor, geom: Geometry, k_per_head: Sequence[int], k_max: Optional[int] = None,
+              with_bitmask: bool = True, idx: Optional[torch.Tensor] = None,
+              bitmask: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Head-aware Top-k: idx [B, heads, nT_max, k_max] int32 (ascending, -1
+    padded) and optionally bitmask [B, heads, nT_max, ceil(nT_max/32)] uint32."""
+    nT = geom.max_tiles()
+    _need(scores, torch.float32, (geom.B, geom.n_heads, nT, nT), "scores")
+    ks = list(k_per_head)
+    if len(ks) != geom.n_heads:
+        raise ValueError("need one k per head")
+    if k_max is None:
+        k_max = max(ks)
+    dev = scores.device
+    if idx is None:
+        idx = torch.empty((geom.B, geom.n_heads, nT, k_max), dtype=torch.int32, device=dev)
+    _need(idx, torch.int32, (geom.B, geom.n_heads, nT, k_max), "idx")
+    if with_bitmask and bitmask is None:
+        bitmask = torch.empty((geom.B, geom.n_heads, nT, (nT + 31) // 32), dtype=torch.uint32, device=dev)
+    if bitmask is not None:
+        _need(bitmask, torch.uint32, (geom.B, geom.n_heads, nT, (nT + 31) // 32), "bitmask")
+    _lib.check(_lib.lib.veda_topk_mask(geom.c, scores.data_ptr(), _lib.int_array(ks), int(k_max), idx.data_ptr(),
+                                       bitmask.data_ptr() if bitmask is not None else None, _stream(scores)),
+               "veda_topk_mask")
+    return idx, bitmask
+
+
+def sparse_attn_fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, idx: torch.Tensor, geom: Geometry,
+                    k_per_head: Sequence[int], scale: Optional[float] = None, with_lse: bool = True,
+                    o_t: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Tile-skipping attention over the selected key tiles; returns tiled O
+    (bf16) and LSE [B, heads, nT_max, 128] (fp32, natural log)."""
+    tshape = _tiled_shape(geom, geom.head_dim)
+    for name, t in (("q_tiled", q_t), ("k_tiled", k_t), ("v_tiled", v_t)):
+        _need(t, torch.bfloat16, tshape, name)
+    if idx.dim() != 4:
+        raise ValueError("idx must be [B, heads, nT_max, k_max]")
+    k_max = idx.shape[3]
+    _need(idx, torch.int32, (geom.B, geom.n_heads, tshape[2], k_max), "idx")
+    ks = list(k_per_head)
+    if len(ks) != geom.n_heads:
+        raise ValueError("need one k per head")
+    if o_t is None:
+        o_t = torch.empty(tshape, dtype=torch.bfloat16, device=q_t.device)
+    _need(o_t, torch.bfloat16, tshape, "o_tiled")
+    if with_lse and lse is None:
+        lse = torch.empty(tshape[:4], dtype=torch.float32, device=q_t.device)
+    if lse is not None:
+        _need(lse, torch.float32, tshape[:4], "lse")
+    sc = float(scale) if scale is not None else 0.0
+    _lib.check(_lib.lib.veda_sparse_attn_fwd(geom.c, q_t.data_ptr(), k_t.data_ptr(), v_t.data_ptr(), idx.data_ptr(),
+                                             _lib.int_array(ks), int(k_max), sc, o_t.data_ptr(),
+                                             lse.data_ptr() if lse is not None else None, _stream(q_t)),
+               "veda_sparse_attn_fwd")
+    return o_t, lse
+
+
+def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
+                  geom: Geometry, k_per_head: Sequence[int], scale: Optional[float] = None,
+                  buffers: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    """One Veda attention layer: permute Q/K/V, TripPool scores, Top-k mask,
+    tile-skipping attention, unpermute. `buffers` (from a previous call)
+    reuses every output allocation. Returns all intermediates and `o`."""
+    b = buffers if buffers is not None else {}
+    b["q_t"] = tile_permute(q, geom, b.get("q_t"))
+    b["k_t"] = tile_permute(k, geom, b.get("k_t"))
+    b["v_t"] = tile_permute(v, geom, b.get("v_t"))
+    est = trippool_score(b["q_t"], b["k_t"], w_q, w_k, geom,
+                         {n: b[n] for n in ("stats_q", "stats_k", "feat_q", "feat_k", "scores")}
+                         if "scores" in b else None)
+    b.update(est)
+    b["idx"], b["bitmask"] = topk_mask(b["scores"], geom, k_per_head, idx=b.get("idx"), bitmask=b.get("bitmask"))
+    b["o_t"], b["lse"] = sparse_attn_fwd(b["q_t"], b["k_t"], b["v_t"], b["idx"], geom, k_per_head, scale,
+                                         o_t=b.get("o_t"), lse=b.get("lse"))
+    b["o"] = tile_unpermute(b["o_t"], geom, b.get("o"))
+    return b

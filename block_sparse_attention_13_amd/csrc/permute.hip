@@ -1,0 +1,106 @@
+// Head-conditioned re-tiling and its inverse (Veda page, "Architecture",
+// Principle 02 "Head-Conditioned Tile Geometry"; "Head-Aware Tile Search").
+//
+// Pure data movement, bound by HBM bandwidth. One workgroup moves one
+// 128-token box of one (batch, head): each token row is d bf16 values
+// (256 B for d = 128), moved as 16-byte vectors so that every wave touches
+// whole 256-byte segments on both sides. All loads of a thread are issued
+// before its stores, which keeps 8 (d = 128) vector loads in flight per lane.
+#include "veda_internal.hpp"
+
+namespace veda {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int D>
+struct RowMap {
+  static constexpr int kChunks = D / 8;                 // 16-byte chunks per token row
+  static constexpr int kRowsPerPass = kThreads / kChunks;
+  static constexpr int kPasses = VEDA_TILE_TOKENS / kRowsPerPass;
+};
+
+// Raster index of slot sigma of a box, or -1 for a pad slot.
+__device__ __forceinline__ int64_t raster_of_slot(const GeoTable& g, const HeadGeo& hg, const BoxExtent& e,
+                                                  int32_t sigma) {
+  if (!slot_is_real(hg, e, sigma)) return -1;
+  const int32_t sx = sigma & ((1 << hg.lpw) - 1);
+  const int32_t sy = (sigma >> hg.lpw) & ((1 << hg.lph) - 1);
+  const int32_t st = sigma >> (hg.lpw + hg.lph);
+  return (int64_t(e.t0 + st) * g.H + (e.y0 + sy)) * g.W + (e.x0 + sx);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void tile_permute_kernel(GeoTable g, const uint16_t* __restrict__ x,
+                                                               int64_t sb, int64_t sn, int64_t sh,
+                                                               uint16_t* __restrict__ xt) {
+  using M = RowMap<D>;
+  const int32_t tau = blockIdx.x, hd = blockIdx.y, b = blockIdx.z;
+  const HeadGeo hg = g.h[hd];
+  const int chunk = threadIdx.x % M::kChunks;
+  const int row0 = threadIdx.x / M::kChunks;
+  uint4* dst = reinterpret_cast<uint4*>(xt + ((int64_t(b) * g.heads + hd) * g.nT_max + tau) * VEDA_TILE_TOKENS * D);
+  uint4 val[M::kPasses];
+  if (tau < hg.nT) {
+    const BoxExtent e = box_extent(g, hg, tau);
+    const uint16_t* src = x + int64_t(b) * sb + int64_t(hd) * sh + chunk * 8;
+#pragma unroll
+    for (int p = 0; p < M::kPasses; ++p) {
+      const int64_t n = raster_of_slot(g, hg, e, row0 + p * M::kRowsPerPass);
+      val[p] = n >= 0 ? *reinterpret_cast<const uint4*>(src + n * sn) : make_uint4(0, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < M::kPasses; ++p) val[p] = make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int p = 0; p < M::kPasses; ++p) dst[(row0 + p * M::kRowsPerPass) * M::kChunks + chunk] = val[p];
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void tile_unpermute_kernel(GeoTable g, const uint16_t* __restrict__ xt,
+                                                                 uint16_t* __restrict__ x, int64_t sb, int64_t sn,
+                                                                 int64_t sh) {
+  using M = RowMap<D>;
+  const int32_t tau = blockIdx.x, hd = blockIdx.y, b = blockIdx.z;
+  const HeadGeo hg = g.h[hd];
+  if (tau >= hg.nT) return;
+  const int chunk = threadIdx.x % M::kChunks;
+  const int row0 = threadIdx.x / M::kChunks;
+  const uint4* src =
+      reinterpret_cast<const uint4*>(xt + ((int64_t(b) * g.heads + hd) * g.nT_max + tau) * VEDA_TILE_TOKENS * D);
+  const BoxExtent e = box_extent(g, hg, tau);
+  uint4 val[M::kPasses];
+#pragma unroll
+  for (int p = 0; p < M::kPasses; ++p) val[p] = src[(row0 + p * M::kRowsPerPass) * M::kChunks + chunk];
+  uint16_t* dst = x + int64_t(b) * sb + int64_t(hd) * sh + chunk * 8;
+#pragma unroll
+  for (int p = 0; p < M::kPasses; ++p) {
+    const int64_t n = raster_of_slot(g, hg, e, row0 + p * M::kRowsPerPass);
+    if (n >= 0) *reinterpret_cast<uint4*>(dst + n * sn) = val[p];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tile_permute(const GeoTable& g, const uint16_t* x, int64_t sb, int64_t sn, int64_t sh,
+                               uint16_t* xt, hipStream_t s) {
+  const dim3 grid(g.nT_max, g.heads, g.B);
+  if (g.d == 128)
+    tile_permute_kernel<128><<<grid, kThreads, 0, s>>>(g, x, sb, sn, sh, xt);
+  else
+    tile_permute_kernel<64><<<grid, kThreads, 0, s>>>(g, x, sb, sn, sh, xt);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_unpermute(const GeoTable& g, const uint16_t* xt, uint16_t* x, int64_t sb, int64_t sn,
+                                 int64_t sh, hipStream_t s) {
+  const dim3 grid(g.nT_max, g.heads, g.B);
+  if (g.d == 128)
+    tile_unpermute_kernel<128><<<grid, kThreads, 0, s>>>(g, xt, x, sb, sn, sh);
+  else
+    tile_unpermute_kernel<64><<<grid, kThreads, 0, s>>>(g, xt, x, sb, sn, sh);
+  return hipGetLastError();
+}
+
+}  // namespace veda

@@ -1,0 +1,119 @@
+// Head-aware Top-k tile mask (Veda page, "Attention Structure Distillation",
+// Execution: Top-k over the estimator's scores, per query tile and per head,
+// yields the binary tile mask passed to the tile-skipping kernel).
+//
+// One wave per row (b, head, query tile). Each score becomes a 32-bit key
+// whose unsigned order is the float order (-0 is first made +0, so signed
+// zeros tie). The row's keys stay in registers (chunk i, lane l holds key
+// tile j = 64*i + l). A bitwise search from the top bit finds the k-th
+// largest key t; then one ascending pass over the chunks keeps every key > t
+// and the lowest-indexed keys == t until k are kept, which is exactly the
+// lower-index tie rule. Ballots give output positions and bitmask words.
+#include "veda_internal.hpp"
+
+namespace veda {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = kThreads / 64;
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;  // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t count_below(uint64_t mask) {  // set bits of lanes < this lane
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
+}
+
+template <int NCH>
+__global__ __launch_bounds__(kThreads) void topk_kernel(GeoTable g, const float* __restrict__ scores, int32_t k_max,
+                                                       int32_t* __restrict__ idx, uint32_t* __restrict__ bitmask) {
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int32_t tq = blockIdx.x * kRowsPerBlock + wave;
+  const int hd = blockIdx.y, b = blockIdx.z;
+  if (tq >= g.nT_max) return;
+  const HeadGeo hg = g.h[hd];
+  const int64_t row = (int64_t(b) * g.heads + hd) * g.nT_max + tq;
+  int32_t* out = idx + row * k_max;
+  const int n_words = (g.nT_max + 31) / 32;
+  uint32_t* bm = bitmask ? bitmask + row * n_words : nullptr;
+
+  if (tq >= hg.nT) {  // no such query tile for this head
+    for (int i = lane; i < k_max; i += 64) out[i] = -1;
+    if (bm)
+      for (int i = lane; i < n_words; i += 64) bm[i] = 0u;
+    return;
+  }
+  const int n = hg.nT, k = hg.k;
+  const float* s = scores + row * g.nT_max;
+  uint32_t key[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int j = i * 64 + lane;
+    key[i] = j < n ? order_key(s[j]) : 0u;  // 0 lies below every finite score's key
+  }
+  // Largest t with #{key >= t} >= k: the k-th largest key.
+  uint32_t t = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) c += key[i] >= cand;
+    if (wave_sum(c) >= k) t = cand;
+  }
+  int c_gt = 0;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) c_gt += key[i] > t;
+  const int need_eq = k - wave_sum(c_gt);  // keys equal to t still to keep, lowest index first
+
+  int kept = 0, eq_seen = 0;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const bool gt = key[i] > t;
+    const bool eq = key[i] == t;
+    const uint64_t eq_mask = __ballot(eq);
+    const bool take = gt || (eq && eq_seen + int(count_below(eq_mask)) < need_eq);
+    const uint64_t take_mask = __ballot(take);
+    if (take) out[kept + int(count_below(take_mask))] = i * 64 + lane;
+    kept += __popcll(take_mask);
+    eq_seen += __popcll(eq_mask);
+    if (bm) {
+      if (lane == 0 && 2 * i < n_words) bm[2 * i] = uint32_t(take_mask);
+      if (lane == 1 && 2 * i + 1 < n_words) bm[2 * i + 1] = uint32_t(take_mask >> 32);
+    }
+  }
+  for (int i = k + lane; i < k_max; i += 64) out[i] = -1;
+}
+
+template <int NCH>
+hipError_t launch_nch(const GeoTable& g, const float* scores, int32_t k_max, int32_t* idx, uint32_t* bitmask,
+                      hipStream_t s) {
+  const dim3 grid((g.nT_max + kRowsPerBlock - 1) / kRowsPerBlock, g.heads, g.B);
+  topk_kernel<NCH><<<grid, kThreads, 0, s>>>(g, scores, k_max, idx, bitmask);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_topk(const GeoTable& g, const float* scores, int32_t k_max, int32_t* idx, uint32_t* bitmask,
+                       hipStream_t s) {
+  const int chunks = (g.nT_max + 63) / 64;
+  if (chunks <= 1) return launch_nch<1>(g, scores, k_max, idx, bitmask, s);
+  if (chunks <= 2) return launch_nch<2>(g, scores, k_max, idx, bitmask, s);
+  if (chunks <= 4) return launch_nch<4>(g, scores, k_max, idx, bitmask, s);
+  if (chunks <= 8) return launch_nch<8>(g, scores, k_max, idx, bitmask, s);
+  if (chunks <= 16) return launch_nch<16>(g, scores, k_max, idx, bitmask, s);
+  if (chunks <= 32) return launch_nch<32>(g, scores, k_max, idx, bitmask, s);
+  if (chunks <= 64) return launch_nch<64>(g, scores, k_max, idx, bitmask, s);
+  return launch_nch<128>(g, scores, k_max, idx, bitmask, s);
+}
+
+}  // namespace veda

@@ -1,0 +1,232 @@
+// TripPool estimator (Veda page, "Attention Structure Distillation",
+// Estimator: per-tile average, maximum and minimum of Q and K, mapped by
+// head-specific Q/K projections to tile scores; "Theoretical Rationale" 2,
+// "Tile Statistics").
+//
+// Two kernels:
+//   trippool_features_kernel  one wave per tile: each lane owns d/64
+//     channels and walks the 128 slots in order (fp32 sum, total-order
+//     max/min over real slots); a wave load is one whole token row, so the
+//     stream from HBM is coalesced. The 3d statistics are staged in LDS and
+//     the same wave projects them with the head's W (held in LDS for the whole
+//     workgroup, 3 workgroups per CU): lane j owns output feature j and
+//     accumulates over the 3d channels in order.
+//   tile_scores_kernel  S = feat_q . feat_k^T per head, 64 x 64 outputs per
+//     workgroup, 4 x 4 per thread, fp32 accumulated over the r channels in order.
+// Every accumulation runs in a fixed ascending order with one rounding per
+// step (products of bf16 values are exact in fp32), so the results are
+// reproducible bit for bit and independent of the launch shape.
+#include "veda_internal.hpp"
+
+namespace veda {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kTilesPerWave = 4;
+constexpr int kTilesPerBlock = kWaves * kTilesPerWave;
+
+// Order-preserving integer key of a bf16 value in the IEEE total order (-0 < +0).
+__device__ __forceinline__ int32_t total_order_key(uint32_t b) {
+  const int32_t mag = int32_t(b & 0x7FFFu);
+  return (b & 0x8000u) ? -mag - 1 : mag;
+}
+__device__ __forceinline__ uint16_t from_total_order_key(int32_t k) {
+  return k >= 0 ? uint16_t(k) : uint16_t(0x8000u | uint32_t(-k - 1));
+}
+
+template <int D, int R>
+__global__ __launch_bounds__(kThreads) void trippool_features_kernel(
+    GeoTable g, const uint16_t* __restrict__ q_t, const uint16_t* __restrict__ k_t,
+    const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wk, uint16_t* __restrict__ stats_q,
+    uint16_t* __restrict__ stats_k, uint16_t* __restrict__ feat_q, uint16_t* __restrict__ feat_k) {
+  constexpr int C = 3 * D;           // statistic channels
+  constexpr int CH = D / 64;         // channels per lane
+  constexpr int kRowsPerLoad = 32;   // token rows held in registers at a time
+  __shared__ uint16_t w_s[C * R];
+  __shared__ float st_s[kWaves][C];
+
+  const int hd = blockIdx.y;
+  const int side = blockIdx.z & 1;  // 0 = Q, 1 = K
+  const int b = blockIdx.z >> 1;
+  const HeadGeo hg = g.h[hd];
+  const uint16_t* xt = side ? k_t : q_t;
+  const uint16_t* w = (side ? wk : wq) + int64_t(hd) * C * R;
+  uint16_t* stats = side ? stats_k : stats_q;
+  uint16_t* feat = side ? feat_k : feat_q;
+
+  // Stage this head's projection matrix (3d x r bf16) in LDS.
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(w);
+    uint4* dst = reinterpret_cast<uint4*>(w_s);
+    for (int i = threadIdx.x; i < C * R / 8; i += kThreads) dst[i] = src[i];
+  }
+  __syncthreads();
+
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  for (int it = 0; it < kTilesPerWave; ++it) {
+    const int32_t tau = blockIdx.x * kTilesPerBlock + it * kWaves + wave;
+    if (tau >= g.nT_max) break;
+    const int64_t row = (int64_t(b) * g.heads + hd) * g.nT_max + tau;
+    uint16_t* st_out = stats + row * C;
+    uint16_t* f_out = feat + row * R;
+    if (tau >= hg.nT) {  // tile beyond this head's grid: defined zeros
+      for (int c = lane; c < C; c += 64) st_out[c] = 0;
+      if (lane < R) f_out[lane] = 0;
+      continue;
+    }
+    const BoxExtent e = box_extent(g, hg, tau);
+    const bool full = box_is_full(hg, e);
+    // Lane owns channels [lane*CH, lane*CH + CH); one wave load reads a whole
+    // token row (d bf16), so every load is a coalesced 128/256-byte segment.
+    const uint16_t* src = xt + row * VEDA_TILE_TOKENS * D + lane * CH;
+    float sum[CH];
+    int32_t mx[CH], mn[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      sum[c] = 0.0f;
+      mx[c] = -(1 << 20);
+      mn[c] = 1 << 20;
+    }
+    int32_t n_real = 0;
+    for (int s0 = 0; s0 < VEDA_TILE_TOKENS; s0 += kRowsPerLoad) {
+      uint32_t v[kRowsPerLoad];
+#pragma unroll
+      for (int i = 0; i < kRowsPerLoad; ++i) {
+        if constexpr (CH == 2)
+          v[i] = *reinterpret_cast<const uint32_t*>(src + (s0 + i) * D);
+        else
+          v[i] = src[(s0 + i) * D];
+      }
+#pragma unroll
+      for (int i = 0; i < kRowsPerLoad; ++i) {
+        if (!full && !slot_is_real(hg, e, s0 + i)) continue;  // uniform over the wave
+        ++n_real;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          const uint32_t bits = (v[i] >> (16 * c)) & 0xFFFFu;
+          sum[c] = sum[c] + bf16_to_f32(uint16_t(bits));
+          const int32_t key = total_order_key(bits);
+          mx[c] = max(mx[c], key);
+          mn[c] = min(mn[c], key);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      // sum / n in double then to float is the correctly rounded float quotient
+      // (53 >= 2*24 + 2, so the double rounding is innocuous).
+      const float avg = float(double(sum[c]) / double(n_real));
+      const uint16_t a = f32_to_bf16_rne(avg);
+      const uint16_t hi = from_total_order_key(mx[c]);
+      const uint16_t lo = from_total_order_key(mn[c]);
+      const int ch = lane * CH + c;
+      st_out[ch] = a;
+      st_out[D + ch] = hi;
+      st_out[2 * D + ch] = lo;
+      st_s[wave][ch] = bf16_to_f32(a);
+      st_s[wave][D + ch] = bf16_to_f32(hi);
+      st_s[wave][2 * D + ch] = bf16_to_f32(lo);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // Projection: lane j < r accumulates sum_c st[c] * W[c][j] in ascending c.
+    if (lane < R) {
+      float acc = 0.0f;
+      for (int c = 0; c < C; ++c) acc = __builtin_fmaf(st_s[wave][c], bf16_to_f32(w_s[c * R + lane]), acc);
+      f_out[lane] = f32_to_bf16_rne(acc);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+constexpr int kScoreTile = 64;
+
+template <int R>
+__global__ __launch_bounds__(kThreads) void tile_scores_kernel(GeoTable g, const uint16_t* __restrict__ feat_q,
+                                                              const uint16_t* __restrict__ feat_k,
+                                                              float* __restrict__ scores) {
+  __shared__ float fq_s[R][kScoreTile];  // transposed: [channel][row]
+  __shared__ float fk_s[R][kScoreTile];
+  const int hd = blockIdx.y, b = blockIdx.z;
+  const HeadGeo hg = g.h[hd];
+  const int i0 = blockIdx.x / ((g.nT_max + kScoreTile - 1) / kScoreTile) * kScoreTile;
+  const int j0 = blockIdx.x % ((g.nT_max + kScoreTile - 1) / kScoreTile) * kScoreTile;
+  const int64_t head_row = (int64_t(b) * g.heads + hd) * g.nT_max;
+  for (int e = threadIdx.x; e < kScoreTile * R; e += kThreads) {
+    const int r = e / R, c = e % R;
+    const int i = i0 + r, j = j0 + r;
+    fq_s[c][r] = i < hg.nT ? bf16_to_f32(feat_q[(head_row + i) * R + c]) : 0.0f;
+    fk_s[c][r] = j < hg.nT ? bf16_to_f32(feat_k[(head_row + j) * R + c]) : 0.0f;
+  }
+  __syncthreads();
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  float acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[a][c] = 0.0f;
+#pragma unroll 8
+  for (int c = 0; c < R; ++c) {
+    const float4 qa = *reinterpret_cast<const float4*>(&fq_s[c][ty * 4]);
+    const float4 kb = *reinterpret_cast<const float4*>(&fk_s[c][tx * 4]);
+    const float qv[4] = {qa.x, qa.y, qa.z, qa.w};
+    const float kv[4] = {kb.x, kb.y, kb.z, kb.w};
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) acc[a][k2] = __builtin_fmaf(qv[a], kv[k2], acc[a][k2]);
+  }
+  const float ninf = -__builtin_inff();
+  const bool vec_ok = (g.nT_max % 4) == 0;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int i = i0 + ty * 4 + a;
+    if (i >= g.nT_max) continue;
+    float* out = scores + (head_row + i) * g.nT_max;
+    const int j = j0 + tx * 4;
+    float v[4];
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) v[k2] = (i < hg.nT && j + k2 < hg.nT) ? acc[a][k2] : ninf;
+    if (vec_ok && j + 3 < g.nT_max) {
+      *reinterpret_cast<float4*>(out + j) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2)
+        if (j + k2 < g.nT_max) out[j + k2] = v[k2];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_trippool_features(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t,
+                                    const uint16_t* wq, const uint16_t* wk, int32_t r, uint16_t* stats_q,
+                                    uint16_t* stats_k, uint16_t* feat_q, uint16_t* feat_k, hipStream_t s) {
+  const dim3 grid((g.nT_max + kTilesPerBlock - 1) / kTilesPerBlock, g.heads, 2 * g.B);
+  if (g.d == 128 && r == 64)
+    trippool_features_kernel<128, 64><<<grid, kThreads, 0, s>>>(g, q_t, k_t, wq, wk, stats_q, stats_k, feat_q, feat_k);
+  else if (g.d == 128 && r == 32)
+    trippool_features_kernel<128, 32><<<grid, kThreads, 0, s>>>(g, q_t, k_t, wq, wk, stats_q, stats_k, feat_q, feat_k);
+  else if (g.d == 64 && r == 64)
+    trippool_features_kernel<64, 64><<<grid, kThreads, 0, s>>>(g, q_t, k_t, wq, wk, stats_q, stats_k, feat_q, feat_k);
+  else
+    trippool_features_kernel<64, 32><<<grid, kThreads, 0, s>>>(g, q_t, k_t, wq, wk, stats_q, stats_k, feat_q, feat_k);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_scores(const GeoTable& g, const uint16_t* feat_q, const uint16_t* feat_k, int32_t r,
+                              float* scores, hipStream_t s) {
+  const int nb = (g.nT_max + kScoreTile - 1) / kScoreTile;
+  const dim3 grid(nb * nb, g.heads, g.B);
+  if (r == 64)
+    tile_scores_kernel<64><<<grid, kThreads, 0, s>>>(g, feat_q, feat_k, scores);
+  else
+    tile_scores_kernel<32><<<grid, kThreads, 0, s>>>(g, feat_q, feat_k, scores);
+  return hipGetLastError();
+}
+
+}  // namespace veda

@@ -1,0 +1,213 @@
+// C ABI of libveda: argument validation, per-head geometry tables and kernel
+// launches. Every argument check runs on the host before any HIP call, so an
+// invalid call enqueues nothing and writes nothing. The library allocates no
+// device memory; the only process-wide state is a per-device cache of the
+// architecture check.
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "veda_internal.hpp"
+
+namespace {
+
+using veda::GeoTable;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int build_table(const veda_geom* g, GeoTable* t) {
+  if (!g || !g->head_tile) return VEDA_ERR_NULL;
+  if (g->B <= 0 || g->n_heads <= 0 || g->n_heads > VEDA_MAX_HEADS) return VEDA_ERR_SHAPE;
+  if (g->head_dim != 64 && g->head_dim != 128) return VEDA_ERR_SHAPE;
+  if (g->grid.T <= 0 || g->grid.H <= 0 || g->grid.W <= 0) return VEDA_ERR_SHAPE;
+  if (g->B > 65535) return VEDA_ERR_SHAPE;
+  std::memset(t, 0, sizeof(*t));
+  t->B = g->B;
+  t->heads = g->n_heads;
+  t->d = g->head_dim;
+  t->T = g->grid.T;
+  t->H = g->grid.H;
+  t->W = g->grid.W;
+  int64_t nT_max = 0;
+  for (int hd = 0; hd < g->n_heads; ++hd) {
+    const veda_tile tl = g->head_tile[hd];
+    if (tl.pt <= 0 || tl.ph <= 0 || tl.pw <= 0) return VEDA_ERR_TILE;
+    if (int64_t(tl.pt) * tl.ph * tl.pw != VEDA_TILE_TOKENS) return VEDA_ERR_TILE;
+    // Each edge divides 128, so it is a power of two.
+    veda::HeadGeo& h = t->h[hd];
+    h.lpt = uint8_t(__builtin_ctz(unsigned(tl.pt)));
+    h.lph = uint8_t(__builtin_ctz(unsigned(tl.ph)));
+    h.lpw = uint8_t(__builtin_ctz(unsigned(tl.pw)));
+    const int64_t nTt = (int64_t(g->grid.T) + tl.pt - 1) / tl.pt;
+    const int64_t nTh = (int64_t(g->grid.H) + tl.ph - 1) / tl.ph;
+    const int64_t nTw = (int64_t(g->grid.W) + tl.pw - 1) / tl.pw;
+    const int64_t nT = nTt * nTh * nTw;
+    if (nT > VEDA_MAX_TILES) return VEDA_ERR_SHAPE;
+    h.nTh = int32_t(nTh);
+    h.nTw = int32_t(nTw);
+    h.nT = int32_t(nT);
+    h.k = 0;
+    if (nT > nT_max) nT_max = nT;
+  }
+  t->nT_max = int32_t(nT_max);
+  return VEDA_OK;
+}
+
+int set_k(const int32_t* k_per_head, int32_t k_max, GeoTable* t) {
+  if (!k_per_head) return VEDA_ERR_NULL;
+  if (k_max <= 0 || k_max > t->nT_max) return VEDA_ERR_K;
+  for (int hd = 0; hd < t->heads; ++hd) {
+    const int32_t k = k_per_head[hd];
+    if (k < 1 || k > t->h[hd].nT || k > k_max) return VEDA_ERR_K;
+    t->h[hd].k = k;
+  }
+  return VEDA_OK;
+}
+
+int check_strides(const veda_raster_strides& s) {
+  if (s.b % 8 || s.n % 8 || s.h % 8) return VEDA_ERR_ALIGN;
+  if (s.b < 0 || s.n < 0 || s.h < 0) return VEDA_ERR_SHAPE;
+  return VEDA_OK;
+}
+
+// The current device must be a gfx950 (MI355X class). Cached per device id.
+int check_device() {
+  static std::atomic<int> cache[64];  // 0 unknown, 1 ok, -1 not gfx950
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return VEDA_ERR_DEVICE;
+  }
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c != 0) {
+      (void)hipGetLastError();  // clear a stale error so launch checks see only ours
+      return c > 0 ? VEDA_OK : VEDA_ERR_DEVICE;
+    }
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return VEDA_ERR_DEVICE;
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) cache[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+  return ok ? VEDA_OK : VEDA_ERR_DEVICE;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? VEDA_OK : VEDA_ERR_LAUNCH; }
+
+#define VEDA_TRY(expr)            \
+  do {                            \
+    const int rc_ = (expr);       \
+    if (rc_ != VEDA_OK) return rc_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* veda_status_str(int status) {
+  switch (status) {
+    case VEDA_OK: return "ok";
+    case VEDA_ERR_NULL: return "null pointer argument";
+    case VEDA_ERR_SHAPE: return "shape out of range";
+    case VEDA_ERR_TILE: return "tile volume is not 128";
+    case VEDA_ERR_K: return "k outside [1, tiles of the head] or above k_max";
+    case VEDA_ERR_ALIGN: return "pointer not 16-byte aligned or stride not a multiple of 8";
+    case VEDA_ERR_DEVICE: return "no gfx950 HIP device current";
+    case VEDA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int veda_num_tiles(const veda_geom* g, int32_t head) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (head < 0 || head >= t.heads) return VEDA_ERR_SHAPE;
+  return t.h[head].nT;
+}
+
+int veda_max_tiles(const veda_geom* g) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  return t.nT_max;
+}
+
+int veda_tile_permute(const veda_geom* g, const void* x_raster, veda_raster_strides s, void* x_tiled,
+                      void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!x_raster || !x_tiled) return VEDA_ERR_NULL;
+  if (!aligned16(x_raster) || !aligned16(x_tiled)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_strides(s));
+  VEDA_TRY(check_device());
+  return launched(veda::launch_tile_permute(t, static_cast<const uint16_t*>(x_raster), s.b, s.n, s.h,
+                                            static_cast<uint16_t*>(x_tiled), static_cast<hipStream_t>(stream)));
+}
+
+int veda_tile_unpermute(const veda_geom* g, const void* x_tiled, void* x_raster, veda_raster_strides s,
+                        void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!x_raster || !x_tiled) return VEDA_ERR_NULL;
+  if (!aligned16(x_raster) || !aligned16(x_tiled)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_strides(s));
+  VEDA_TRY(check_device());
+  return launched(veda::launch_tile_unpermute(t, static_cast<const uint16_t*>(x_tiled),
+                                              static_cast<uint16_t*>(x_raster), s.b, s.n, s.h,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int veda_trippool_score(const veda_geom* g, const void* q_tiled, const void* k_tiled, const void* w_q,
+                        const void* w_k, int32_t rank, void* stats_q, void* stats_k, void* feat_q, void* feat_k,
+                        float* scores, void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!q_tiled || !k_tiled || !w_q || !w_k || !stats_q || !stats_k || !feat_q || !feat_k || !scores)
+    return VEDA_ERR_NULL;
+  if (rank != 32 && rank != 64) return VEDA_ERR_SHAPE;
+  for (const void* p : {q_tiled, k_tiled, w_q, w_k, static_cast<const void*>(stats_q),
+                        static_cast<const void*>(stats_k), static_cast<const void*>(feat_q),
+                        static_cast<const void*>(feat_k), static_cast<const void*>(scores)})
+    if (!aligned16(p)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_device());
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  VEDA_TRY(launched(veda::launch_trippool_features(
+      t, static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_tiled),
+      static_cast<const uint16_t*>(w_q), static_cast<const uint16_t*>(w_k), rank, static_cast<uint16_t*>(stats_q),
+      static_cast<uint16_t*>(stats_k), static_cast<uint16_t*>(feat_q), static_cast<uint16_t*>(feat_k), st)));
+  return launched(veda::launch_tile_scores(t, static_cast<const uint16_t*>(feat_q),
+                                           static_cast<const uint16_t*>(feat_k), rank, scores, st));
+}
+
+int veda_topk_mask(const veda_geom* g, const float* scores, const int32_t* k_per_head, int32_t k_max,
+                   int32_t* idx, uint32_t* bitmask, void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!scores || !idx) return VEDA_ERR_NULL;
+  VEDA_TRY(set_k(k_per_head, k_max, &t));
+  if (!aligned16(scores) || !aligned16(idx) || (bitmask && !aligned16(bitmask))) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_device());
+  return launched(veda::launch_topk(t, scores, k_max, idx, bitmask, static_cast<hipStream_t>(stream)));
+}
+
+int veda_sparse_attn_fwd(const veda_geom* g, const void* q_tiled, const void* k_tiled, const void* v_tiled,
+                         const int32_t* idx, const int32_t* k_per_head, int32_t k_max, float softmax_scale,
+                         void* o_tiled, float* lse, void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!q_tiled || !k_tiled || !v_tiled || !idx || !o_tiled) return VEDA_ERR_NULL;
+  VEDA_TRY(set_k(k_per_head, k_max, &t));
+  for (const void* p : {q_tiled, k_tiled, v_tiled, static_cast<const void*>(idx), static_cast<const void*>(o_tiled)})
+    if (!aligned16(p)) return VEDA_ERR_ALIGN;
+  if (lse && !aligned16(lse)) return VEDA_ERR_ALIGN;
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) softmax_scale = 1.0f / std::sqrt(float(t.d));
+  VEDA_TRY(check_device());
+  return launched(veda::launch_sparse_attn(
+      t, static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_tiled),
+      static_cast<const uint16_t*>(v_tiled), idx, k_max, softmax_scale, static_cast<uint16_t*>(o_tiled), lse,
+      static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

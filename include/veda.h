@@ -1,0 +1,187 @@
+/*
+ * veda.h - C ABI of the Veda tile-sparse self-attention forward for AMD
+ * MI355X (gfx950).
+ *
+ * Method: "Veda: Scalable Video Diffusion via Distilled Sparse Attention"
+ * (project page veda-sparse.github.io). One attention layer is five calls:
+ *
+ *   veda_tile_permute      x3  raster Q/K/V -> head-specific 128-token tiles
+ *   veda_trippool_score        TripPool stats -> head-specific projections -> tile scores
+ *   veda_topk_mask             head-aware Top-k per query tile -> index lists (+ bitmask)
+ *   veda_sparse_attn_fwd       flash-attention forward over the selected K/V tiles only
+ *   veda_tile_unpermute        tiled O -> raster O
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Tensors are DEVICE pointers allocated and owned by the caller; the library
+ * never allocates, frees or caches device memory and keeps no state between
+ * calls (re-entrant, thread-safe). Small arrays marked "host" are read during
+ * the call only. `stream` is a hipStream_t (NULL = the default stream); every
+ * call only enqueues work on it and never synchronises, so results are
+ * visible in stream order. Inputs are read-only; outputs must not overlap
+ * inputs or each other.
+ *
+ * Geometry. The latent grid is (T, H, W); the raster token index is
+ * n = (t*H + y)*W + x. Head hd uses tile (pt, ph, pw) with pt*ph*pw = 128
+ * (so each edge is a power of two). Each axis is padded up to a multiple of
+ * the tile edge, giving nT_hd = ceil(T/pt)*ceil(H/ph)*ceil(W/pw) tiles;
+ * nT_max is the largest nT_hd over heads. Tiles are numbered in raster order
+ * of their box coordinates and the 128 slots of a tile in raster order of
+ * the offsets (t%pt, y%ph, x%pw). A slot no real token maps to is a pad slot.
+ *
+ * Layouts (row-major, contiguous unless a stride is given):
+ *   raster x        [B, N, heads, d] bf16 with element strides veda_raster_strides (channel stride 1)
+ *   tiled x         [B, heads, nT_max, 128, d] bf16
+ *   stats           [B, heads, nT_max, 3d] bf16, [avg | max | min]
+ *   features        [B, heads, nT_max, r] bf16
+ *   W_q, W_k        [heads, 3d, r] bf16 (features = stats @ W)
+ *   scores          [B, heads, nT_max, nT_max] fp32
+ *   idx             [B, heads, nT_max, k_max] int32
+ *   bitmask         [B, heads, nT_max, ceil(nT_max/32)] uint32
+ *   lse             [B, heads, nT_max, 128] fp32
+ *
+ * Defined outputs: every output byte is written. Pad slots of tiled tensors
+ * hold 0; tiles with index >= nT_hd hold 0 (tiled, stats, features), -inf
+ * (scores and lse) or -1 (idx) and 0 (bitmask); scores outside the head's
+ * nT_hd x nT_hd block are -inf; idx entries past k_hd are -1.
+ *
+ * Errors: every call returns VEDA_OK (0) or a negative status. All argument
+ * checks run on the host BEFORE anything is enqueued, so a call that fails
+ * them writes nothing. Checks: null pointers; B, heads or a grid edge <= 0;
+ * heads > VEDA_MAX_HEADS; d not 64 or 128; r not 32 or 64; a tile whose
+ * volume is not 128; nT_max > VEDA_MAX_TILES; k_hd outside [1, nT_hd] or
+ * above k_max; a tensor pointer not 16-byte aligned or a raster stride not a
+ * multiple of 8 elements; the current device not gfx950. A failed launch
+ * returns VEDA_ERR_LAUNCH. Nothing throws or aborts across this ABI.
+ */
+#ifndef VEDA_H_
+#define VEDA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VEDA_TILE_TOKENS 128
+#define VEDA_MAX_HEADS 128
+#define VEDA_MAX_TILES 8192
+
+enum {
+  VEDA_OK = 0,
+  VEDA_ERR_NULL = -1,    /* a required pointer is NULL */
+  VEDA_ERR_SHAPE = -2,   /* B, heads, grid, d, r or a size limit out of range */
+  VEDA_ERR_TILE = -3,    /* a head's tile volume is not 128 */
+  VEDA_ERR_K = -4,       /* k_hd outside [1, nT_hd] or above k_max */
+  VEDA_ERR_ALIGN = -5,   /* a pointer not 16-byte aligned, or a stride not a multiple of 8 */
+  VEDA_ERR_DEVICE = -6,  /* no HIP device, or the current device is not gfx950 */
+  VEDA_ERR_LAUNCH = -7   /* a kernel launch failed */
+};
+
+typedef struct { int32_t T, H, W; } veda_grid;
+typedef struct { int32_t pt, ph, pw; } veda_tile;
+
+typedef struct {
+  int32_t B;                   /* batch */
+  int32_t n_heads;             /* attention heads, 1..VEDA_MAX_HEADS */
+  int32_t head_dim;            /* d: 64 or 128 */
+  veda_grid grid;              /* latent grid (T, H, W) */
+  const veda_tile* head_tile;  /* host array [n_heads]: tile shape of each head */
+} veda_geom;
+
+/* Element strides of a raster tensor [B, N, heads, d]; the channel stride is 1. */
+typedef struct { int64_t b, n, h; } veda_raster_strides;
+
+/* Text of a status code (static storage). */
+const char* veda_status_str(int status);
+
+/* Tiles of head `head` (host only, no device work): nT_hd >= 1, or a negative status. */
+int veda_num_tiles(const veda_geom* g, int32_t head);
+
+/* Largest tile count over heads (host only): nT_max >= 1, or a negative status. */
+int veda_max_tiles(const veda_geom* g);
+
+/*
+ * Head-conditioned re-tiling of a raster tensor (Veda page, "Architecture",
+ * Principle 02 "Head-Conditioned Tile Geometry": per-head tile shapes
+ * (p_t, p_h, p_w); "Head-Aware Tile Search": p_t*p_h*p_w = B = 128).
+ *   x_raster  in   raster bf16 tensor, strides `s` (elements)
+ *   x_tiled   out  tiled bf16 [B, heads, nT_max, 128, d]; pad slots and tiles >= nT_hd are 0
+ */
+int veda_tile_permute(const veda_geom* g, const void* x_raster, veda_raster_strides s,
+                      void* x_tiled, void* stream);
+
+/*
+ * TripPool estimator (Veda page, "Attention Structure Distillation",
+ * Estimator: average, maximum and minimum per tile, then head-specific Q/K
+ * projections score each query-tile x key-tile pair; "Theoretical
+ * Rationale" 2 "Tile Statistics").
+ *   q_tiled, k_tiled  in   tiled bf16 Q and K
+ *   w_q, w_k          in   bf16 [heads, 3d, rank]
+ *   rank              in   r: 32 or 64
+ *   stats_q, stats_k  out  bf16 [B, heads, nT_max, 3d]: avg (fp32 sum in slot order over real
+ *                          tokens from +0, correctly rounded divide, round-to-nearest-even to
+ *                          bf16), max and min (exact; -0 orders below +0)
+ *   feat_q, feat_k    out  bf16 [B, heads, nT_max, rank]: stats @ W, fp32 accumulated one
+ *                          channel at a time in ascending order from +0, then rounded to bf16
+ *   scores            out  fp32 [B, heads, nT_max, nT_max]: feat_q . feat_k, fp32 accumulated
+ *                          in ascending channel order from +0; -inf outside the head's block
+ * The fixed accumulation order makes every output reproducible bit for bit.
+ */
+int veda_trippool_score(const veda_geom* g, const void* q_tiled, const void* k_tiled,
+                        const void* w_q, const void* w_k, int32_t rank,
+                        void* stats_q, void* stats_k, void* feat_q, void* feat_k,
+                        float* scores, void* stream);
+
+/*
+ * Head-aware Top-k tile mask (Veda page, "Attention Structure Distillation",
+ * Execution: Top-k per query tile gives the binary tile mask). For every
+ * (b, hd, query tile) the k_hd largest scores among key tiles 0..nT_hd-1;
+ * equal scores go to the lower tile index and -0 equals +0.
+ *   scores      in   fp32 [B, heads, nT_max, nT_max] (finite within each head's block)
+ *   k_per_head  in   host int32 [heads]: k_hd, 1 <= k_hd <= nT_hd, k_hd <= k_max
+ *   k_max       in   row length of idx
+ *   idx         out  int32 [B, heads, nT_max, k_max]: kept tiles ascending, then -1
+ *   bitmask     out  uint32 [B, heads, nT_max, ceil(nT_max/32)], bit j%32 of word j/32; may be NULL
+ */
+int veda_topk_mask(const veda_geom* g, const float* scores, const int32_t* k_per_head,
+                   int32_t k_max, int32_t* idx, uint32_t* bitmask, void* stream);
+
+/*
+ * Tile-skipping attention forward (Veda page, "Attention Structure
+ * Distillation", Execution: the kernel fetches only the selected K/V tiles;
+ * "Principle 03" Tile-Sparse Kernel; "Theoretical Rationale" 1 "Softmax
+ * Geometry": each query row is a softmax over the kept keys, i.e. the dense
+ * probabilities renormalised by Z / Z_hat, with log-sum-exp LSE).
+ * Query token i of tile tq attends to the real (non-pad) keys of the tiles
+ * idx[b, hd, tq, 0..k_hd-1]; logits are scale * q.k; bf16 MFMA products with
+ * fp32 accumulation and an fp32 online softmax.
+ *   q_tiled, k_tiled, v_tiled  in   tiled bf16
+ *   idx                        in   int32 [B, heads, nT_max, k_max] from veda_topk_mask
+ *                                   (entries 0..k_hd-1 must lie in [0, nT_hd))
+ *   k_per_head                 in   host int32 [heads]
+ *   softmax_scale              in   logit scale; <= 0 selects 1/sqrt(d)
+ *   o_tiled                    out  tiled bf16 O; tiles >= nT_hd are 0; pad query slots hold the
+ *                                   output of a zero query
+ *   lse                        out  fp32 [B, heads, nT_max, 128], natural log of the softmax
+ *                                   denominator of the scaled logits; -inf for tiles >= nT_hd; may be NULL
+ */
+int veda_sparse_attn_fwd(const veda_geom* g, const void* q_tiled, const void* k_tiled,
+                         const void* v_tiled, const int32_t* idx, const int32_t* k_per_head,
+                         int32_t k_max, float softmax_scale, void* o_tiled, float* lse,
+                         void* stream);
+
+/*
+ * Inverse re-tiling: raster x[b, n, hd, :] = tiled x at the slot of token n
+ * (the inverse of veda_tile_permute; pad slots are dropped).
+ *   x_tiled   in   tiled bf16 [B, heads, nT_max, 128, d]
+ *   x_raster  out  raster bf16 tensor, strides `s`; every (b, n, hd, c) element is written
+ */
+int veda_tile_unpermute(const veda_geom* g, const void* x_tiled, void* x_raster,
+                        veda_raster_strides s, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VEDA_H_ */

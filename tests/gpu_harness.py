@@ -1,0 +1,86 @@
+"""Helpers for the GPU parity tests: move seeded host bytes to the device, run
+the HIP path through the C ABI, and compare with the CPU oracle computed from
+the same host bytes."""
+
+from __future__ import annotations
+
+import math
+import sys
+from typing import Dict, List, Sequence
+
+import numpy as np
+import torch
+
+import oracle as O
+
+# Tolerances for attention output and LSE (bf16 inputs, fp32 MFMA accumulate,
+# P rounded to bf16 before the PV product, fp32 online softmax). O is stored
+# in bf16, whose half-ulp alone exceeds 1e-2 once |o| >= 4 (1.5625e-2 on
+# [4, 8)); the max-abs bound therefore applies to the error beyond the
+# output's own quantisation: |got - want| <= 1e-2 + half_ulp_bf16(want).
+O_MAX_ABS = 1e-2
+O_REL_L2 = 5e-3
+LSE_MAX_ABS = 2e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.bfloat16).cuda()
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.uint32:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    if t.dtype == torch.float32:
+        return t.numpy().view(np.uint32)
+    return t.numpy()
+
+
+def f32_of_bf16(t: torch.Tensor) -> np.ndarray:
+    return O.bf16_bits_to_float(bits_of(t))
+
+
+def geometry(w, heads: Sequence[int] = None):
+    import block_sparse_attention_13_amd as V
+    return V.Geometry(w.B, w.heads, w.d, w.grid, w.head_tiles())
+
+
+def oracle_head(data: Dict[str, np.ndarray], w, b: int, hd: int, k: int, query_tiles=None, scale=None):
+    """The oracle's whole layer for one (batch, head) from the host bytes."""
+    q, k_, v = (O.bf16_bits_to_float(data[n][b, :, hd, :]) for n in ("q", "k", "v"))
+    wq, wk = (O.bf16_bits_to_float(data[n][hd]) for n in ("wq", "wk"))
+    return O.head_forward(q, k_, v, wq, wk, w.grid, w.head_tiles()[hd], k, scale=scale, query_tiles=query_tiles)
+
+
+def compare_o(got: np.ndarray, want: np.ndarray, what: str):
+    """Element-wise attention check: max-abs and relative L2."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = got - want
+    max_abs = float(np.max(np.abs(err)))
+    excess = float(np.max(np.abs(err) - half_ulp_bf16(want)))
+    rel = float(np.linalg.norm(err) / max(np.linalg.norm(want), 1e-30))
+    assert excess <= O_MAX_ABS and rel <= O_REL_L2, \
+        f"{what}: max-abs {max_abs:.3e} ({excess:.3e} beyond bf16 output rounding), rel-L2 {rel:.3e}"
+    return max_abs, rel
+
+
+def half_ulp_bf16(x: np.ndarray) -> np.ndarray:
+    """Half the spacing of bfloat16 numbers at |x| (8 significant bits)."""
+    a = np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 8)
+
+
+def compare_lse(got: np.ndarray, want: np.ndarray, what: str):
+    err = float(np.max(np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64))))
+    assert err <= LSE_MAX_ABS, f"{what}: LSE max-abs {err:.3e}"
+    return err

@@ -1,0 +1,272 @@
+"""HIP path vs the CPU oracle, through the C ABI, on the same seeded host bytes.
+
+Bit-exact: tiled Q/K/V, TripPool stats, features, tile scores, index lists,
+bitmasks, unpermuted layouts. Within tolerance (max-abs 1e-2, rel-L2 5e-3 for
+O; 2e-3 for LSE): attention outputs. Large workloads run in full on the GPU
+and are checked on sampled heads and query tiles."""
+
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle as O
+from gpu_harness import (bits_of, compare_lse, compare_o, f32_of_bf16, geometry, oracle_head, say, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+W = datagen.WORKLOADS
+
+
+def _lib():
+    import block_sparse_attention_13_amd as V
+    return V
+
+
+def run_layer(w, data, k_per_head=None, buffers=None):
+    V = _lib()
+    geom = geometry(w)
+    ks = k_per_head or w.k_per_head()
+    q, k, v = (to_dev_bf16(data[n]) for n in ("q", "k", "v"))
+    wq, wk = to_dev_bf16(data["wq"]), to_dev_bf16(data["wk"])
+    out = V.layer_forward(q, k, v, wq, wk, geom, ks, buffers=buffers)
+    torch.cuda.synchronize()
+    return geom, out, (q, k, v, wq, wk)
+
+
+def _sample_tiles(nT, count, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, nT // 2, nT - 2, nT - 1]
+    extra = rng.choice(nT, size=min(nT, count), replace=False).tolist()
+    return sorted(set(t for t in fixed + extra if 0 <= t < nT))
+
+
+def check_head(w, data, out, hd, ks, tiles, b=0, check_attention=True):
+    """Full bit-exact check of one head's tiling and estimator, and attention
+    on the sampled query tiles."""
+    d, nT = w.d, w.tiles_per_head()[hd]
+    nT_max = max(w.tiles_per_head())
+    tile = w.head_tiles()[hd]
+    r = oracle_head(data, w, b, hd, ks[hd], query_tiles=tiles if check_attention else [])
+    for name in ("q_t", "k_t", "v_t"):
+        got = bits_of(out[name][b, hd])
+        assert np.array_equal(got[:nT].reshape(-1, d), O.float_to_bf16_bits(r[name[0] + "t"])), (name, hd)
+        assert not got[nT:].any(), (name, hd, "tiles beyond the head must be zero")
+    for name in ("stats_q", "stats_k", "feat_q", "feat_k"):
+        got = bits_of(out[name][b, hd])
+        assert np.array_equal(got[:nT], O.float_to_bf16_bits(r[name])), (name, hd)
+        assert not got[nT:].any(), (name, hd)
+    S = out["scores"][b, hd].cpu().numpy()
+    assert np.array_equal(S[:nT, :nT].view(np.uint32), r["scores"].view(np.uint32)), ("scores", hd)
+    assert np.all(np.isneginf(S[nT:, :])) and np.all(np.isneginf(S[:, nT:])), ("scores pad", hd)
+    idx = out["idx"][b, hd].cpu().numpy()
+    k = ks[hd]
+    assert np.array_equal(idx[:nT, :k], r["idx"]), ("idx", hd)
+    assert np.all(idx[:nT, k:] == -1) and np.all(idx[nT:] == -1), ("idx pad", hd)
+    bm = bits_of(out["bitmask"][b, hd])
+    words = (nT_max + 31) // 32
+    want_bm = np.zeros((nT_max, words), np.uint32)
+    want_bm[:nT, :r["bitmask"].shape[1]] = r["bitmask"]
+    assert np.array_equal(bm, want_bm), ("bitmask", hd)
+    if not check_attention:
+        return r
+    pos = O.tiled_position(w.grid, tile)
+    rows = np.flatnonzero(np.isfinite(r["lse"]))
+    o_gpu = f32_of_bf16(out["o"][b, :, hd, :])
+    compare_o(o_gpu[rows], r["o"][rows], f"{w.name} head {hd} O")
+    lse_t = out["lse"][b, hd].cpu().numpy().reshape(-1)
+    compare_lse(lse_t[pos[rows]], r["lse"][rows], f"{w.name} head {hd}")
+    # pad query slots hold the output of a zero query: the mean of the real
+    # value rows of the selected tiles
+    valid = np.zeros(nT * 128, bool)
+    valid[pos] = True
+    v_t = O.bf16_bits_to_float(bits_of(out["v_t"][b, hd])).reshape(nT_max, 128, d).astype(np.float64)
+    o_t = f32_of_bf16(out["o_t"][b, hd]).reshape(nT_max, 128, d)
+    for t in tiles:
+        pads = np.flatnonzero(~valid[t * 128:(t + 1) * 128])
+        if len(pads):
+            sel = r["idx"][t]
+            keys = np.concatenate([v_t[j][valid[j * 128:(j + 1) * 128]] for j in sel])
+            want = keys.mean(axis=0)
+            compare_o(o_t[t, pads], np.broadcast_to(want, (len(pads), d)), f"pad queries of tile {t}")
+    if nT < nT_max:
+        assert not bits_of(out["o_t"][b, hd])[nT:].any()
+        assert np.all(np.isneginf(out["lse"][b, hd, nT:].cpu().numpy()))
+    return r
+
+
+@pytest.mark.parametrize("name,heads,tiles_per_head", [
+    ("tiny", None, None),
+    ("480p", None, 24),
+    ("720p", [0, 1, 2, 21, 39], 12),
+    ("hc", [0, 1, 2, 3, 4, 5, 38, 39], 12),
+])
+def test_layer_matches_oracle(name, heads, tiles_per_head):
+    w = W[name]
+    say(f"[parity] workload {name}: {w.description}")
+    data = datagen.generate(w)
+    geom, out, _ = run_layer(w, data)
+    ks = w.k_per_head()
+    for hd in (heads if heads is not None else range(w.heads)):
+        nT = w.tiles_per_head()[hd]
+        tiles = list(range(nT)) if tiles_per_head is None else _sample_tiles(nT, tiles_per_head, seed=hd)
+        check_head(w, data, out, hd, ks, tiles)
+    # every head: lists are ascending, in range, k_hd long
+    idx = out["idx"].cpu().numpy()
+    for hd in range(w.heads):
+        nT, k = w.tiles_per_head()[hd], ks[hd]
+        row = idx[0, hd, :nT, :k]
+        assert np.all(np.diff(row, axis=1) > 0) and row.min() >= 0 and row.max() < nT
+
+
+def test_estimator_is_deterministic():
+    V = _lib()
+    w = W["480p"]
+    data = datagen.generate(w)
+    geom, out, (q, k, v, wq, wk) = run_layer(w, data)
+    first = out["scores"].clone()
+    for _ in range(2):
+        again = V.trippool_score(out["q_t"], out["k_t"], wq, wk, geom)
+        torch.cuda.synchronize()
+        assert torch.equal(again["scores"].view(torch.int32), first.view(torch.int32))
+
+
+def test_unpermute_inverts_permute_with_strided_raster():
+    """Q taken as a strided slice of a packed [B, N, 3, heads, d] tensor."""
+    V = _lib()
+    w = dataclasses.replace(W["480p"], heads=4, B=2)
+    g = geometry(w)
+    rng = np.random.default_rng(11)
+    packed = rng.integers(0, 1 << 16, size=(w.B, w.tokens, 3, w.heads, w.d), dtype=np.uint16)
+    packed &= np.uint16(0x7F7F)  # finite bf16 patterns
+    dev = to_dev_bf16(packed)
+    x = dev[:, :, 1]                                     # strides (N*3*H*d, 3*H*d, d, 1)
+    xt = V.tile_permute(x, g)
+    back = V.tile_unpermute(xt, g)
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16), x.contiguous().view(torch.int16))
+    want, _ = O.tile_permute(packed[1, :, 1, 3, :], w.grid, w.head_tiles()[3])
+    assert np.array_equal(bits_of(xt[1, 3]).reshape(-1, w.d), want)
+
+
+def _random_workload(grid, tiles, d, r, heads, seed, keep=None, k=None):
+    return datagen.Workload("custom", 1, heads, d, r, grid, tuple(tiles), keep, k, False, seed, "custom")
+
+
+@pytest.mark.parametrize("grid,tiles,d,r", [
+    ((5, 6, 20), [(2, 4, 16)], 64, 64),
+    ((3, 9, 17), [(1, 8, 16), (8, 4, 4)], 128, 32),
+    ((2, 8, 8), [(2, 8, 8)], 128, 64),
+])
+def test_dense_when_every_tile_is_kept(grid, tiles, d, r):
+    """k = all tiles: the sparse layer is plain softmax attention."""
+    w = _random_workload(grid, tiles, d, r, heads=len(tiles), seed=21)
+    say(f"[dense] grid {grid} tiles {tiles} d {d} r {r}")
+    data = datagen.generate(w)
+    ks = w.tiles_per_head()
+    geom, out, _ = run_layer(w, data, k_per_head=ks)
+    for hd in range(w.heads):
+        q, k, v = (O.bf16_bits_to_float(data[n][0, :, hd, :]) for n in ("q", "k", "v"))
+        od, lsed = O.dense_attention(q, k, v, 1.0 / math.sqrt(d))
+        compare_o(f32_of_bf16(out["o"][0, :, hd, :]), od, f"dense head {hd}")
+        pos = O.tiled_position(grid, tiles[hd % len(tiles)])
+        compare_lse(out["lse"][0, hd].cpu().numpy().reshape(-1)[pos], lsed, f"dense head {hd}")
+        check_head(w, data, out, hd, ks, list(range(ks[hd])))
+
+
+def test_single_tile_kept():
+    w = _random_workload((4, 16, 16), [(2, 8, 8)], 64, 32, heads=2, seed=5)
+    data = datagen.generate(w)
+    ks = [1, 1]
+    geom, out, _ = run_layer(w, data, k_per_head=ks)
+    for hd in range(2):
+        check_head(w, data, out, hd, ks, list(range(8)))
+
+
+def test_equal_scores_keep_the_lower_tile():
+    """Duplicate key tiles give exactly equal scores: the lower index must win
+    end to end, and the lists must match the oracle's."""
+    w = _random_workload((4, 16, 16), [(2, 8, 8)], 64, 32, heads=2, seed=9)
+    data = datagen.generate(w)
+    # copy key box 0 into boxes 3, 5 and 6 (raster positions of each box)
+    pos = O.tiled_position(w.grid, (2, 8, 8))
+    box = pos // 128
+    for hd in range(2):
+        src = data["k"][0, box == 0, hd, :]
+        order0 = np.argsort(pos[box == 0])
+        for dst in (3, 5, 6):
+            sel = np.flatnonzero(box == dst)
+            data["k"][0, sel[np.argsort(pos[sel])], hd, :] = src[order0]
+    ks = [2, 2]
+    geom, out, _ = run_layer(w, data, k_per_head=ks)
+    S = out["scores"].cpu().numpy()
+    assert np.array_equal(S[0, 0, :, 0], S[0, 0, :, 3]) and np.array_equal(S[0, 0, :, 0], S[0, 0, :, 6])
+    for hd in range(2):
+        check_head(w, data, out, hd, ks, list(range(8)))
+
+
+def test_topk_on_crafted_scores():
+    """Given scores full of exact ties and signed zeros, the GPU lists equal a
+    brute-force stable sort's, at several row lengths including the largest."""
+    V = _lib()
+    rng = np.random.default_rng(3)
+    for grid, tile, k in (((4, 16, 16), (2, 8, 8), 3), ((21, 30, 52), (4, 4, 8), 34),
+                          ((64, 64, 256), (4, 4, 8), 200)):
+        g = V.Geometry(1, 1, 128, grid, [tile])
+        nT = g.max_tiles()
+        say(f"[topk] {nT} key tiles, k {k}")
+        rows = min(nT, 256)
+        S = rng.integers(-4, 5, size=(rows, nT)).astype(np.float32) * np.float32(0.25)
+        S[S == 0] = np.where(rng.random((S == 0).sum()) < 0.5, np.float32(-0.0), np.float32(0.0))
+        S[::7] = rng.standard_normal((len(S[::7]), nT)).astype(np.float32)
+        full = np.full((nT, nT), np.float32(1.0))
+        full[:rows] = S
+        dev = torch.from_numpy(full).reshape(1, 1, nT, nT).cuda()
+        idx, bm = V.topk_mask(dev, g, [k])
+        torch.cuda.synchronize()
+        got = idx[0, 0, :rows].cpu().numpy()
+        assert np.array_equal(got, O.topk(S, k))
+        for rr in range(0, rows, 37):
+            assert got[rr].tolist() == O.topk_row_bruteforce(S[rr], k)
+        assert np.array_equal(bits_of(bm[0, 0, :rows]), O.bitmask(got, nT))
+        # the constant rows keep the first k tiles
+        assert np.all(idx[0, 0, rows:].cpu().numpy() == np.arange(k))
+
+
+def test_every_output_byte_is_written():
+    """Outputs pre-filled with garbage end up fully defined."""
+    w = W["hc"].with_heads(6)
+    data = datagen.generate(w)
+    geom = geometry(w)
+    nT = geom.max_tiles()
+    B, Hh, d = w.B, w.heads, w.d
+    g = lambda shape, dt: torch.full(shape, 0x7FC0 if dt == torch.bfloat16 else -1, dtype=torch.int16 if dt == torch.bfloat16 else torch.int32, device="cuda").view(dt)
+    bufs = {
+        "q_t": g((B, Hh, nT, 128, d), torch.bfloat16), "k_t": g((B, Hh, nT, 128, d), torch.bfloat16),
+        "v_t": g((B, Hh, nT, 128, d), torch.bfloat16), "o_t": g((B, Hh, nT, 128, d), torch.bfloat16),
+        "stats_q": g((B, Hh, nT, 3 * d), torch.bfloat16), "stats_k": g((B, Hh, nT, 3 * d), torch.bfloat16),
+        "feat_q": g((B, Hh, nT, w.r), torch.bfloat16), "feat_k": g((B, Hh, nT, w.r), torch.bfloat16),
+        "scores": g((B, Hh, nT, nT), torch.float32), "idx": g((B, Hh, nT, max(w.k_per_head())), torch.int32),
+        "bitmask": g((B, Hh, nT, (nT + 31) // 32), torch.int32).view(torch.uint32),
+        "lse": g((B, Hh, nT, 128), torch.float32), "o": g((B, w.tokens, Hh, d), torch.bfloat16),
+    }
+    geom, out, _ = run_layer(w, data, buffers=bufs)
+    ks = w.k_per_head()
+    for hd in (0, 1, 2):
+        check_head(w, data, out, hd, ks, _sample_tiles(w.tiles_per_head()[hd], 6, hd))
+    assert not torch.isnan(out["o"].float()).any()
+
+
+def test_invalid_call_raises_and_writes_nothing():
+    V = _lib()
+    w = W["tiny"]
+    geom = geometry(w)
+    s = torch.zeros((1, 2, 8, 8), dtype=torch.float32, device="cuda")
+    idx = torch.full((1, 2, 8, 4), 7, dtype=torch.int32, device="cuda")
+    with pytest.raises(V.VedaError):
+        V.topk_mask(s, geom, [9, 4], k_max=4, idx=idx, with_bitmask=False)
+    torch.cuda.synchronize()
+    assert torch.all(idx == 7)
