@@ -11,14 +11,19 @@
 //                   the two halves of its 128 logits), so row max and row sum
 //                   are in-lane plus one exchange between the half-waves.
 //   online softmax  base-2 with scale*log2(e) folded into one FMA; pad keys of
-//                   border tiles get -inf; rescale O by exp2(m_old - m_new).
-//   O^T += V_j^T P^T  32x32x16 bf16 MFMA; P is rounded to bf16 and used in
-//                   the very registers the softmax produced it in (the key
-//                   order of the contraction is chosen to match them).
-// K and V tiles (32 KiB each for d = 128) are double-buffered in LDS: the
-// global loads of tile i+1 are in flight while tile i is computed. V is
-// transposed on its way to LDS (an 8x8 register transpose per thread) so the
-// PV operand reads are contiguous. Query tiles of a head are dealt out so that
+//                   border tiles get -inf through a branch-free bias. The
+//                   running max only moves (and O is only rescaled) when a
+//                   row's max grows by more than 2^8, so most tiles skip the
+//                   rescale; P values up to 2^8 are exact in bf16's range.
+//   O^T += V_j^T P^T  32x32x16 bf16 MFMA; P is rounded to bf16 (hardware
+//                   pack) and used in the very registers the softmax produced
+//                   it in (the key order of the contraction is chosen to match).
+// K and V tiles (32 KiB each for d = 128) go global -> registers -> LDS; V is
+// transposed on the way (an 8x8 register transpose per thread) so PV operand
+// reads are contiguous. The global loads of tile i+1 are in flight while tile i
+// is computed. kStages = 2 double-buffers the LDS tiles (one workgroup per
+// CU); kStages = 1 single-buffers them so two workgroups share a CU and one's
+// softmax overlaps the other's MFMA. Query tiles of a head are dealt out so
 // each XCD works on a contiguous run of neighbouring query tiles, whose key
 // selections overlap, while all XCDs share the same head's K/V in the MALL.
 #include "veda_internal.hpp"
@@ -27,28 +32,35 @@ namespace veda {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;           // 8 waves: 4 query groups x 2 key halves
+constexpr int kHalfThreads = kThreads / 2;
 constexpr int kTok = VEDA_TILE_TOKENS;  // 128 keys / queries per tile
 constexpr int kPadK = 8;                // LDS row padding (bf16 elements)
+constexpr float kRescaleSlack = 8.0f;   // log2 of the largest unnormalised P
 
 template <int D>
 struct AttnShape {
-  static constexpr int KS = D + kPadK;                 // K row stride in LDS (elements)
-  static constexpr int VS = kTok + kPadK;              // V^T row stride in LDS (elements)
-  static constexpr int kKPasses = kTok * D / 8 / kThreads;   // 16-byte K loads per thread
-  static constexpr int kVBlocks = (kTok / 8) * (D / 8);      // 8x8 V blocks per tile
-  static constexpr int kDC = D / 16;                   // MFMA k-steps over the head dim
-  static constexpr int kDB = D / 32;                   // 32-row blocks of O^T
+  static constexpr int KS = D + kPadK;                  // K row stride in LDS (elements)
+  static constexpr int VS = kTok + kPadK;               // V^T row stride in LDS (elements)
+  static constexpr int kKPasses = kTok * D / 8 / kHalfThreads;  // 16-byte K loads per K-staging thread
+  static constexpr int kVBlocks = (kTok / 8) * (D / 8);         // 8x8 V blocks per tile
+  static constexpr int kDC = D / 16;                    // MFMA k-steps over the head dim
+  static constexpr int kDB = D / 32;                    // 32-row blocks of O^T
+  static_assert(kKPasses <= 8 && kVBlocks <= kHalfThreads, "staging layout");
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16_rne(lo)) | (uint32_t(f32_to_bf16_rne(hi)) << 16);
+  const floatx2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
 // Query tile handled by workgroup x of a head: the tiles of a head are split
@@ -59,42 +71,45 @@ __device__ __forceinline__ int32_t xcd_tile_order(int32_t x, int32_t n) {
   return xcd < r ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
 }
 
+// Threads 0..255 stage the K tile (kKPasses 16-byte rows pieces each),
+// threads 256..511 stage one 8x8 block of V each (8 rows of 16 bytes).
 template <int D>
 __device__ __forceinline__ void load_kv(const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt,
-                                        u32x4 (&kreg)[AttnShape<D>::kKPasses], u32x4 (&vreg)[8]) {
+                                        u32x4 (&st)[8]) {
   using S = AttnShape<D>;
   const int t = threadIdx.x;
+  if (t < kHalfThreads) {
 #pragma unroll
-  for (int p = 0; p < S::kKPasses; ++p)
-    kreg[p] = *reinterpret_cast<const u32x4*>(kt + (p * kThreads + t) * 8);
-  if (t < S::kVBlocks) {
-    const int kg = t / (D / 8), dg = t % (D / 8);
+    for (int p = 0; p < S::kKPasses; ++p)
+      st[p] = *reinterpret_cast<const u32x4*>(kt + (p * kHalfThreads + t) * 8);
+  } else if (t - kHalfThreads < S::kVBlocks) {
+    const int b = t - kHalfThreads, kg = b / (D / 8), dg = b % (D / 8);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) vreg[r] = *reinterpret_cast<const u32x4*>(vt + (kg * 8 + r) * D + dg * 8);
+    for (int r = 0; r < 8; ++r) st[r] = *reinterpret_cast<const u32x4*>(vt + (kg * 8 + r) * D + dg * 8);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void store_kv(uint16_t* ks, uint16_t* vs, const u32x4 (&kreg)[AttnShape<D>::kKPasses],
-                                         const u32x4 (&vreg)[8]) {
+__device__ __forceinline__ void store_kv(uint16_t* ks, uint16_t* vs, const u32x4 (&st)[8]) {
   using S = AttnShape<D>;
   const int t = threadIdx.x;
+  if (t < kHalfThreads) {
 #pragma unroll
-  for (int p = 0; p < S::kKPasses; ++p) {
-    const int e = (p * kThreads + t) * 8;  // element offset inside the dense tile
-    *reinterpret_cast<u32x4*>(ks + (e / D) * S::KS + e % D) = kreg[p];
-  }
-  if (t < S::kVBlocks) {
-    const int kg = t / (D / 8), dg = t % (D / 8);
-    // vreg[r] holds V[8kg + r][8dg .. 8dg+7]; row i of the transpose is
+    for (int p = 0; p < S::kKPasses; ++p) {
+      const int e = (p * kHalfThreads + t) * 8;  // element offset inside the dense tile
+      *reinterpret_cast<u32x4*>(ks + (e / D) * S::KS + e % D) = st[p];
+    }
+  } else if (t - kHalfThreads < S::kVBlocks) {
+    const int b = t - kHalfThreads, kg = b / (D / 8), dg = b % (D / 8);
+    // st[r] holds V[8kg + r][8dg .. 8dg+7]; row i of the transpose is
     // V[8kg .. 8kg+7][8dg + i].
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       u32x4 o;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const uint32_t a = vreg[2 * p][i / 2], b = vreg[2 * p + 1][i / 2];
-        o[p] = (i & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+        const uint32_t a = st[2 * p][i / 2], c = st[2 * p + 1][i / 2];
+        o[p] = (i & 1) ? ((a >> 16) | (c & 0xFFFF0000u)) : ((a & 0xFFFFu) | (c << 16));
       }
       *reinterpret_cast<u32x4*>(vs + (dg * 8 + i) * S::VS + kg * 8) = o;
     }
@@ -102,7 +117,7 @@ __device__ __forceinline__ void store_kv(uint16_t* ks, uint16_t* vs, const u32x4
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
+__global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
     GeoTable g, const uint16_t* __restrict__ q_t, const uint16_t* __restrict__ k_t,
     const uint16_t* __restrict__ v_t, const int32_t* __restrict__ idx, int32_t k_max, float scale_log2,
     uint16_t* __restrict__ o_t, float* __restrict__ lse) {
@@ -126,17 +141,20 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     return;
   }
 
+  // Wave (qg, half): queries 32qg..32qg+31 against keys 64half..64half+63 of
+  // every selected tile; the two halves are merged at the end.
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int qg = wave & 3, half = wave >> 2;
   const int l32 = lane % 32, h = lane / 32;
   const int32_t* sel = idx + (head_base + tq) * k_max;
   const int kh = hg.k;
   const uint16_t* kbase = k_t + head_base * tile_elems;
   const uint16_t* vbase = v_t + head_base * tile_elems;
 
-  // Q^T operand: lane (query 32w + l32, half h) holds d = 16dc + 8h .. +7.
+  // Q^T operand: lane (query 32qg + l32, half-wave h) holds d = 16dc + 8h .. +7.
   u32x4 qf[S::kDC];
   {
-    const uint16_t* qrow = q_t + (head_base + tq) * tile_elems + (wave * 32 + l32) * D + 8 * h;
+    const uint16_t* qrow = q_t + (head_base + tq) * tile_elems + (qg * 32 + l32) * D + 8 * h;
 #pragma unroll
     for (int dc = 0; dc < S::kDC; ++dc) qf[dc] = *reinterpret_cast<const u32x4*>(qrow + 16 * dc);
   }
@@ -149,11 +167,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
   float m_run = -__builtin_inff(), l_run = 0.0f;
 
   // Entries outside [0, nT_hd) are skipped (they contribute no keys).
-  u32x4 kreg[S::kKPasses], vreg[8];
+  u32x4 stage[8];
   int32_t j = sel[0];
   if (unsigned(j) < unsigned(hg.nT)) {
-    load_kv<D>(kbase + int64_t(j) * tile_elems, vbase + int64_t(j) * tile_elems, kreg, vreg);
-    store_kv<D>(ks_s[0], vs_s[0], kreg, vreg);
+    load_kv<D>(kbase + int64_t(j) * tile_elems, vbase + int64_t(j) * tile_elems, stage);
+    store_kv<D>(ks_s[0], vs_s[0], stage);
   }
   __syncthreads();
 
@@ -161,106 +179,136 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_fwd_kernel(
     const int cur = i & 1;
     const int32_t jn = (i + 1 < kh) ? sel[i + 1] : -1;
     const bool jn_ok = unsigned(jn) < unsigned(hg.nT);
-    if (jn_ok) load_kv<D>(kbase + int64_t(jn) * tile_elems, vbase + int64_t(jn) * tile_elems, kreg, vreg);
+    if (jn_ok) load_kv<D>(kbase + int64_t(jn) * tile_elems, vbase + int64_t(jn) * tile_elems, stage);
     if (unsigned(j) < unsigned(hg.nT)) {
-    // S^T[kb]: keys 32kb + (8(v/4) + 4h + v%4), query l32.
-    const uint16_t* ks = ks_s[cur];
-    floatx16 sacc[4];
+      // S^T[kb]: keys 32(2half + kb) + (8(v/4) + 4h + v%4), query l32.
+      const uint16_t* ks = ks_s[cur];
+      floatx16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.0f;
+        for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.0f;
+        const uint16_t* krow = ks + (64 * half + 32 * kb + l32) * S::KS + 8 * h;
 #pragma unroll
-      for (int dc = 0; dc < S::kDC; ++dc) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + (32 * kb + l32) * S::KS + 16 * dc + 8 * h);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[dc]), sacc[kb], 0, 0, 0);
-      }
-    }
-
-    // Pad keys of a border tile take no part.
-    const BoxExtent e = box_extent(g, hg, j);
-    // Branch-free: the bias is +0 for a real key and -inf for a pad key,
-    // built from integer compares (no per-element control flow).
-    if (!box_is_full(hg, e)) {
-      const int pwm = (1 << hg.lpw) - 1, phm = (1 << hg.lph) - 1, sh = hg.lpw + hg.lph;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int sig = 32 * kb + 8 * (v / 4) + 4 * h + (v % 4);
-          const uint32_t real = uint32_t((sig & pwm) < e.vw) & uint32_t(((sig >> hg.lpw) & phm) < e.vh) &
-                                uint32_t((sig >> sh) < e.vt);
-          sacc[kb][v] += __uint_as_float((real - 1u) & 0xFF800000u);
-        }
-    }
-
-    // Online softmax in base 2.
-    float mx = sacc[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.0f;
-    u32x4 pf[4][2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], scale_log2, -m_new));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v + 1], scale_log2, -m_new));
-        psum += p0 + p1;
-        pf[kb][v / 8][(v % 8) / 2] = pack_bf16x2(p0, p1);
-      }
-    }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < S::kDB; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
-
-    // O^T[db] += V^T P^T over the 128 keys, 16 at a time: k-slot v' of half h
-    // is key 32kb + 16c2 + 8(v'/4) + 4h + v'%4.
-    const uint16_t* vs = vs_s[cur];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-#pragma unroll
-        for (int db = 0; db < S::kDB; ++db) {
-          const uint16_t* vrow = vs + (32 * db + l32) * S::VS + 32 * kb + 16 * c2 + 4 * h;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-          const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[kb][c2]), oacc[db], 0, 0, 0);
+        for (int dc = 0; dc < S::kDC; ++dc) {
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 16 * dc);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[dc]), sacc[kb], 0, 0, 0);
         }
       }
-    }
 
+      // Pad keys of a border tile get -inf: the box's real-slot mask is built
+      // once per tile with uniform ops; each lane pulls its bits (its keys are
+      // bits 32kb + 8(v/4) + v%4 of the mask shifted by 64half + 4h).
+      const BoxExtent e = box_extent(g, hg, j);
+      if (!box_is_full(hg, e)) {
+        const uint64_t wm = box_slot_mask64(hg, e, 64 * half) >> (4 * h);
+        const uint32_t wlo = uint32_t(wm), whi = uint32_t(wm >> 32);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const uint32_t real = ((kb ? whi : wlo) >> (8 * (v / 4) + (v % 4))) & 1u;
+            sacc[kb][v] += __uint_as_float((real - 1u) & 0xFF800000u);
+          }
+      }
+
+      // Online softmax in base 2 with a lazily moved running max.
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < S::kDB; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+      }
+      // A half that has seen only pad keys so far keeps m = -inf; its
+      // exponents must then still be exp2(-inf) = 0, not NaN.
+      const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
+      float psum = 0.0f;
+      u32x4 pf[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], scale_log2, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v + 1], scale_log2, -m_use));
+          psum += p0 + p1;
+          pf[kb][v / 8][(v % 8) / 2] = pack_bf16x2(p0, p1);
+        }
+      }
+      l_run += psum;
+
+      // O^T[db] += V^T P^T over this half's 64 keys, 16 at a time: k-slot v'
+      // of half-wave h is key 64half + 32kb + 16c2 + 8(v'/4) + 4h + v'%4.
+      const uint16_t* vs = vs_s[cur];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+          for (int db = 0; db < S::kDB; ++db) {
+            const uint16_t* vrow = vs + (32 * db + l32) * S::VS + 64 * half + 32 * kb + 16 * c2 + 4 * h;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+            const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+            oacc[db] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[kb][c2]), oacc[db], 0, 0, 0);
+          }
+        }
+      }
     }  // valid tile
-    if (jn_ok) store_kv<D>(ks_s[cur ^ 1], vs_s[cur ^ 1], kreg, vreg);
+    if (jn_ok) store_kv<D>(ks_s[cur ^ 1], vs_s[cur ^ 1], stage);
     j = jn;
     __syncthreads();
   }
 
-  // Epilogue: combine the half-wave partial sums, normalise, write O and LSE.
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.0f / l_tot;
-  uint16_t* orow = o_tile + (wave * 32 + l32) * D;
+  // Merge the two key halves through LDS (the K/V buffers are free now):
+  // m = max(m0, m1), O = O0 2^(m0-m) + O1 2^(m1-m), l likewise.
+  float* red = reinterpret_cast<float*>(&ks_s[0][0]);       // [4][kDB*16][64] partial O^T
+  float* red_ml = red + 4 * S::kDB * 16 * 64;                // [4][2][64] m, l
+  static_assert(sizeof(ks_s) >= (4 * S::kDB * 16 * 64 + 4 * 2 * 64) * sizeof(float), "merge space");
+  const float l_half = l_run + __shfl_xor(l_run, 32, 64);
+  if (half == 1) {
 #pragma unroll
-  for (int db = 0; db < S::kDB; ++db) {
+    for (int db = 0; db < S::kDB; ++db)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      u32x2 w;
-      w[0] = pack_bf16x2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv);
-      w[1] = pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv);
-      *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g4 + 4 * h) = w;
-    }
+      for (int v = 0; v < 16; ++v) red[((qg * S::kDB + db) * 16 + v) * 64 + lane] = oacc[db][v];
+    red_ml[(qg * 2 + 0) * 64 + lane] = m_run;
+    red_ml[(qg * 2 + 1) * 64 + lane] = l_half;
   }
-  if (lse_tile && h == 0) lse_tile[wave * 32 + l32] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+  __syncthreads();
+  if (half == 0) {
+    const float m1 = red_ml[(qg * 2 + 0) * 64 + lane];
+    const float l1 = red_ml[(qg * 2 + 1) * 64 + lane];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+    const float l_tot = l_half * a0 + l1 * a1;
+    const float inv = 1.0f / l_tot;
+    const float c0 = a0 * inv, c1 = a1 * inv;
+    uint16_t* orow = o_tile + (qg * 32 + l32) * D;
+#pragma unroll
+    for (int db = 0; db < S::kDB; ++db) {
+      float o[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[v] = oacc[db][v] * c0 + red[((qg * S::kDB + db) * 16 + v) * 64 + lane] * c1;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        u32x2 w;
+        w[0] = pack_bf16x2(o[4 * g4 + 0], o[4 * g4 + 1]);
+        w[1] = pack_bf16x2(o[4 * g4 + 2], o[4 * g4 + 3]);
+        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g4 + 4 * h) = w;
+      }
+    }
+    if (lse_tile && h == 0) lse_tile[qg * 32 + l32] = (m + __log2f(l_tot)) * 0.69314718055994530942f;
+  }
 }
 
 }  // namespace

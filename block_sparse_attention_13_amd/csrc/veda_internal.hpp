@@ -29,7 +29,12 @@ struct BoxExtent {
   int32_t vt, vh, vw;  // real extent along t, y, x
 };
 
-__device__ __forceinline__ BoxExtent box_extent(const GeoTable& g, const HeadGeo& hg, int32_t tau) {
+#define VEDA_HD __host__ __device__ __forceinline__
+
+VEDA_HD int32_t imin(int32_t a, int32_t b) { return a < b ? a : b; }
+VEDA_HD int32_t imax(int32_t a, int32_t b) { return a > b ? a : b; }
+
+VEDA_HD BoxExtent box_extent(const GeoTable& g, const HeadGeo& hg, int32_t tau) {
   const int32_t pt = 1 << hg.lpt, ph = 1 << hg.lph, pw = 1 << hg.lpw;
   const int32_t bx = tau % hg.nTw;
   const int32_t rest = tau / hg.nTw;
@@ -39,22 +44,43 @@ __device__ __forceinline__ BoxExtent box_extent(const GeoTable& g, const HeadGeo
   e.t0 = bt * pt;
   e.y0 = by * ph;
   e.x0 = bx * pw;
-  e.vt = min(pt, g.T - e.t0);
-  e.vh = min(ph, g.H - e.y0);
-  e.vw = min(pw, g.W - e.x0);
+  e.vt = imin(pt, g.T - e.t0);
+  e.vh = imin(ph, g.H - e.y0);
+  e.vw = imin(pw, g.W - e.x0);
   return e;
 }
 
-__device__ __forceinline__ bool box_is_full(const HeadGeo& hg, const BoxExtent& e) {
+VEDA_HD bool box_is_full(const HeadGeo& hg, const BoxExtent& e) {
   return e.vt == (1 << hg.lpt) && e.vh == (1 << hg.lph) && e.vw == (1 << hg.lpw);
 }
 
 // Slot sigma of a box is real iff each of its offsets lies inside the real extent.
-__device__ __forceinline__ bool slot_is_real(const HeadGeo& hg, const BoxExtent& e, int32_t sigma) {
+VEDA_HD bool slot_is_real(const HeadGeo& hg, const BoxExtent& e, int32_t sigma) {
   const int32_t sx = sigma & ((1 << hg.lpw) - 1);
   const int32_t sy = (sigma >> hg.lpw) & ((1 << hg.lph) - 1);
   const int32_t st = sigma >> (hg.lpw + hg.lph);
   return st < e.vt && sy < e.vh && sx < e.vw;
+}
+
+// 64 bits of a periodic slot pattern: bit b (slot base + b) is set iff
+// (slot mod 2^lg_period) < lim. Slots are numbered 0..127 inside a box.
+VEDA_HD uint64_t periodic_slot_bits(int lg_period, int lim, int base) {
+  if (lg_period >= 6) {  // period 64 or 128: the condition is a plain prefix
+    const int n = imin(imax(lim - (lg_period == 7 ? base : 0), 0), 64);
+    return n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+  }
+  const int period = 1 << lg_period;
+  uint64_t w = lim >= period ? ((1ull << period) - 1ull) : ((1ull << lim) - 1ull);
+  for (int p = period; p < 64; p <<= 1) w |= w << p;
+  return w;
+}
+
+// Bits base..base+63 of the box's real-slot mask (bit sigma set iff slot sigma
+// holds a real token): x offset < vw, y offset < vh and t offset < vt.
+VEDA_HD uint64_t box_slot_mask64(const HeadGeo& hg, const BoxExtent& e, int base) {
+  const int lxy = hg.lpw + hg.lph;
+  return periodic_slot_bits(hg.lpw, e.vw, base) & periodic_slot_bits(lxy, e.vh << hg.lpw, base) &
+         periodic_slot_bits(7, e.vt << lxy, base);
 }
 
 // bf16 <-> fp32 (round to nearest even; inputs here are always finite).
