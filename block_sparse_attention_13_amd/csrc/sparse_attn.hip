@@ -24,8 +24,9 @@
 // transposed on the way (each thread turns 16 keys x 4 channels into eight
 // 16-byte chunks of V^T in MFMA key order) so each PV operand is one 16-byte
 // read; the V^T rows are XOR-swizzled so chunk writes and operand reads are
-// free of bank conflicts. The LDS tiles are double-buffered: the global loads
-// of tile i+1 are in flight while tile i is computed. Query tiles of a head are dealt out so
+// free of bank conflicts. The LDS tiles are double-buffered and the staging
+// is pipelined two tiles deep (loads get a whole iteration to land; LDS
+// stores run under the PV MFMAs). Query tiles of a head are dealt out so
 // each XCD works on a contiguous run of neighbouring query tiles, whose key
 // selections overlap, while all XCDs share the same head's K/V in the MALL.
 #include "veda_internal.hpp"
@@ -149,10 +150,12 @@ struct WaveState {
 };
 
 // One selected key tile j for one wave: S^T, mask, online softmax, PV.
-template <int D>
+// after_s() runs once the S^T MFMAs are issued and after_pv() once the PV
+// MFMAs are issued, so staging work placed there overlaps the matrix cores.
+template <int D, class AfterS, class AfterPV>
 __device__ __forceinline__ void attend_tile(WaveState<D>& w, const uint16_t* ks, const uint16_t* vs,
                                             const GeoTable& g, const HeadGeo& hg, int32_t j, int half, int h,
-                                            int l32, float scale_log2) {
+                                            int l32, float scale_log2, AfterS&& after_s, AfterPV&& after_pv) {
   using S = AttnShape<D>;
   // S^T[kb]: keys 64half + 32kb + (8(v/4) + 4h + v%4), query l32.
   floatx16 sacc[2];
@@ -167,6 +170,7 @@ __device__ __forceinline__ void attend_tile(WaveState<D>& w, const uint16_t* ks,
       sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(w.qf[dc]), sacc[kb], 0, 0, 0);
     }
   }
+  after_s();
 
   // Pad keys of a border tile get -inf: the box's real-slot mask is built
   // once per tile with uniform ops; each lane pulls its bits (its keys are
@@ -235,10 +239,15 @@ __device__ __forceinline__ void attend_tile(WaveState<D>& w, const uint16_t* ks,
       }
     }
   }
+  after_pv();
 }
 
-// The tile loop of one wave; kStageK selects which half of the next tile this
-// wave stages. Every thread runs the same number of iterations and barriers.
+// The tile loop of one wave; kStageK selects which half of each tile this
+// wave stages. Staging is pipelined two tiles deep: during iteration i the
+// staging registers hold tile i+1, loaded at the end of iteration i-1; once
+// the PV MFMAs of tile i are issued they go to the free LDS buffer and the
+// loads of tile i+2 start, so every load has a whole iteration to land and
+// the LDS stores run under the PV MFMAs. Every thread runs the same number of iterations and barriers.
 template <int D, bool kStageK>
 __device__ __forceinline__ void attend_all(WaveState<D>& w, uint16_t (&ks_s)[2][kTok * AttnShape<D>::KS],
                                            uint16_t (&vs_s)[2][D * kTok], const GeoTable& g, const HeadGeo& hg,
@@ -246,27 +255,33 @@ __device__ __forceinline__ void attend_all(WaveState<D>& w, uint16_t (&ks_s)[2][
                                            int half, int h, int l32, float scale_log2) {
   const int64_t tile_elems = int64_t(kTok) * D;
   const unsigned nT = unsigned(hg.nT);
+  const int kh = hg.k;
   Stager<D, kStageK> stg;
   stg.t = threadIdx.x % kHalfThreads;
   // Entries outside [0, nT_hd) contribute no keys; tile 0 stands in as a
   // harmless load source so every load is unconditional.
+  auto src = [&](int32_t jt) { return unsigned(jt) < nT ? jt : 0; };
   int32_t j = sel[0];
-  {
-    const int32_t js = unsigned(j) < nT ? j : 0;
-    stg.load(kbase + int64_t(js) * tile_elems, vbase + int64_t(js) * tile_elems);
-    stg.store(ks_s[0], vs_s[0]);
-  }
+  stg.load(kbase + int64_t(src(j)) * tile_elems, vbase + int64_t(src(j)) * tile_elems);
+  stg.store(ks_s[0], vs_s[0]);
+  int32_t jn = kh > 1 ? sel[1] : 0;
+  stg.load(kbase + int64_t(src(jn)) * tile_elems, vbase + int64_t(src(jn)) * tile_elems);
   __syncthreads();
-  const int kh = hg.k;
   for (int i = 0; i < kh; ++i) {
     const int cur = i & 1;
     const bool has_next = i + 1 < kh;
-    const int32_t jn = has_next ? sel[i + 1] : 0;
-    const int32_t js = unsigned(jn) < nT ? jn : 0;
-    stg.load(kbase + int64_t(js) * tile_elems, vbase + int64_t(js) * tile_elems);
-    if (unsigned(j) < nT) attend_tile<D>(w, ks_s[cur], vs_s[cur], g, hg, j, half, h, l32, scale_log2);
-    if (has_next) stg.store(ks_s[cur ^ 1], vs_s[cur ^ 1]);
+    const int32_t jnn = i + 2 < kh ? sel[i + 2] : 0;
+    auto nothing = [] {};
+    auto restage = [&] {  // tile i+1 -> free LDS buffer, then start loading tile i+2
+      if (has_next) stg.store(ks_s[cur ^ 1], vs_s[cur ^ 1]);
+      stg.load(kbase + int64_t(src(jnn)) * tile_elems, vbase + int64_t(src(jnn)) * tile_elems);
+    };
+    if (unsigned(j) < nT)
+      attend_tile<D>(w, ks_s[cur], vs_s[cur], g, hg, j, half, h, l32, scale_log2, nothing, restage);
+    else
+      restage();
     j = jn;
+    jn = jnn;
     __syncthreads();
   }
 }
