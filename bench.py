@@ -158,7 +158,7 @@ def main():
             ev[0].record(stream)
         V.tile_permute(q, geom, bufs["q_t"])
         V.tile_permute(k, geom, bufs["k_t"])
-        V.tile_permute(v, geom, bufs["v_t"])
+        V.tile_permute(v, geom, bufs["v_t"], layout=V.CHANNEL_MAJOR)
         if ev is not None:
             ev[1].record(stream)
         V.trippool_score(bufs["q_t"], bufs["k_t"], wq, wk, geom,

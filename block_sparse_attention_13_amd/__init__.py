@@ -6,6 +6,7 @@ C ABI, and raises VedaError on a non-zero status. No computation happens in
 Python: the five steps of the layer are HIP kernels.
 
   tile_permute     raster [B, N, heads, d] -> tiled [B, heads, nT_max, 128, d]
+                   (token-major) or [B, heads, nT_max, d, 128] (channel-major)
   trippool_score   tiled Q, K + W_q, W_k  -> stats, features, tile scores
   topk_mask        scores -> ascending index lists (+ bitmask) per query tile
   sparse_attn_fwd  tiled Q, K, V + index lists -> tiled O (+ LSE)
@@ -25,9 +26,11 @@ from . import _lib
 from ._lib import VedaError
 
 __all__ = ["Geometry", "VedaError", "tile_permute", "tile_unpermute", "trippool_score", "topk_mask",
-           "sparse_attn_fwd", "layer_forward", "TILE_TOKENS"]
+           "sparse_attn_fwd", "layer_forward", "TILE_TOKENS", "TOKEN_MAJOR", "CHANNEL_MAJOR"]
 
 TILE_TOKENS = _lib.VEDA_TILE_TOKENS
+TOKEN_MAJOR = _lib.VEDA_TILED_TOKEN_MAJOR
+CHANNEL_MAJOR = _lib.VEDA_TILED_CHANNEL_MAJOR
 
 
 @dataclasses.dataclass
@@ -92,15 +95,28 @@ def _tiled_shape(geom: Geometry, last: int):
     return (geom.B, geom.n_heads, geom.max_tiles(), TILE_TOKENS, last)
 
 
-def tile_permute(x: torch.Tensor, geom: Geometry, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+def _tiled_cm_shape(geom: Geometry):
+    return (geom.B, geom.n_heads, geom.max_tiles(), geom.head_dim, TILE_TOKENS)
+
+
+def tile_permute(x: torch.Tensor, geom: Geometry, out: Optional[torch.Tensor] = None,
+                 layout: int = TOKEN_MAJOR) -> torch.Tensor:
     """Gather a raster tensor [B, N, heads, d] (bf16, any strides with unit
-    channel stride) into head-tiled order [B, heads, nT_max, 128, d]."""
+    channel stride) into head-tiled order: [B, heads, nT_max, 128, d] for
+    TOKEN_MAJOR, [B, heads, nT_max, d, 128] for CHANNEL_MAJOR (each tile
+    transposed; the layout sparse_attn_fwd takes V in)."""
     s = _raster_strides(x, geom, "x")
-    shape = _tiled_shape(geom, geom.head_dim)
+    if layout == TOKEN_MAJOR:
+        shape = _tiled_shape(geom, geom.head_dim)
+    elif layout == CHANNEL_MAJOR:
+        shape = _tiled_cm_shape(geom)
+    else:
+        raise ValueError("layout must be TOKEN_MAJOR or CHANNEL_MAJOR")
     if out is None:
         out = torch.empty(shape, dtype=torch.bfloat16, device=x.device)
     _need(out, torch.bfloat16, shape, "out")
-    _lib.check(_lib.lib.veda_tile_permute(geom.c, x.data_ptr(), s, out.data_ptr(), _stream(x)), "veda_tile_permute")
+    _lib.check(_lib.lib.veda_tile_permute(geom.c, x.data_ptr(), s, out.data_ptr(), int(layout), _stream(x)),
+               "veda_tile_permute")
     return out
 
 
@@ -180,11 +196,14 @@ def sparse_attn_fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, idx
                     k_per_head: Sequence[int], scale: Optional[float] = None, with_lse: bool = True,
                     o_t: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Tile-skipping attention over the selected key tiles; returns tiled O
-    (bf16) and LSE [B, heads, nT_max, 128] (fp32, natural log)."""
+    """Tile-skipping attention over the selected key tiles. Q and K are
+    token-major tiles, V channel-major ([B, heads, nT_max, d, 128]); returns
+    tiled O (bf16, token-major) and LSE [B, heads, nT_max, 128] (fp32,
+    natural log)."""
     tshape = _tiled_shape(geom, geom.head_dim)
-    for name, t in (("q_tiled", q_t), ("k_tiled", k_t), ("v_tiled", v_t)):
+    for name, t in (("q_tiled", q_t), ("k_tiled", k_t)):
         _need(t, torch.bfloat16, tshape, name)
+    _need(v_t, torch.bfloat16, _tiled_cm_shape(geom), "v_tiled")
     if idx.dim() != 4:
         raise ValueError("idx must be [B, heads, nT_max, k_max]")
     k_max = idx.shape[3]
@@ -216,7 +235,7 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.
     b = buffers if buffers is not None else {}
     b["q_t"] = tile_permute(q, geom, b.get("q_t"))
     b["k_t"] = tile_permute(k, geom, b.get("k_t"))
-    b["v_t"] = tile_permute(v, geom, b.get("v_t"))
+    b["v_t"] = tile_permute(v, geom, b.get("v_t"), layout=CHANNEL_MAJOR)
     est = trippool_score(b["q_t"], b["k_t"], w_q, w_k, geom,
                          {n: b[n] for n in ("stats_q", "stats_k", "feat_q", "feat_k", "scores")}
                          if "scores" in b else None)

@@ -15,6 +15,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libveda.so"
 VEDA_TILE_TOKENS = 128
 VEDA_MAX_HEADS = 128
 VEDA_MAX_TILES = 8192
+VEDA_TILED_TOKEN_MAJOR = 0
+VEDA_TILED_CHANNEL_MAJOR = 1
 
 STATUS = {
     0: "VEDA_OK", -1: "VEDA_ERR_NULL", -2: "VEDA_ERR_SHAPE", -3: "VEDA_ERR_TILE", -4: "VEDA_ERR_K",
@@ -58,7 +60,7 @@ def _load():
     lib.veda_num_tiles.restype = ctypes.c_int
     lib.veda_max_tiles.argtypes = [POINTER(VedaGeom)]
     lib.veda_max_tiles.restype = ctypes.c_int
-    lib.veda_tile_permute.argtypes = [POINTER(VedaGeom), c_void_p, VedaRasterStrides, c_void_p, c_void_p]
+    lib.veda_tile_permute.argtypes = [POINTER(VedaGeom), c_void_p, VedaRasterStrides, c_void_p, c_int32, c_void_p]
     lib.veda_tile_permute.restype = ctypes.c_int
     lib.veda_tile_unpermute.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, VedaRasterStrides, c_void_p]
     lib.veda_tile_unpermute.restype = ctypes.c_int
@@ -93,4 +95,5 @@ def int_array(values):
 
 
 __all__ = ["lib", "VedaGeom", "VedaGrid", "VedaTile", "VedaRasterStrides", "VedaError", "check", "int_array",
-           "EXPORTS", "STATUS", "VEDA_TILE_TOKENS", "VEDA_MAX_HEADS", "VEDA_MAX_TILES", "c_uint32"]
+           "EXPORTS", "STATUS", "VEDA_TILE_TOKENS", "VEDA_MAX_HEADS", "VEDA_MAX_TILES",
+           "VEDA_TILED_TOKEN_MAJOR", "VEDA_TILED_CHANNEL_MAJOR", "c_uint32"]

@@ -1,5 +1,8 @@
 // Head-conditioned re-tiling and its inverse (Veda page, "Architecture",
 // Principle 02 "Head-Conditioned Tile Geometry"; "Head-Aware Tile Search").
+// Tiles are written token-major [.., 128, d] or channel-major [.., d, 128];
+// the attention kernel takes V channel-major so its tiles can be copied into
+// LDS as they are.
 //
 // Pure data movement, bound by HBM bandwidth. One workgroup moves one
 // 128-token box of one (batch, head): each token row is d bf16 values
@@ -57,6 +60,48 @@ __global__ __launch_bounds__(kThreads) void tile_permute_kernel(GeoTable g, cons
   for (int p = 0; p < M::kPasses; ++p) dst[(row0 + p * M::kRowsPerPass) * M::kChunks + chunk] = val[p];
 }
 
+// Channel-major tiles [.., d, 128]: each thread moves an 8-slot x 8-channel
+// block, read as 8 token rows of 16 bytes and written, transposed in
+// registers, as 8 channel rows of 16 bytes. Lanes run along the slot groups,
+// so each output row (128 slots, 256 bytes) is written by 16 adjacent lanes.
+template <int D>
+__global__ __launch_bounds__(kThreads) void tile_permute_cm_kernel(GeoTable g, const uint16_t* __restrict__ x,
+                                                                  int64_t sb, int64_t sn, int64_t sh,
+                                                                  uint16_t* __restrict__ xt) {
+  constexpr int kBlocks = (VEDA_TILE_TOKENS / 8) * (D / 8);
+  const int32_t tau = blockIdx.x, hd = blockIdx.y, b = blockIdx.z;
+  const HeadGeo hg = g.h[hd];
+  if (int(threadIdx.x) >= kBlocks) return;
+  const int sg = threadIdx.x % 16, cg = threadIdx.x / 16;
+  uint16_t* dst = xt + ((int64_t(b) * g.heads + hd) * g.nT_max + tau) * VEDA_TILE_TOKENS * D;
+  uint4 in[8];
+  if (tau < hg.nT) {
+    const BoxExtent e = box_extent(g, hg, tau);
+    const uint16_t* src = x + int64_t(b) * sb + int64_t(hd) * sh + cg * 8;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int64_t n = raster_of_slot(g, hg, e, 8 * sg + r);
+      in[r] = n >= 0 ? *reinterpret_cast<const uint4*>(src + n * sn) : make_uint4(0, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) in[r] = make_uint4(0, 0, 0, 0);
+  }
+  // in[r] holds channels 8cg..8cg+7 of slot 8sg + r; row i of the output is
+  // channel 8cg + i over slots 8sg..8sg+7.
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(in);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t o[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t a = w[(2 * p) * 4 + i / 2], c = w[(2 * p + 1) * 4 + i / 2];
+      o[p] = (i & 1) ? ((a >> 16) | (c & 0xFFFF0000u)) : ((a & 0xFFFFu) | (c << 16));
+    }
+    *reinterpret_cast<uint4*>(dst + (8 * cg + i) * VEDA_TILE_TOKENS + 8 * sg) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void tile_unpermute_kernel(GeoTable g, const uint16_t* __restrict__ xt,
                                                                  uint16_t* __restrict__ x, int64_t sb, int64_t sn,
@@ -84,8 +129,15 @@ __global__ __launch_bounds__(kThreads) void tile_unpermute_kernel(GeoTable g, co
 }  // namespace
 
 hipError_t launch_tile_permute(const GeoTable& g, const uint16_t* x, int64_t sb, int64_t sn, int64_t sh,
-                               uint16_t* xt, hipStream_t s) {
+                               uint16_t* xt, bool channel_major, hipStream_t s) {
   const dim3 grid(g.nT_max, g.heads, g.B);
+  if (channel_major) {
+    if (g.d == 128)
+      tile_permute_cm_kernel<128><<<grid, kThreads, 0, s>>>(g, x, sb, sn, sh, xt);
+    else
+      tile_permute_cm_kernel<64><<<grid, kThreads, 0, s>>>(g, x, sb, sn, sh, xt);
+    return hipGetLastError();
+  }
   if (g.d == 128)
     tile_permute_kernel<128><<<grid, kThreads, 0, s>>>(g, x, sb, sn, sh, xt);
   else

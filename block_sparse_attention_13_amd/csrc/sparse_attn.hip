@@ -10,8 +10,11 @@
 // selected key tile j:
 //   S^T = K_j Q^T   32x32x16 bf16 MFMA, fp32 accumulate. Computing S
 //                   transposed puts one query per lane (lanes l and l+32 hold
-//                   the two halves of its 128 logits), so row max and row sum
-//                   are in-lane plus one exchange between the half-waves.
+//                   the two halves of its logits), so row max and row sum are
+//                   in-lane plus one exchange between the half-waves. Lane l
+//                   of a 32-key block feeds key row pi(l) (bits 2 and 3 of l
+//                   swapped), so each lane ends up holding runs of 8
+//                   consecutive keys.
 //   online softmax  base-2 with scale*log2(e) folded into one FMA; pad keys of
 //                   border tiles get -inf through a branch-free bias. The
 //                   running max only moves (and O is only rescaled) when a
@@ -19,16 +22,17 @@
 //                   rescale; P values up to 2^8 are exact in bf16's range.
 //   O^T += V_j^T P^T  32x32x16 bf16 MFMA; P is rounded to bf16 (hardware
 //                   pack) and used in the very registers the softmax produced
-//                   it in (the key order of the contraction is chosen to match).
-// K and V tiles (32 KiB each for d = 128) go global -> registers -> LDS; V is
-// transposed on the way (each thread turns 16 keys x 4 channels into eight
-// 16-byte chunks of V^T in MFMA key order) so each PV operand is one 16-byte
-// read; the V^T rows are XOR-swizzled so chunk writes and operand reads are
-// free of bank conflicts. The LDS tiles are double-buffered and the staging
-// is pipelined two tiles deep (loads get a whole iteration to land; LDS
-// stores run under the PV MFMAs). Query tiles of a head are dealt out so
-// each XCD works on a contiguous run of neighbouring query tiles, whose key
-// selections overlap, while all XCDs share the same head's K/V in the MALL.
+//                   it in: 8 consecutive keys, so each V^T operand is one
+//                   16-byte chunk of a channel row.
+// K (token-major) and V (channel-major) tiles go from global memory straight
+// into LDS with the gfx950 LDS-DMA loads (no registers, no LDS store
+// instructions): every wave copies eight 1-KiB chunks, four rows each, and
+// picks each lane's source chunk so that the rows land XOR-swizzled (position
+// = chunk ^ (row & 15)), which keeps the MFMA operand reads free of bank
+// conflicts. The LDS tiles are double-buffered: the copy of tile i+1 runs
+// under the compute of tile i. Query tiles of a head are dealt out so each XCD
+// works on a contiguous run of neighbouring query tiles, whose key selections
+// overlap, while all XCDs share the same head's K/V in the MALL.
 #include "veda_internal.hpp"
 
 namespace veda {
@@ -42,20 +46,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 512;           // 8 waves: 4 query groups x 2 key halves
-constexpr int kHalfThreads = kThreads / 2;
+constexpr int kWaves = kThreads / 64;
 constexpr int kTok = VEDA_TILE_TOKENS;  // 128 keys / queries per tile
-constexpr int kPadK = 8;                // LDS row padding (bf16 elements)
 constexpr float kRescaleSlack = 8.0f;   // log2 of the largest unnormalised P
 
 template <int D>
 struct AttnShape {
-  static constexpr int KS = D + kPadK;                  // K row stride in LDS (elements)
-  static constexpr int kKPasses = kTok * D / 8 / kHalfThreads;  // 16-byte K loads per K-staging thread
-  static constexpr int kVQuads = D / 4;                 // 4-channel groups of V
-  static constexpr int kVBlocks = (kTok / 16) * kVQuads;        // 16-key x 4-channel V blocks per tile
+  static constexpr int kTileElems = kTok * D;           // one K or V tile (bf16 elements)
+  static constexpr int kKPos = D / 8;                   // 16-byte positions per K row
+  static constexpr int kKRowsPerChunk = 64 / kKPos;     // K rows per 1-KiB DMA chunk
+  static constexpr int kChunks = kTileElems / 512;      // 1-KiB chunks per tile (K or V)
+  static constexpr int kChunksPerWave = 2 * kChunks / kWaves;
   static constexpr int kDC = D / 16;                    // MFMA k-steps over the head dim
   static constexpr int kDB = D / 32;                    // 32-row blocks of O^T
-  static_assert(kKPasses <= 8 && kVBlocks <= kHalfThreads, "staging layout");
+  static_assert(kChunks % (kWaves / 2) == 0, "K and V chunks split over 4 waves each");
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -66,15 +70,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
-// V^T in LDS: row d (a channel) holds the tile's 128 keys as 16 chunks of 16
-// bytes. Chunk c = 2G + h holds keys 16G + 4h + {0..3} and 16G + 8 + 4h + {0..3},
-// exactly the eight keys lane half h feeds to one PV MFMA; it is stored at
-// position c ^ swz(d). swz makes both the chunk writes (rows 4q + i, 16 or 8
-// consecutive q) and the operand reads (16 or 8 consecutive rows) hit distinct
-// bank groups for 64 and for 32 LDS banks.
-__device__ __forceinline__ int vt_swizzle(int d) {
-  return ((d ^ (d >> 3)) & 3) | (d & 4) | ((((d >> 3) ^ (d >> 5)) & 1) << 3);
-}
+// Key row fed by lane l of a 32-key block: bits 2 and 3 of l swapped.
+__device__ __forceinline__ int key_perm(int l) { return (l & ~12) | ((l & 4) << 1) | ((l & 8) >> 1); }
 
 // Query tile handled by workgroup x of a head: the tiles of a head are split
 // into 8 contiguous runs, run r going to the workgroups x with x % 8 == r
@@ -84,106 +81,77 @@ __device__ __forceinline__ int32_t xcd_tile_order(int32_t x, int32_t n) {
   return xcd < r ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
 }
 
-// Staging of the next K/V tile, specialised by role so that the staging
-// registers are written on one path only: waves 0-3 stage K (kKPasses
-// 16-byte row pieces per thread), waves 4-7 stage V as 16-key x 4-channel
-// blocks (16 rows of 8 bytes; rows 2m and 2m+1 share st[m]).
-template <int D, bool kStageK>
-struct Stager {
+// Copy one K tile (token-major rows of D) and one V tile (channel-major rows
+// of 128 keys) into LDS with LDS-DMA loads: waves 0-3 take the K chunks,
+// waves 4-7 the V chunks. A chunk is 1 KiB of LDS (lane l fills 16 bytes at
+// l*16); the lane loads the global 16-byte piece that belongs at its swizzled
+// position, so row r holds its piece c at position c ^ (r & (positions-1)).
+template <int D>
+__device__ __forceinline__ void dma_tile(uint16_t* ks, uint16_t* vs, const uint16_t* __restrict__ kt,
+                                         const uint16_t* __restrict__ vt, int wave, int lane) {
   using S = AttnShape<D>;
-  u32x4 st[8];
-  int t;  // thread index within the staging half (0..255)
-
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt) {
-    if constexpr (kStageK) {
+  if (wave < kWaves / 2) {
 #pragma unroll
-      for (int p = 0; p < S::kKPasses; ++p) st[p] = *reinterpret_cast<const u32x4*>(kt + (p * kHalfThreads + t) * 8);
-    } else if (t < S::kVBlocks) {
-      const int dq = t % S::kVQuads, kg = t / S::kVQuads;
-      const uint16_t* src = vt + (16 * kg) * D + 4 * dq;
+    for (int i = 0; i < S::kChunksPerWave; ++i) {
+      const int c = wave * S::kChunksPerWave + i;
+      const int r = c * S::kKRowsPerChunk + lane / S::kKPos, p = lane % S::kKPos;
+      const uint16_t* src = kt + r * D + ((p ^ (r & (S::kKPos - 1))) * 8);
+      __builtin_amdgcn_global_load_lds(src, ks + c * 512, 16, 0, 0);
+    }
+  } else {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const u32x2 a = *reinterpret_cast<const u32x2*>(src + (2 * m) * D);
-        const u32x2 c = *reinterpret_cast<const u32x2*>(src + (2 * m + 1) * D);
-        st[m] = u32x4{a[0], a[1], c[0], c[1]};
-      }
+    for (int i = 0; i < S::kChunksPerWave; ++i) {
+      const int c = (wave - kWaves / 2) * S::kChunksPerWave + i;
+      const int d = c * 4 + lane / 16, p = lane % 16;
+      const uint16_t* src = vt + d * kTok + ((p ^ (d & 15)) * 8);
+      __builtin_amdgcn_global_load_lds(src, vs + c * 512, 16, 0, 0);
     }
   }
-
-  __device__ __forceinline__ void store(uint16_t* ks, uint16_t* vs) const {
-    if constexpr (kStageK) {
-#pragma unroll
-      for (int p = 0; p < S::kKPasses; ++p) {
-        const int e = (p * kHalfThreads + t) * 8;  // element offset inside the dense tile
-        *reinterpret_cast<u32x4*>(ks + (e / D) * S::KS + e % D) = st[p];
-      }
-    } else if (t < S::kVBlocks) {
-      const int dq = t % S::kVQuads, kg = t / S::kVQuads;
-      // Channel 4dq + i of key row r (0..15) is 16-bit half i%2 of dword
-      // 2(r%2) + i/2 of st[r/2].
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 4 * dq + i;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          u32x4 o;
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const int ra = (p < 2 ? 4 * hh : 8 + 4 * hh) + 2 * (p % 2), rb = ra + 1;
-            const uint32_t a = st[ra / 2][2 * (ra % 2) + i / 2], c = st[rb / 2][2 * (rb % 2) + i / 2];
-            o[p] = (i & 1) ? ((a >> 16) | (c & 0xFFFF0000u)) : ((a & 0xFFFFu) | (c << 16));
-          }
-          *reinterpret_cast<u32x4*>(vs + d * kTok + (((2 * kg + hh) ^ vt_swizzle(d)) * 8)) = o;
-        }
-      }
-    }
-  }
-};
+}
 
 // Per-wave state of the online softmax for 32 queries x one key half.
 template <int D>
 struct WaveState {
   using S = AttnShape<D>;
-  u32x4 qf[S::kDC];      // Q^T operand: d = 16dc + 8h .. +7 of query l32
+  u32x4 qf[S::kDC];       // Q^T operand: d = 16dc + 8h .. +7 of query l32
   floatx16 oacc[S::kDB];  // O^T partial: d = 32db + 8(v/4) + 4h + v%4, query l32
   float m_run, l_run;     // running max (base 2, scaled) and partial sum
 };
 
 // One selected key tile j for one wave: S^T, mask, online softmax, PV.
-// after_s() runs once the S^T MFMAs are issued and after_pv() once the PV
-// MFMAs are issued, so staging work placed there overlaps the matrix cores.
-template <int D, class AfterS, class AfterPV>
+template <int D>
 __device__ __forceinline__ void attend_tile(WaveState<D>& w, const uint16_t* ks, const uint16_t* vs,
                                             const GeoTable& g, const HeadGeo& hg, int32_t j, int half, int h,
-                                            int l32, float scale_log2, AfterS&& after_s, AfterPV&& after_pv) {
+                                            int l32, float scale_log2) {
   using S = AttnShape<D>;
-  // S^T[kb]: keys 64half + 32kb + (8(v/4) + 4h + v%4), query l32.
+  // S^T[kb]: row i = 8(v/4) + 4h + v%4 of block kb is key
+  // 64half + 32kb + pi(i) = 64half + 32kb + 16(v/8) + 8h + 4((v/4)%2) + v%4.
   floatx16 sacc[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.0f;
-    const uint16_t* krow = ks + (64 * half + 32 * kb + l32) * S::KS + 8 * h;
+    const int r = 64 * half + 32 * kb + key_perm(l32);
+    const uint16_t* krow = ks + r * D;
 #pragma unroll
     for (int dc = 0; dc < S::kDC; ++dc) {
-      const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 16 * dc);
+      const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + (((2 * dc + h) ^ (r & (S::kKPos - 1))) * 8));
       sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(w.qf[dc]), sacc[kb], 0, 0, 0);
     }
   }
-  after_s();
 
   // Pad keys of a border tile get -inf: the box's real-slot mask is built
-  // once per tile with uniform ops; each lane pulls its bits (its keys are
-  // bits 32kb + 8(v/4) + v%4 of the mask shifted by 64half + 4h).
+  // once per tile with uniform ops; each lane pulls its bits.
   const BoxExtent e = box_extent(g, hg, j);
   if (!box_is_full(hg, e)) {
-    const uint64_t wm = box_slot_mask64(hg, e, 64 * half) >> (4 * h);
+    const uint64_t wm = box_slot_mask64(hg, e, 64 * half) >> (8 * h);
     const uint32_t wlo = uint32_t(wm), whi = uint32_t(wm >> 32);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const uint32_t real = ((kb ? whi : wlo) >> (8 * (v / 4) + (v % 4))) & 1u;
+        const int bit = 16 * (v / 8) + 4 * ((v / 4) % 2) + (v % 4);
+        const uint32_t real = ((kb ? whi : wlo) >> bit) & 1u;
         sacc[kb][v] += __uint_as_float((real - 1u) & 0xFF800000u);
       }
   }
@@ -223,12 +191,12 @@ __device__ __forceinline__ void attend_tile(WaveState<D>& w, const uint16_t* ks,
   w.l_run += psum;
 
   // O^T[db] += V^T P^T over this half's 64 keys, 16 at a time: k-slot v' of
-  // half-wave h is key 64half + 32kb + 16c2 + 8(v'/4) + 4h + v'%4, i.e.
-  // chunk 2G + h of group G = 4half + 2kb + c2 in the V^T rows.
+  // half-wave h is key 64half + 32kb + 16c2 + 8h + v', i.e. 16-byte chunk
+  // 8half + 4kb + 2c2 + h of the V^T row.
 #pragma unroll
   for (int db = 0; db < S::kDB; ++db) {
     const int d = 32 * db + l32;
-    const int t0 = (8 * half + h) ^ vt_swizzle(d);
+    const int t0 = (8 * half + h) ^ (d & 15);
     const uint16_t* vrow = vs + d * kTok;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -239,51 +207,6 @@ __device__ __forceinline__ void attend_tile(WaveState<D>& w, const uint16_t* ks,
       }
     }
   }
-  after_pv();
-}
-
-// The tile loop of one wave; kStageK selects which half of each tile this
-// wave stages. Staging is pipelined two tiles deep: during iteration i the
-// staging registers hold tile i+1, loaded at the end of iteration i-1; once
-// the PV MFMAs of tile i are issued they go to the free LDS buffer and the
-// loads of tile i+2 start, so every load has a whole iteration to land and
-// the LDS stores run under the PV MFMAs. Every thread runs the same number of iterations and barriers.
-template <int D, bool kStageK>
-__device__ __forceinline__ void attend_all(WaveState<D>& w, uint16_t (&ks_s)[2][kTok * AttnShape<D>::KS],
-                                           uint16_t (&vs_s)[2][D * kTok], const GeoTable& g, const HeadGeo& hg,
-                                           const int32_t* sel, const uint16_t* kbase, const uint16_t* vbase,
-                                           int half, int h, int l32, float scale_log2) {
-  const int64_t tile_elems = int64_t(kTok) * D;
-  const unsigned nT = unsigned(hg.nT);
-  const int kh = hg.k;
-  Stager<D, kStageK> stg;
-  stg.t = threadIdx.x % kHalfThreads;
-  // Entries outside [0, nT_hd) contribute no keys; tile 0 stands in as a
-  // harmless load source so every load is unconditional.
-  auto src = [&](int32_t jt) { return unsigned(jt) < nT ? jt : 0; };
-  int32_t j = sel[0];
-  stg.load(kbase + int64_t(src(j)) * tile_elems, vbase + int64_t(src(j)) * tile_elems);
-  stg.store(ks_s[0], vs_s[0]);
-  int32_t jn = kh > 1 ? sel[1] : 0;
-  stg.load(kbase + int64_t(src(jn)) * tile_elems, vbase + int64_t(src(jn)) * tile_elems);
-  __syncthreads();
-  for (int i = 0; i < kh; ++i) {
-    const int cur = i & 1;
-    const bool has_next = i + 1 < kh;
-    const int32_t jnn = i + 2 < kh ? sel[i + 2] : 0;
-    auto nothing = [] {};
-    auto restage = [&] {  // tile i+1 -> free LDS buffer, then start loading tile i+2
-      if (has_next) stg.store(ks_s[cur ^ 1], vs_s[cur ^ 1]);
-      stg.load(kbase + int64_t(src(jnn)) * tile_elems, vbase + int64_t(src(jnn)) * tile_elems);
-    };
-    if (unsigned(j) < nT)
-      attend_tile<D>(w, ks_s[cur], vs_s[cur], g, hg, j, half, h, l32, scale_log2, nothing, restage);
-    else
-      restage();
-    j = jn;
-    jn = jnn;
-    __syncthreads();
-  }
 }
 
 template <int D>
@@ -292,14 +215,14 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
     const uint16_t* __restrict__ v_t, const int32_t* __restrict__ idx, int32_t k_max, float scale_log2,
     uint16_t* __restrict__ o_t, float* __restrict__ lse) {
   using S = AttnShape<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t ks_s[2][kTok * S::KS];
-  __shared__ __attribute__((aligned(16))) uint16_t vs_s[2][D * kTok];
+  // [buffer][K | V] tiles; after the loop the space holds the half merge.
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][S::kTileElems];
 
   const int hd = blockIdx.y, b = blockIdx.z;
   const HeadGeo hg = g.h[hd];
   const int32_t tq = xcd_tile_order(blockIdx.x, g.nT_max);
   const int64_t head_base = (int64_t(b) * g.heads + hd) * g.nT_max;
-  const int64_t tile_elems = int64_t(kTok) * D;
+  const int64_t tile_elems = S::kTileElems;
   uint16_t* o_tile = o_t + (head_base + tq) * tile_elems;
   float* lse_tile = lse ? lse + (head_base + tq) * kTok : nullptr;
 
@@ -319,6 +242,8 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
   const int32_t* sel = idx + (head_base + tq) * k_max;
   const uint16_t* kbase = k_t + head_base * tile_elems;
   const uint16_t* vbase = v_t + head_base * tile_elems;
+  const unsigned nT = unsigned(hg.nT);
+  const int kh = hg.k;
 
   WaveState<D> w;
   {
@@ -332,20 +257,29 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
     for (int v = 0; v < 16; ++v) w.oacc[db][v] = 0.0f;
   w.m_run = -__builtin_inff();
   w.l_run = 0.0f;
-  // Let Q land before the loop, so no wait on it inside the loop can drain
-  // the in-order counter that the staging loads share.
-  __builtin_amdgcn_s_waitcnt(0);
 
-  if (wave < 4)
-    attend_all<D, true>(w, ks_s, vs_s, g, hg, sel, kbase, vbase, half, h, l32, scale_log2);
-  else
-    attend_all<D, false>(w, ks_s, vs_s, g, hg, sel, kbase, vbase, half, h, l32, scale_log2);
+  // Entries outside [0, nT_hd) contribute no keys; tile 0 stands in as a
+  // harmless copy source.
+  auto src = [&](int32_t jt) { return int64_t(unsigned(jt) < nT ? jt : 0) * tile_elems; };
+  int32_t j = sel[0];
+  dma_tile<D>(lds[0][0], lds[0][1], kbase + src(j), vbase + src(j), wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);  // Q and the first tile have landed
+  __syncthreads();
+  for (int i = 0; i < kh; ++i) {
+    const int cur = i & 1;
+    const int32_t jn = i + 1 < kh ? sel[i + 1] : 0;
+    if (i + 1 < kh) dma_tile<D>(lds[cur ^ 1][0], lds[cur ^ 1][1], kbase + src(jn), vbase + src(jn), wave, lane);
+    if (unsigned(j) < nT) attend_tile<D>(w, lds[cur][0], lds[cur][1], g, hg, j, half, h, l32, scale_log2);
+    j = jn;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile i+1 have landed
+    __syncthreads();
+  }
 
-  // Merge the two key halves through LDS (the K/V buffers are free now):
+  // Merge the two key halves through LDS (the tile buffers are free now):
   // m = max(m0, m1), O = O0 2^(m0-m) + O1 2^(m1-m), l likewise.
-  float* red = reinterpret_cast<float*>(&ks_s[0][0]);       // [4][kDB*16][64] partial O^T
+  float* red = reinterpret_cast<float*>(&lds[0][0][0]);     // [4][kDB*16][64] partial O^T
   float* red_ml = red + 4 * S::kDB * 16 * 64;                // [4][2][64] m, l
-  static_assert(sizeof(ks_s) >= (4 * S::kDB * 16 * 64 + 4 * 2 * 64) * sizeof(float), "merge space");
+  static_assert(sizeof(lds) >= (4 * S::kDB * 16 * 64 + 4 * 2 * 64) * sizeof(float), "merge space");
   const float l_half = w.l_run + __shfl_xor(w.l_run, 32, 64);
   if (half == 1) {
 #pragma unroll

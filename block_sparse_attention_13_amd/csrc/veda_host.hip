@@ -135,15 +135,17 @@ int veda_max_tiles(const veda_geom* g) {
 }
 
 int veda_tile_permute(const veda_geom* g, const void* x_raster, veda_raster_strides s, void* x_tiled,
-                      void* stream) {
+                      int32_t layout, void* stream) {
   GeoTable t;
   VEDA_TRY(build_table(g, &t));
   if (!x_raster || !x_tiled) return VEDA_ERR_NULL;
+  if (layout != VEDA_TILED_TOKEN_MAJOR && layout != VEDA_TILED_CHANNEL_MAJOR) return VEDA_ERR_SHAPE;
   if (!aligned16(x_raster) || !aligned16(x_tiled)) return VEDA_ERR_ALIGN;
   VEDA_TRY(check_strides(s));
   VEDA_TRY(check_device());
   return launched(veda::launch_tile_permute(t, static_cast<const uint16_t*>(x_raster), s.b, s.n, s.h,
-                                            static_cast<uint16_t*>(x_tiled), static_cast<hipStream_t>(stream)));
+                                            static_cast<uint16_t*>(x_tiled), layout == VEDA_TILED_CHANNEL_MAJOR,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 int veda_tile_unpermute(const veda_geom* g, const void* x_tiled, void* x_raster, veda_raster_strides s,

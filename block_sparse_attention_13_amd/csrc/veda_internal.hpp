@@ -94,7 +94,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 // Host-side launchers, one per kernel family (each defined next to its kernel).
 hipError_t launch_tile_permute(const GeoTable& g, const uint16_t* x, int64_t sb, int64_t sn, int64_t sh,
-                               uint16_t* xt, hipStream_t s);
+                               uint16_t* xt, bool channel_major, hipStream_t s);
 hipError_t launch_tile_unpermute(const GeoTable& g, const uint16_t* xt, uint16_t* x, int64_t sb, int64_t sn,
                                  int64_t sh, hipStream_t s);
 hipError_t launch_trippool_features(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t,

@@ -31,7 +31,8 @@
  *
  * Layouts (row-major, contiguous unless a stride is given):
  *   raster x        [B, N, heads, d] bf16 with element strides veda_raster_strides (channel stride 1)
- *   tiled x         [B, heads, nT_max, 128, d] bf16
+ *   tiled x         [B, heads, nT_max, 128, d] bf16 (token-major), or
+ *                   [B, heads, nT_max, d, 128] bf16 (channel-major: each tile transposed)
  *   stats           [B, heads, nT_max, 3d] bf16, [avg | max | min]
  *   features        [B, heads, nT_max, r] bf16
  *   W_q, W_k        [heads, 3d, r] bf16 (features = stats @ W)
@@ -66,6 +67,9 @@ extern "C" {
 #define VEDA_TILE_TOKENS 128
 #define VEDA_MAX_HEADS 128
 #define VEDA_MAX_TILES 8192
+
+/* Layout of a tiled tensor: token-major [.., 128, d] or channel-major [.., d, 128]. */
+enum { VEDA_TILED_TOKEN_MAJOR = 0, VEDA_TILED_CHANNEL_MAJOR = 1 };
 
 enum {
   VEDA_OK = 0,
@@ -106,10 +110,13 @@ int veda_max_tiles(const veda_geom* g);
  * Principle 02 "Head-Conditioned Tile Geometry": per-head tile shapes
  * (p_t, p_h, p_w); "Head-Aware Tile Search": p_t*p_h*p_w = B = 128).
  *   x_raster  in   raster bf16 tensor, strides `s` (elements)
- *   x_tiled   out  tiled bf16 [B, heads, nT_max, 128, d]; pad slots and tiles >= nT_hd are 0
+ *   x_tiled   out  tiled bf16 in `layout`: VEDA_TILED_TOKEN_MAJOR [B, heads, nT_max, 128, d] or
+ *                  VEDA_TILED_CHANNEL_MAJOR [B, heads, nT_max, d, 128] (the layout the attention
+ *                  call takes V in); pad slots and tiles >= nT_hd are 0
+ *   layout    in   VEDA_TILED_TOKEN_MAJOR or VEDA_TILED_CHANNEL_MAJOR (else VEDA_ERR_SHAPE)
  */
 int veda_tile_permute(const veda_geom* g, const void* x_raster, veda_raster_strides s,
-                      void* x_tiled, void* stream);
+                      void* x_tiled, int32_t layout, void* stream);
 
 /*
  * TripPool estimator (Veda page, "Attention Structure Distillation",
@@ -156,7 +163,8 @@ int veda_topk_mask(const veda_geom* g, const float* scores, const int32_t* k_per
  * Query token i of tile tq attends to the real (non-pad) keys of the tiles
  * idx[b, hd, tq, 0..k_hd-1]; logits are scale * q.k; bf16 MFMA products with
  * fp32 accumulation and an fp32 online softmax.
- *   q_tiled, k_tiled, v_tiled  in   tiled bf16
+ *   q_tiled, k_tiled           in   tiled bf16, token-major [B, heads, nT_max, 128, d]
+ *   v_tiled                    in   tiled bf16, channel-major [B, heads, nT_max, d, 128]
  *   idx                        in   int32 [B, heads, nT_max, k_max] from veda_topk_mask
  *                                   (entries 0..k_hd-1 must lie in [0, nT_hd))
  *   k_per_head                 in   host int32 [heads]

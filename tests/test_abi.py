@@ -35,6 +35,9 @@ def test_header_constants_match_binding():
     assert int(consts["VEDA_TILE_TOKENS"]) == _lib.VEDA_TILE_TOKENS
     assert int(consts["VEDA_MAX_HEADS"]) == _lib.VEDA_MAX_HEADS
     assert int(consts["VEDA_MAX_TILES"]) == _lib.VEDA_MAX_TILES
+    layouts = dict((n, int(v)) for n, v in re.findall(r"(VEDA_TILED_[A-Z_]+) = (\d+)", text))
+    assert layouts == {"VEDA_TILED_TOKEN_MAJOR": _lib.VEDA_TILED_TOKEN_MAJOR,
+                       "VEDA_TILED_CHANNEL_MAJOR": _lib.VEDA_TILED_CHANNEL_MAJOR}
     codes = dict((n, int(v)) for n, v in re.findall(r"(VEDA_(?:OK|ERR_[A-Z]+)) = (-?\d+)", text))
     assert {v: k for k, v in codes.items()} == _lib.STATUS
     for code in _lib.STATUS:
@@ -77,10 +80,13 @@ def test_call_errors_precede_any_device_work():
     L = _lib.lib
     g = _geom()
     s = _lib.VedaRasterStrides(8 * 16 * 128, 128, 128)
-    assert L.veda_tile_permute(g.c, None, s, FAKE, None) == -1
-    assert L.veda_tile_permute(g.c, FAKE + 2, s, FAKE, None) == -5
-    assert L.veda_tile_permute(g.c, FAKE, _lib.VedaRasterStrides(1024, 129, 128), FAKE, None) == -5
-    assert L.veda_tile_permute(_geom(tiles=((2, 2, 2),)).c, FAKE, s, FAKE, None) == -3
+    TM, CM = _lib.VEDA_TILED_TOKEN_MAJOR, _lib.VEDA_TILED_CHANNEL_MAJOR
+    assert L.veda_tile_permute(g.c, None, s, FAKE, TM, None) == -1
+    assert L.veda_tile_permute(g.c, FAKE + 2, s, FAKE, CM, None) == -5
+    assert L.veda_tile_permute(g.c, FAKE, _lib.VedaRasterStrides(1024, 129, 128), FAKE, TM, None) == -5
+    assert L.veda_tile_permute(_geom(tiles=((2, 2, 2),)).c, FAKE, s, FAKE, TM, None) == -3
+    assert L.veda_tile_permute(g.c, FAKE, s, FAKE, 2, None) == -2
+    assert L.veda_tile_permute(g.c, FAKE, s, FAKE, -1, None) == -2
     assert L.veda_tile_unpermute(g.c, FAKE, None, s, None) == -1
     ks = _lib.int_array([3])
     assert L.veda_trippool_score(g.c, FAKE, FAKE, FAKE, FAKE, 48, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2
@@ -106,7 +112,7 @@ def test_valid_call_without_gpu_reports_device_error():
     from block_sparse_attention_13_amd import _lib
     g = _geom()
     s = _lib.VedaRasterStrides(8 * 16 * 128, 128, 128)
-    assert _lib.lib.veda_tile_permute(g.c, FAKE, s, FAKE, None) == -6
+    assert _lib.lib.veda_tile_permute(g.c, FAKE, s, FAKE, _lib.VEDA_TILED_CHANNEL_MAJOR, None) == -6
 
 
 def test_python_wrappers_validate_before_calling():

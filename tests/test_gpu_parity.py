@@ -53,6 +53,8 @@ def check_head(w, data, out, hd, ks, tiles, b=0, check_attention=True):
     r = oracle_head(data, w, b, hd, ks[hd], query_tiles=tiles if check_attention else [])
     for name in ("q_t", "k_t", "v_t"):
         got = bits_of(out[name][b, hd])
+        if name == "v_t":  # channel-major tiles [nT_max, d, 128]
+            got = np.ascontiguousarray(got.swapaxes(1, 2))
         assert np.array_equal(got[:nT].reshape(-1, d), O.float_to_bf16_bits(r[name[0] + "t"])), (name, hd)
         assert not got[nT:].any(), (name, hd, "tiles beyond the head must be zero")
     for name in ("stats_q", "stats_k", "feat_q", "feat_k"):
@@ -83,7 +85,7 @@ def check_head(w, data, out, hd, ks, tiles, b=0, check_attention=True):
     # value rows of the selected tiles
     valid = np.zeros(nT * 128, bool)
     valid[pos] = True
-    v_t = O.bf16_bits_to_float(bits_of(out["v_t"][b, hd])).reshape(nT_max, 128, d).astype(np.float64)
+    v_t = O.bf16_bits_to_float(bits_of(out["v_t"][b, hd])).reshape(nT_max, d, 128).swapaxes(1, 2).astype(np.float64)
     o_t = f32_of_bf16(out["o_t"][b, hd]).reshape(nT_max, 128, d)
     for t in tiles:
         pads = np.flatnonzero(~valid[t * 128:(t + 1) * 128])
@@ -150,6 +152,11 @@ def test_unpermute_inverts_permute_with_strided_raster():
     assert torch.equal(back.view(torch.int16), x.contiguous().view(torch.int16))
     want, _ = O.tile_permute(packed[1, :, 1, 3, :], w.grid, w.head_tiles()[3])
     assert np.array_equal(bits_of(xt[1, 3]).reshape(-1, w.d), want)
+    # channel-major tiles are the token-major ones transposed, tile by tile
+    xc = V.tile_permute(x, g, layout=V.CHANNEL_MAJOR)
+    torch.cuda.synchronize()
+    assert xc.shape == (w.B, w.heads, g.max_tiles(), w.d, 128)
+    assert torch.equal(xc.view(torch.int16), xt.transpose(3, 4).contiguous().view(torch.int16))
 
 
 def _random_workload(grid, tiles, d, r, heads, seed, keep=None, k=None):
@@ -246,7 +253,7 @@ def test_every_output_byte_is_written():
     g = lambda shape, dt: torch.full(shape, 0x7FC0 if dt == torch.bfloat16 else -1, dtype=torch.int16 if dt == torch.bfloat16 else torch.int32, device="cuda").view(dt)
     bufs = {
         "q_t": g((B, Hh, nT, 128, d), torch.bfloat16), "k_t": g((B, Hh, nT, 128, d), torch.bfloat16),
-        "v_t": g((B, Hh, nT, 128, d), torch.bfloat16), "o_t": g((B, Hh, nT, 128, d), torch.bfloat16),
+        "v_t": g((B, Hh, nT, d, 128), torch.bfloat16), "o_t": g((B, Hh, nT, 128, d), torch.bfloat16),
         "stats_q": g((B, Hh, nT, 3 * d), torch.bfloat16), "stats_k": g((B, Hh, nT, 3 * d), torch.bfloat16),
         "feat_q": g((B, Hh, nT, w.r), torch.bfloat16), "feat_k": g((B, Hh, nT, w.r), torch.bfloat16),
         "scores": g((B, Hh, nT, nT), torch.float32), "idx": g((B, Hh, nT, max(w.k_per_head())), torch.int32),
