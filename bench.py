@@ -19,6 +19,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -57,6 +58,38 @@ def stage_bytes(w) -> dict:
         "topk": scores + idx,
         "unpermute": tiled + raster,
     }
+
+
+ATTN_COUNTERS = os.path.join(ROOT, "profiles", "sparse_attn_long245k_hbm_counters.md")
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_13_amd", "csrc", "sparse_attn.hip")
+
+
+def attention_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads
+    for a plain copy of known size), or None when that summary is missing,
+    covers another workload, or was taken from a different kernel source."""
+    import hashlib
+    if workload != "long" or not os.path.exists(ATTN_COUNTERS):
+        return None
+    with open(ATTN_COUNTERS) as f:
+        text = f.read()
+    m_b = re.search(r"^traffic_bytes_per_launch = (\d+)$", text, re.M)
+    m_h = re.search(r"^kernel_source_sha256_16 = ([0-9a-f]{16})$", text, re.M)
+    if not (m_b and m_h):
+        return None
+    with open(ATTN_SOURCE, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != m_h.group(1):
+            return None
+    return int(m_b.group(1))
+
+
+def attention_bytes(w) -> int:
+    """Algorithmic HBM bytes of one attention launch: Q, K, V read once, O and
+    LSE written once, the index lists read once."""
+    nT = max(w.tiles_per_head())
+    tiled = w.B * w.heads * nT * 128 * w.d * 2
+    return 4 * tiled + w.B * w.heads * nT * 128 * 4 + w.B * w.heads * nT * max(w.k_per_head()) * 4
 
 
 def cpu_baseline(w, data, sample_tiles: int, seconds_hint: float = 20.0):
@@ -107,7 +140,7 @@ def main():
     ap.add_argument("--workload", default="long")
     ap.add_argument("--heads", type=int, default=0, help="run only the first N heads (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tiles", type=int, default=24)
+    ap.add_argument("--cpu-sample-tiles", type=int, default=1920)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (HBM counter calibration)")
     args = ap.parse_args()
@@ -230,7 +263,8 @@ def main():
         "stage_ms": stage_ms,
         "stage_hbm_gbs": hbm,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": attention_traffic(args.workload),
+                     "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": attention_bytes(w),
                      "kernel": "sparse_attn_fwd_kernel<128>", "flops_per_launch": f_attn},
         "cpu_baseline": cpu,
     }
