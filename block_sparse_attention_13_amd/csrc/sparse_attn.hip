@@ -81,31 +81,49 @@ __device__ __forceinline__ int32_t xcd_tile_order(int32_t x, int32_t n) {
   return xcd < r ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
 }
 
-// Copy one K tile (token-major rows of D) and one V tile (channel-major rows
-// of 128 keys) into LDS with LDS-DMA loads: waves 0-3 take the K chunks,
-// waves 4-7 the V chunks. A chunk is 1 KiB of LDS (lane l fills 16 bytes at
-// l*16); the lane loads the global 16-byte piece that belongs at its swizzled
-// position, so row r holds its piece c at position c ^ (r & (positions-1)).
+// LDS-DMA copy plan of one wave. A tile is 32 (D = 128) or 16 (D = 64)
+// chunks of 1 KiB; waves 0-3 copy K chunks, waves 4-7 V chunks. In LDS, lane
+// l of a chunk fills bytes 16l..16l+15; the lane loads the global 16-byte
+// piece that belongs at its swizzled position, so row r holds its piece c at
+// position c ^ (r mod positions-per-row, at most 16). The swizzle repeats every
+// 16 rows = 4 chunks, so chunk 4q + s of a tile starts at byte 4096q + off[s]
+// of the global tile.
 template <int D>
-__device__ __forceinline__ void dma_tile(uint16_t* ks, uint16_t* vs, const uint16_t* __restrict__ kt,
-                                         const uint16_t* __restrict__ vt, int wave, int lane) {
+struct DmaPlan {
+  uint32_t off[4];  // per-lane source byte offsets of chunks 0..3 of this wave's role
+  int first;        // first chunk of this wave (a multiple of 4)
+  bool is_k;        // wave copies K (else V)
+};
+
+template <int D>
+__device__ __forceinline__ DmaPlan<D> dma_plan(int wave, int lane) {
   using S = AttnShape<D>;
-  if (wave < kWaves / 2) {
+  DmaPlan<D> pl;
+  pl.is_k = wave < kWaves / 2;
+  pl.first = (pl.is_k ? wave : wave - kWaves / 2) * S::kChunksPerWave;
 #pragma unroll
-    for (int i = 0; i < S::kChunksPerWave; ++i) {
-      const int c = wave * S::kChunksPerWave + i;
+  for (int c = 0; c < 4; ++c) {
+    if (pl.is_k) {  // token-major K: kKRowsPerChunk rows of D per chunk
       const int r = c * S::kKRowsPerChunk + lane / S::kKPos, p = lane % S::kKPos;
-      const uint16_t* src = kt + r * D + ((p ^ (r & (S::kKPos - 1))) * 8);
-      __builtin_amdgcn_global_load_lds(src, ks + c * 512, 16, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < S::kChunksPerWave; ++i) {
-      const int c = (wave - kWaves / 2) * S::kChunksPerWave + i;
+      pl.off[c] = uint32_t(r * D + ((p ^ (r & (S::kKPos - 1))) * 8)) * 2u;
+    } else {        // channel-major V: 4 rows of 128 keys per chunk
       const int d = c * 4 + lane / 16, p = lane % 16;
-      const uint16_t* src = vt + d * kTok + ((p ^ (d & 15)) * 8);
-      __builtin_amdgcn_global_load_lds(src, vs + c * 512, 16, 0, 0);
+      pl.off[c] = uint32_t(d * kTok + ((p ^ (d & 15)) * 8)) * 2u;
     }
+  }
+  return pl;
+}
+
+// Issue this wave's share of one tile copy: src is the global tile (K or V
+// by role), dst its LDS buffer.
+template <int D>
+__device__ __forceinline__ void dma_issue(const DmaPlan<D>& pl, const uint16_t* src, uint16_t* dst) {
+  using S = AttnShape<D>;
+  const char* base = reinterpret_cast<const char*>(src);
+#pragma unroll
+  for (int i = 0; i < S::kChunksPerWave; ++i) {
+    const int c = pl.first + i;
+    __builtin_amdgcn_global_load_lds(base + 4096 * (c / 4) + pl.off[i % 4], dst + c * 512, 16, 0, 0);
   }
 }
 
@@ -118,15 +136,12 @@ struct WaveState {
   float m_run, l_run;     // running max (base 2, scaled) and partial sum
 };
 
-// One selected key tile j for one wave: S^T, mask, online softmax, PV.
+// S^T for this wave's 64 keys of one tile: block kb, row i = 8(v/4) + 4h + v%4
+// is key 64half + 32kb + pi(i) = 64half + 32kb + 16(v/8) + 8h + 4((v/4)%2) + v%4.
 template <int D>
-__device__ __forceinline__ void attend_tile(WaveState<D>& w, const uint16_t* ks, const uint16_t* vs,
-                                            const GeoTable& g, const HeadGeo& hg, int32_t j, int half, int h,
-                                            int l32, float scale_log2) {
+__device__ __forceinline__ void s_tile(floatx16 (&sacc)[2], const WaveState<D>& w, const uint16_t* ks, int half,
+                                       int h, int l32) {
   using S = AttnShape<D>;
-  // S^T[kb]: row i = 8(v/4) + 4h + v%4 of block kb is key
-  // 64half + 32kb + pi(i) = 64half + 32kb + 16(v/8) + 8h + 4((v/4)%2) + v%4.
-  floatx16 sacc[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -139,12 +154,24 @@ __device__ __forceinline__ void attend_tile(WaveState<D>& w, const uint16_t* ks,
       sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(w.qf[dc]), sacc[kb], 0, 0, 0);
     }
   }
+}
 
-  // Pad keys of a border tile get -inf: the box's real-slot mask is built
-  // once per tile with uniform ops; each lane pulls its bits.
+// Real-key bits of this wave's 64 keys of tile j, shifted so bit
+// 16(v/8) + 4((v/4)%2) + v%4 (+32 for kb = 1) is S^T element v of block kb;
+// 0 for an index outside the head (the tile then contributes nothing).
+__device__ __forceinline__ uint64_t real_key_bits(const GeoTable& g, const HeadGeo& hg, int32_t j, int half, int h) {
+  if (unsigned(j) >= unsigned(hg.nT)) return 0ull;
   const BoxExtent e = box_extent(g, hg, j);
-  if (!box_is_full(hg, e)) {
-    const uint64_t wm = box_slot_mask64(hg, e, 64 * half) >> (8 * h);
+  if (box_is_full(hg, e)) return ~0ull;
+  return box_slot_mask64(hg, e, 64 * half) >> (8 * h);
+}
+
+// Mask and the running-max update of the online softmax (base 2, max moved
+// lazily: only when a row's max grows by more than 2^kRescaleSlack).
+template <int D>
+__device__ __forceinline__ void softmax_max(WaveState<D>& w, floatx16 (&sacc)[2], uint64_t wm, float scale_log2) {
+  using S = AttnShape<D>;
+  if (wm != ~0ull) {  // pad keys get -inf through a branch-free bias
     const uint32_t wlo = uint32_t(wm), whi = uint32_t(wm >> 32);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -155,8 +182,6 @@ __device__ __forceinline__ void attend_tile(WaveState<D>& w, const uint16_t* ks,
         sacc[kb][v] += __uint_as_float((real - 1u) & 0xFF800000u);
       }
   }
-
-  // Online softmax in base 2 with a lazily moved running max.
   float mx = sacc[0][0];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -173,11 +198,17 @@ __device__ __forceinline__ void attend_tile(WaveState<D>& w, const uint16_t* ks,
 #pragma unroll
       for (int v = 0; v < 16; ++v) w.oacc[db][v] *= alpha;
   }
+}
+
+// Exponentials, row sums and P^T packed to bf16 in MFMA B-operand order
+// (8 consecutive keys per u32x4).
+template <int D>
+__device__ __forceinline__ void softmax_exp(WaveState<D>& w, const floatx16 (&sacc)[2], u32x4 (&pf)[2][2],
+                                            float scale_log2) {
   // A half that has seen only pad keys so far keeps m = -inf; its exponents
   // must then still be exp2(-inf) = 0, not NaN.
   const float m_use = w.m_run == -__builtin_inff() ? 0.0f : w.m_run;
   float psum = 0.0f;
-  u32x4 pf[2][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -189,10 +220,15 @@ __device__ __forceinline__ void attend_tile(WaveState<D>& w, const uint16_t* ks,
     }
   }
   w.l_run += psum;
+}
 
-  // O^T[db] += V^T P^T over this half's 64 keys, 16 at a time: k-slot v' of
-  // half-wave h is key 64half + 32kb + 16c2 + 8h + v', i.e. 16-byte chunk
-  // 8half + 4kb + 2c2 + h of the V^T row.
+// O^T[db] += V^T P^T over this half's 64 keys, 16 at a time: k-slot v' of
+// half-wave h is key 64half + 32kb + 16c2 + 8h + v', i.e. 16-byte chunk
+// 8half + 4kb + 2c2 + h of the V^T row.
+template <int D>
+__device__ __forceinline__ void pv_tile(WaveState<D>& w, const u32x4 (&pf)[2][2], const uint16_t* vs, int half,
+                                        int h, int l32) {
+  using S = AttnShape<D>;
 #pragma unroll
   for (int db = 0; db < S::kDB; ++db) {
     const int d = 32 * db + l32;
@@ -215,8 +251,9 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
     const uint16_t* __restrict__ v_t, const int32_t* __restrict__ idx, int32_t k_max, float scale_log2,
     uint16_t* __restrict__ o_t, float* __restrict__ lse) {
   using S = AttnShape<D>;
-  // [buffer][K | V] tiles; after the loop the space holds the half merge.
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][S::kTileElems];
+  // K buffers lds[0..1], V buffers lds[2..3]; after the loop the space holds
+  // the half merge.
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4][S::kTileElems];
 
   const int hd = blockIdx.y, b = blockIdx.z;
   const HeadGeo hg = g.h[hd];
@@ -240,10 +277,13 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
   const int qg = wave & 3, half = wave >> 2;
   const int l32 = lane % 32, h = lane / 32;
   const int32_t* sel = idx + (head_base + tq) * k_max;
-  const uint16_t* kbase = k_t + head_base * tile_elems;
-  const uint16_t* vbase = v_t + head_base * tile_elems;
   const unsigned nT = unsigned(hg.nT);
   const int kh = hg.k;
+  const DmaPlan<D> plan = dma_plan<D>(wave, lane);
+  // This wave's copy source: K or V of this head. Entries outside
+  // [0, nT_hd) contribute no keys; tile 0 stands in as a harmless source.
+  const uint16_t* role_base = (plan.is_k ? k_t : v_t) + head_base * tile_elems;
+  auto tile_src = [&](int32_t jt) { return role_base + int64_t(unsigned(jt) < nT ? jt : 0) * tile_elems; };
 
   WaveState<D> w;
   {
@@ -258,26 +298,71 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
   w.m_run = -__builtin_inff();
   w.l_run = 0.0f;
 
-  // Entries outside [0, nT_hd) contribute no keys; tile 0 stands in as a
-  // harmless copy source.
-  auto src = [&](int32_t jt) { return int64_t(unsigned(jt) < nT ? jt : 0) * tile_elems; };
+  // Software pipeline over the selected tiles. Iteration i computes S of
+  // tile i+1 (its K landed during iteration i-1) while it runs the softmax
+  // and PV of tile i; meanwhile K of tile i+2 and V of tile i+1 are copied.
+  //   K of tile t in lds[t & 1]; V of tile t in lds[2 + (t & 1)].
+  // A buffer is overwritten only after the barrier that ends the iteration
+  // in which it was last read.
   int32_t j = sel[0];
-  dma_tile<D>(lds[0][0], lds[0][1], kbase + src(j), vbase + src(j), wave, lane);
-  __builtin_amdgcn_s_waitcnt(0);  // Q and the first tile have landed
+  const int32_t j1 = kh > 1 ? sel[1] : 0;
+  if (plan.is_k) {
+    dma_issue<D>(plan, tile_src(j), lds[0]);
+    dma_issue<D>(plan, tile_src(j1), lds[1]);
+  } else {
+    dma_issue<D>(plan, tile_src(j), lds[2]);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // Q and the first copies have landed
   __syncthreads();
-  for (int i = 0; i < kh; ++i) {
+  floatx16 sc[2];
+  s_tile<D>(sc, w, lds[0], half, h, l32);
+  __syncthreads();  // every wave has read lds[0] before tile 2 lands there
+
+  // One pipelined iteration: s_cur holds S of tile i, s_next receives S of
+  // tile i+1 (computed unconditionally; after the last tile it is unused).
+  auto iteration = [&](int i, floatx16 (&s_cur)[2], floatx16 (&s_next)[2]) {
     const int cur = i & 1;
     const int32_t jn = i + 1 < kh ? sel[i + 1] : 0;
-    if (i + 1 < kh) dma_tile<D>(lds[cur ^ 1][0], lds[cur ^ 1][1], kbase + src(jn), vbase + src(jn), wave, lane);
-    if (unsigned(j) < nT) attend_tile<D>(w, lds[cur][0], lds[cur][1], g, hg, j, half, h, l32, scale_log2);
+    if (plan.is_k) {
+      if (i + 2 < kh) dma_issue<D>(plan, tile_src(sel[i + 2]), lds[cur]);
+    } else {
+      if (i + 1 < kh) dma_issue<D>(plan, tile_src(jn), lds[2 + (cur ^ 1)]);
+    }
+    softmax_max<D>(w, s_cur, real_key_bits(g, hg, j, half, h), scale_log2);
+    u32x4 pf[2][2];
+    s_tile<D>(s_next, w, lds[cur ^ 1], half, h, l32);
+    softmax_exp<D>(w, s_cur, pf, scale_log2);
+    pv_tile<D>(w, pf, lds[2 + cur], half, h, l32);
+    // Interleave: K operand reads run ahead; each S MFMA of the next tile is
+    // followed by a slice of this tile's softmax arithmetic, so the VALU work
+    // runs while the matrix core is busy; the PV MFMAs follow.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
     j = jn;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile i+1 have landed
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies for the next iteration have landed
     __syncthreads();
+  };
+  floatx16 sn[2];
+  int i = 0;
+  for (; i + 1 < kh; i += 2) {
+    iteration(i, sc, sn);
+    iteration(i + 1, sn, sc);
   }
+  if (i < kh) iteration(i, sc, sn);
 
   // Merge the two key halves through LDS (the tile buffers are free now):
   // m = max(m0, m1), O = O0 2^(m0-m) + O1 2^(m1-m), l likewise.
-  float* red = reinterpret_cast<float*>(&lds[0][0][0]);     // [4][kDB*16][64] partial O^T
+  float* red = reinterpret_cast<float*>(&lds[0][0]);        // [4][kDB*16][64] partial O^T
   float* red_ml = red + 4 * S::kDB * 16 * 64;                // [4][2][64] m, l
   static_assert(sizeof(lds) >= (4 * S::kDB * 16 * 64 + 4 * 2 * 64) * sizeof(float), "merge space");
   const float l_half = w.l_run + __shfl_xor(w.l_run, 32, 64);
