@@ -81,50 +81,61 @@ __device__ __forceinline__ int32_t xcd_tile_order(int32_t x, int32_t n) {
   return xcd < r ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
 }
 
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
 // LDS-DMA copy plan of one wave. A tile is 32 (D = 128) or 16 (D = 64)
-// chunks of 1 KiB; waves 0-3 copy K chunks, waves 4-7 V chunks. In LDS, lane
-// l of a chunk fills bytes 16l..16l+15; the lane loads the global 16-byte
-// piece that belongs at its swizzled position, so row r holds its piece c at
-// position c ^ (r mod positions-per-row, at most 16). The swizzle repeats every
-// 16 rows = 4 chunks, so chunk 4q + s of a tile starts at byte 4096q + off[s]
-// of the global tile.
+// chunks of 1 KiB; waves 0-3 copy K chunks, waves 4-7 V chunks, through
+// buffer loads that write LDS directly (the tile's byte offset in a scalar
+// register, one 32-bit offset per lane and chunk). In LDS, lane l of a chunk
+// fills bytes 16l..16l+15; the lane loads the global 16-byte piece that
+// belongs at its swizzled position, so row r holds its piece c at position
+// c ^ (r mod positions-per-row, at most 16).
 template <int D>
 struct DmaPlan {
-  uint32_t off[4];  // per-lane source byte offsets of chunks 0..3 of this wave's role
-  int first;        // first chunk of this wave (a multiple of 4)
-  bool is_k;        // wave copies K (else V)
+  const uint16_t* base;                         // this head's K or V tiles
+  int32_t bytes;                                // their extent
+  uint32_t off[AttnShape<D>::kChunksPerWave];   // per-lane source byte offsets within a tile
+  int first;                                    // first chunk of this wave
+  bool is_k;                                    // wave copies K (else V)
 };
 
 template <int D>
-__device__ __forceinline__ DmaPlan<D> dma_plan(int wave, int lane) {
+__device__ __forceinline__ DmaPlan<D> dma_plan(int wave, int lane, const uint16_t* k_head, const uint16_t* v_head,
+                                               int32_t n_tiles) {
   using S = AttnShape<D>;
   DmaPlan<D> pl;
   pl.is_k = wave < kWaves / 2;
   pl.first = (pl.is_k ? wave : wave - kWaves / 2) * S::kChunksPerWave;
+  pl.base = pl.is_k ? k_head : v_head;
+  pl.bytes = n_tiles * S::kTileElems * 2;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int i = 0; i < S::kChunksPerWave; ++i) {
+    const int c = pl.first + i;
     if (pl.is_k) {  // token-major K: kKRowsPerChunk rows of D per chunk
       const int r = c * S::kKRowsPerChunk + lane / S::kKPos, p = lane % S::kKPos;
-      pl.off[c] = uint32_t(r * D + ((p ^ (r & (S::kKPos - 1))) * 8)) * 2u;
+      pl.off[i] = uint32_t(r * D + ((p ^ (r & (S::kKPos - 1))) * 8)) * 2u;
     } else {        // channel-major V: 4 rows of 128 keys per chunk
       const int d = c * 4 + lane / 16, p = lane % 16;
-      pl.off[c] = uint32_t(d * kTok + ((p ^ (d & 15)) * 8)) * 2u;
+      pl.off[i] = uint32_t(d * kTok + ((p ^ (d & 15)) * 8)) * 2u;
     }
   }
   return pl;
 }
 
-// Issue this wave's share of one tile copy: src is the global tile (K or V
-// by role), dst its LDS buffer.
+// One 1-KiB LDS-DMA copy: lane l loads 16 bytes at byte tile_bytes + voff
+// of a raw buffer over [base, base + bytes) (stride 0; reads past the end
+// would return 0) into LDS bytes 16l..16l+15 of dst.
+__device__ __forceinline__ void dma_copy(const uint16_t* base, int32_t bytes, uint32_t voff, uint32_t tile_bytes,
+                                         lds_u16* dst) {
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, tile_bytes, 0, 0);
+}
+
 template <int D>
-__device__ __forceinline__ void dma_issue(const DmaPlan<D>& pl, const uint16_t* src, uint16_t* dst) {
-  using S = AttnShape<D>;
-  const char* base = reinterpret_cast<const char*>(src);
+__device__ __forceinline__ void dma_issue(const DmaPlan<D>& pl, uint32_t tile_bytes, lds_u16* dst) {
 #pragma unroll
-  for (int i = 0; i < S::kChunksPerWave; ++i) {
-    const int c = pl.first + i;
-    __builtin_amdgcn_global_load_lds(base + 4096 * (c / 4) + pl.off[i % 4], dst + c * 512, 16, 0, 0);
-  }
+  for (int i = 0; i < AttnShape<D>::kChunksPerWave; ++i)
+    dma_copy(pl.base, pl.bytes, pl.off[i], tile_bytes, dst + (pl.first + i) * 512);
 }
 
 // Per-wave state of the online softmax for 32 queries x one key half.
@@ -187,7 +198,10 @@ __device__ __forceinline__ void softmax_max(WaveState<D>& w, floatx16 (&sacc)[2]
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+  {  // lanes l and l + 32 hold the two halves of one query's keys
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+  }
   if (__builtin_amdgcn_ballot_w64(mx > w.m_run + kRescaleSlack) != 0) {
     const float m_new = fmaxf(w.m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_new);
@@ -200,48 +214,88 @@ __device__ __forceinline__ void softmax_max(WaveState<D>& w, floatx16 (&sacc)[2]
   }
 }
 
-// Exponentials, row sums and P^T packed to bf16 in MFMA B-operand order
-// (8 consecutive keys per u32x4).
+// K fragment of S^T step t (block kb = t / kDC, k-step dc = t % kDC) for
+// this lane: 16 bytes of key row 64half + 32kb + pi(l32), channels
+// 16dc + 8h .. +7, at its swizzled position.
 template <int D>
-__device__ __forceinline__ void softmax_exp(WaveState<D>& w, const floatx16 (&sacc)[2], u32x4 (&pf)[2][2],
-                                            float scale_log2) {
+__device__ __forceinline__ u32x4 k_frag(const uint16_t* ks, int t, int half, int h, int l32) {
+  using S = AttnShape<D>;
+  const int kb = t / S::kDC, dc = t % S::kDC;
+  const int r = 64 * half + 32 * kb + key_perm(l32);
+  return *reinterpret_cast<const u32x4*>(ks + r * D + (((2 * dc + h) ^ (r & (S::kKPos - 1))) * 8));
+}
+
+// V^T fragment of PV step t (block db = t / 4, kb = (t / 2) % 2, c2 = t % 2):
+// 16 bytes of channel row 32db + l32, keys 64half + 32kb + 16c2 + 8h .. +7,
+// i.e. chunk 8half + 4kb + 2c2 + h of the row, at its swizzled position.
+template <int D>
+__device__ __forceinline__ u32x4 v_frag(const uint16_t* vs, int t, int half, int h, int l32) {
+  const int db = t / 4, kb = (t / 2) % 2, c2 = t % 2;
+  const int d = 32 * db + l32;
+  return *reinterpret_cast<const u32x4*>(vs + d * kTok + (((8 * half + 4 * kb + 2 * c2 + h) ^ (d & 15)) * 8));
+}
+
+// The hot part of one pipelined iteration, in the order the instructions
+// are to issue. Step t issues one QK^T MFMA of the next tile (operand read
+// kLook steps ahead), one pair of exponentials of this tile and, every other
+// step, one LDS-DMA chunk, so the VALU work and the copies run while the
+// matrix core is busy and no burst of copies fills the vector-memory queue.
+// The PV MFMAs of this tile follow, their V^T reads kLook steps ahead.
+// Scheduling fences keep each step's instructions together.
+template <int D>
+__device__ __forceinline__ void hot_tile(WaveState<D>& w, const floatx16 (&s_cur)[2], floatx16 (&s_next)[2],
+                                         const uint16_t* ks_next, const uint16_t* vs_cur, const DmaPlan<D>& pl,
+                                         uint32_t dma_tile_bytes, lds_u16* dma_dst, int half, int h, int l32,
+                                         float scale_log2) {
+  using S = AttnShape<D>;
+  constexpr int kLook = 4;
+  constexpr int kS = 2 * S::kDC;           // QK^T MFMAs per tile
+  constexpr int kE = 16;                   // exponential pairs per tile
+  constexpr int kPV = 4 * S::kDB;          // PV MFMAs per tile
+  constexpr int kSteps = kS > kE ? kS : kE;
+
   // A half that has seen only pad keys so far keeps m = -inf; its exponents
   // must then still be exp2(-inf) = 0, not NaN.
   const float m_use = w.m_run == -__builtin_inff() ? 0.0f : w.m_run;
   float psum = 0.0f;
+  u32x4 pf[2][2];
+  u32x4 kf[kS];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int t = 0; t < kLook && t < kS; ++t) kf[t] = k_frag<D>(ks_next, t, half, h, l32);
 #pragma unroll
-    for (int v = 0; v < 16; v += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], scale_log2, -m_use));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v + 1], scale_log2, -m_use));
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s_next[kb][v] = 0.0f;
+
+#pragma unroll
+  for (int t = 0; t < kSteps; ++t) {
+    if (t + kLook < kS) kf[t + kLook] = k_frag<D>(ks_next, t + kLook, half, h, l32);
+    if (t < kS) {
+      const int kb = t / S::kDC, dc = t % S::kDC;
+      s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[t]), as_bf16x8(w.qf[dc]), s_next[kb], 0, 0, 0);
+    }
+    if (t < kE) {  // keys v, v + 1 of block kb
+      const int kb = t / 8, v = 2 * (t % 8);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][v], scale_log2, -m_use));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][v + 1], scale_log2, -m_use));
       psum += p0 + p1;
       pf[kb][v / 8][(v % 8) / 2] = pack_bf16x2(p0, p1);
     }
+    if (t % 2 == 1 && t / 2 < S::kChunksPerWave)
+      dma_copy(pl.base, pl.bytes, pl.off[t / 2], dma_tile_bytes, dma_dst + (pl.first + t / 2) * 512);
+    __builtin_amdgcn_sched_barrier(0);
   }
   w.l_run += psum;
-}
 
-// O^T[db] += V^T P^T over this half's 64 keys, 16 at a time: k-slot v' of
-// half-wave h is key 64half + 32kb + 16c2 + 8h + v', i.e. 16-byte chunk
-// 8half + 4kb + 2c2 + h of the V^T row.
-template <int D>
-__device__ __forceinline__ void pv_tile(WaveState<D>& w, const u32x4 (&pf)[2][2], const uint16_t* vs, int half,
-                                        int h, int l32) {
-  using S = AttnShape<D>;
+  u32x4 vf[kPV];
 #pragma unroll
-  for (int db = 0; db < S::kDB; ++db) {
-    const int d = 32 * db + l32;
-    const int t0 = (8 * half + h) ^ (d & 15);
-    const uint16_t* vrow = vs + d * kTok;
+  for (int t = 0; t < kLook; ++t) vf[t] = v_frag<D>(vs_cur, t, half, h, l32);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const u32x4 vf = *reinterpret_cast<const u32x4*>(vrow + ((t0 ^ (4 * kb + 2 * c2)) * 8));
-        w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[kb][c2]), w.oacc[db], 0, 0, 0);
-      }
-    }
+  for (int t = 0; t < kPV; ++t) {
+    if (t + kLook < kPV) vf[t + kLook] = v_frag<D>(vs_cur, t + kLook, half, h, l32);
+    const int db = t / 4, kb = (t / 2) % 2, c2 = t % 2;
+    w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[t]), as_bf16x8(pf[kb][c2]), w.oacc[db], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -279,11 +333,11 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
   const int32_t* sel = idx + (head_base + tq) * k_max;
   const unsigned nT = unsigned(hg.nT);
   const int kh = hg.k;
-  const DmaPlan<D> plan = dma_plan<D>(wave, lane);
-  // This wave's copy source: K or V of this head. Entries outside
-  // [0, nT_hd) contribute no keys; tile 0 stands in as a harmless source.
-  const uint16_t* role_base = (plan.is_k ? k_t : v_t) + head_base * tile_elems;
-  auto tile_src = [&](int32_t jt) { return role_base + int64_t(unsigned(jt) < nT ? jt : 0) * tile_elems; };
+  const DmaPlan<D> plan = dma_plan<D>(wave, lane, k_t + head_base * tile_elems, v_t + head_base * tile_elems, g.nT_max);
+  // Byte offset of a copy source tile; entries outside [0, nT_hd) contribute
+  // no keys and tile 0 stands in as a harmless source.
+  auto tile_src = [&](int32_t jt) { return uint32_t(unsigned(jt) < nT ? jt : 0) * uint32_t(tile_elems * 2); };
+  lds_u16* const lbuf = (lds_u16*)&lds[0][0];   // lds[b] is lbuf + b * kTileElems
 
   WaveState<D> w;
   {
@@ -304,13 +358,16 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
   //   K of tile t in lds[t & 1]; V of tile t in lds[2 + (t & 1)].
   // A buffer is overwritten only after the barrier that ends the iteration
   // in which it was last read.
-  int32_t j = sel[0];
-  const int32_t j1 = kh > 1 ? sel[1] : 0;
+  // Tile indices of iterations i, i+1, i+2 (clamped to the last entry
+  // past the end: such copies and products are never used). The next one is
+  // loaded just before each iteration's closing barrier, so no scalar load is
+  // in flight while the LDS operand reads are being waited for.
+  int32_t j = sel[0], jn = sel[min(1, kh - 1)], jn2 = sel[min(2, kh - 1)];
   if (plan.is_k) {
-    dma_issue<D>(plan, tile_src(j), lds[0]);
-    dma_issue<D>(plan, tile_src(j1), lds[1]);
+    dma_issue<D>(plan, tile_src(j), lbuf);
+    dma_issue<D>(plan, tile_src(jn), lbuf + S::kTileElems);
   } else {
-    dma_issue<D>(plan, tile_src(j), lds[2]);
+    dma_issue<D>(plan, tile_src(j), lbuf + 2 * S::kTileElems);
   }
   __builtin_amdgcn_s_waitcnt(0);  // Q and the first copies have landed
   __syncthreads();
@@ -322,34 +379,15 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
   // tile i+1 (computed unconditionally; after the last tile it is unused).
   auto iteration = [&](int i, floatx16 (&s_cur)[2], floatx16 (&s_next)[2]) {
     const int cur = i & 1;
-    const int32_t jn = i + 1 < kh ? sel[i + 1] : 0;
-    if (plan.is_k) {
-      if (i + 2 < kh) dma_issue<D>(plan, tile_src(sel[i + 2]), lds[cur]);
-    } else {
-      if (i + 1 < kh) dma_issue<D>(plan, tile_src(jn), lds[2 + (cur ^ 1)]);
-    }
     softmax_max<D>(w, s_cur, real_key_bits(g, hg, j, half, h), scale_log2);
-    u32x4 pf[2][2];
-    s_tile<D>(s_next, w, lds[cur ^ 1], half, h, l32);
-    softmax_exp<D>(w, s_cur, pf, scale_log2);
-    pv_tile<D>(w, pf, lds[2 + cur], half, h, l32);
-    // Interleave: K operand reads run ahead; each S MFMA of the next tile is
-    // followed by a slice of this tile's softmax arithmetic, so the VALU work
-    // runs while the matrix core is busy; the PV MFMAs follow.
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-    }
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
+    // K of tile i+2 into lds[cur] (K of tile i, read in the previous
+    // iteration) or V of tile i+1 into lds[2 + (cur ^ 1)] (V of tile i-1).
+    hot_tile<D>(w, s_cur, s_next, lds[cur ^ 1], lds[2 + cur], plan, tile_src(plan.is_k ? jn2 : jn),
+                lbuf + (plan.is_k ? cur : 2 + (cur ^ 1)) * S::kTileElems, half, h, l32, scale_log2);
     j = jn;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies for the next iteration have landed
+    jn = jn2;
+    jn2 = sel[min(i + 3, kh - 1)];
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies and the next index have landed
     __syncthreads();
   };
   floatx16 sn[2];
