@@ -172,6 +172,7 @@ __device__ __forceinline__ void s_tile(floatx16 (&sacc)[2], const WaveState<D>& 
 // 0 for an index outside the head (the tile then contributes nothing).
 __device__ __forceinline__ uint64_t real_key_bits(const GeoTable& g, const HeadGeo& hg, int32_t j, int half, int h) {
   if (unsigned(j) >= unsigned(hg.nT)) return 0ull;
+  if (hg.all_full) return ~0ull;
   const BoxExtent e = box_extent(g, hg, j);
   if (box_is_full(hg, e)) return ~0ull;
   return box_slot_mask64(hg, e, 64 * half) >> (8 * h);
@@ -262,17 +263,14 @@ __device__ __forceinline__ void hot_tile(WaveState<D>& w, const floatx16 (&s_cur
   u32x4 kf[kS];
 #pragma unroll
   for (int t = 0; t < kLook && t < kS; ++t) kf[t] = k_frag<D>(ks_next, t, half, h, l32);
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s_next[kb][v] = 0.0f;
-
+  const floatx16 zero = {};
 #pragma unroll
   for (int t = 0; t < kSteps; ++t) {
     if (t + kLook < kS) kf[t + kLook] = k_frag<D>(ks_next, t + kLook, half, h, l32);
     if (t < kS) {
       const int kb = t / S::kDC, dc = t % S::kDC;
-      s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[t]), as_bf16x8(w.qf[dc]), s_next[kb], 0, 0, 0);
+      s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[t]), as_bf16x8(w.qf[dc]),
+                                                           dc == 0 ? zero : s_next[kb], 0, 0, 0);
     }
     if (t < kE) {  // keys v, v + 1 of block kb
       const int kb = t / 8, v = 2 * (t % 8);

@@ -38,6 +38,7 @@ int build_table(const veda_geom* g, GeoTable* t) {
     h.lpt = uint8_t(__builtin_ctz(unsigned(tl.pt)));
     h.lph = uint8_t(__builtin_ctz(unsigned(tl.ph)));
     h.lpw = uint8_t(__builtin_ctz(unsigned(tl.pw)));
+    h.all_full = uint8_t(g->grid.T % tl.pt == 0 && g->grid.H % tl.ph == 0 && g->grid.W % tl.pw == 0);
     const int64_t nTt = (int64_t(g->grid.T) + tl.pt - 1) / tl.pt;
     const int64_t nTh = (int64_t(g->grid.H) + tl.ph - 1) / tl.ph;
     const int64_t nTw = (int64_t(g->grid.W) + tl.pw - 1) / tl.pw;

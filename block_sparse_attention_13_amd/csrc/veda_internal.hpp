@@ -11,9 +11,11 @@
 namespace veda {
 
 // Per-head tiling: edges are powers of two (their product is 128), stored as
-// log2; box counts along h and w; total boxes; kept tiles per query tile.
+// log2; whether every box is full (each grid edge a multiple of the tile
+// edge: no pad slots anywhere); box counts along h and w; total boxes; kept
+// tiles per query tile.
 struct HeadGeo {
-  uint8_t lpt, lph, lpw, pad_;
+  uint8_t lpt, lph, lpw, all_full;
   int32_t nTh, nTw, nT, k;
 };
 
