@@ -94,7 +94,7 @@ template <int D>
 struct DmaPlan {
   const uint16_t* base;                         // this head's K or V tiles
   int32_t bytes;                                // their extent
-  uint32_t off[AttnShape<D>::kChunksPerWave];   // per-lane source byte offsets within a tile
+  uint32_t off[4];                              // per-lane source byte offsets of chunks first..first+3
   int first;                                    // first chunk of this wave
   bool is_k;                                    // wave copies K (else V)
 };
@@ -108,8 +108,10 @@ __device__ __forceinline__ DmaPlan<D> dma_plan(int wave, int lane, const uint16_
   pl.first = (pl.is_k ? wave : wave - kWaves / 2) * S::kChunksPerWave;
   pl.base = pl.is_k ? k_head : v_head;
   pl.bytes = n_tiles * S::kTileElems * 2;
+  // The swizzle repeats every 16 rows = 4 chunks, so chunk first + 4q + s
+  // starts 4096q bytes after chunk first + s.
 #pragma unroll
-  for (int i = 0; i < S::kChunksPerWave; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const int c = pl.first + i;
     if (pl.is_k) {  // token-major K: kKRowsPerChunk rows of D per chunk
       const int r = c * S::kKRowsPerChunk + lane / S::kKPos, p = lane % S::kKPos;
@@ -135,7 +137,7 @@ template <int D>
 __device__ __forceinline__ void dma_issue(const DmaPlan<D>& pl, uint32_t tile_bytes, lds_u16* dst) {
 #pragma unroll
   for (int i = 0; i < AttnShape<D>::kChunksPerWave; ++i)
-    dma_copy(pl.base, pl.bytes, pl.off[i], tile_bytes, dst + (pl.first + i) * 512);
+    dma_copy(pl.base, pl.bytes, pl.off[i % 4], tile_bytes + 4096u * (i / 4), dst + (pl.first + i) * 512);
 }
 
 // Per-wave state of the online softmax for 32 queries x one key half.
@@ -249,7 +251,8 @@ __device__ __forceinline__ void hot_tile(WaveState<D>& w, const floatx16 (&s_cur
                                          uint32_t dma_tile_bytes, lds_u16* dma_dst, int half, int h, int l32,
                                          float scale_log2) {
   using S = AttnShape<D>;
-  constexpr int kLook = 4;
+  constexpr int kLook = 4;                 // LDS operand reads in flight ahead of the S MFMAs
+  constexpr int kLookV = 4;                // ... and ahead of the PV MFMAs
   constexpr int kS = 2 * S::kDC;           // QK^T MFMAs per tile
   constexpr int kE = 16;                   // exponential pairs per tile
   constexpr int kPV = 4 * S::kDB;          // PV MFMAs per tile
@@ -280,17 +283,17 @@ __device__ __forceinline__ void hot_tile(WaveState<D>& w, const floatx16 (&s_cur
       pf[kb][v / 8][(v % 8) / 2] = pack_bf16x2(p0, p1);
     }
     if (t % 2 == 1 && t / 2 < S::kChunksPerWave)
-      dma_copy(pl.base, pl.bytes, pl.off[t / 2], dma_tile_bytes, dma_dst + (pl.first + t / 2) * 512);
+      dma_copy(pl.base, pl.bytes, pl.off[(t / 2) % 4], dma_tile_bytes + 4096u * (t / 8), dma_dst + (pl.first + t / 2) * 512);
     __builtin_amdgcn_sched_barrier(0);
   }
   w.l_run += psum;
 
   u32x4 vf[kPV];
 #pragma unroll
-  for (int t = 0; t < kLook; ++t) vf[t] = v_frag<D>(vs_cur, t, half, h, l32);
+  for (int t = 0; t < kLookV; ++t) vf[t] = v_frag<D>(vs_cur, t, half, h, l32);
 #pragma unroll
   for (int t = 0; t < kPV; ++t) {
-    if (t + kLook < kPV) vf[t + kLook] = v_frag<D>(vs_cur, t + kLook, half, h, l32);
+    if (t + kLookV < kPV) vf[t + kLookV] = v_frag<D>(vs_cur, t + kLookV, half, h, l32);
     const int db = t / 4, kb = (t / 2) % 2, c2 = t % 2;
     w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[t]), as_bf16x8(pf[kb][c2]), w.oacc[db], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
