@@ -84,6 +84,27 @@ def attention_traffic(workload: str):
     return int(m_b.group(1))
 
 
+ATTN_MFMA_COUNTERS = os.path.join(ROOT, "profiles", "sparse_attn_long245k_mfma_counters.md")
+
+
+def attention_mfma_counters(workload: str):
+    """MFMA-busy fraction of SIMD cycles and the effective shader clock of the
+    attention kernel from the committed rocprofv3 counter summary, or None
+    when it is missing, covers another workload or another kernel source."""
+    import hashlib
+    if workload != "long" or not os.path.exists(ATTN_MFMA_COUNTERS):
+        return None
+    with open(ATTN_MFMA_COUNTERS) as f:
+        text = f.read()
+    vals = dict(re.findall(r"^(mfma_busy_frac|effective_clock_ghz|kernel_source_sha256_16) = (\S+)$", text, re.M))
+    if len(vals) != 3:
+        return None
+    with open(ATTN_SOURCE, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != vals["kernel_source_sha256_16"]:
+            return None
+    return {"mfma_busy_frac": float(vals["mfma_busy_frac"]), "effective_clock_ghz": float(vals["effective_clock_ghz"])}
+
+
 def attention_bytes(w) -> int:
     """Algorithmic HBM bytes of one attention launch: Q, K, V read once, O and
     LSE written once, the index lists read once."""
@@ -132,43 +153,31 @@ def cpu_baseline(w, data, sample_tiles: int, seconds_hint: float = 20.0):
     }
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="long")
-    ap.add_argument("--heads", type=int, default=0, help="run only the first N heads (0 = all)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tiles", type=int, default=1920)
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="only run a plain device copy of MIB MiB a few times (HBM counter calibration)")
-    args = ap.parse_args()
+def valid_pair_flops(w, idx_cpu) -> float:
+    """Attention flops over real query x real key pairs only (pad slots of
+    border tiles excluded), from the kept tile lists."""
+    import numpy as np
+    T, H, W = w.grid
+    total = 0.0
+    for hd, (pt, ph, pw) in enumerate(w.head_tiles()):
+        nTt, nTh, nTw = -(-T // pt), -(-H // ph), -(-W // pw)
+        ct = np.minimum(pt, T - np.arange(nTt) * pt)
+        ch = np.minimum(ph, H - np.arange(nTh) * ph)
+        cw = np.minimum(pw, W - np.arange(nTw) * pw)
+        real = (ct[:, None, None] * ch[None, :, None] * cw[None, None, :]).reshape(-1).astype(np.float64)
+        k = w.k_per_head()[hd]
+        for b in range(w.B):
+            sel = idx_cpu[b, hd, :len(real), :k]
+            total += float((real[:, None] * real[sel]).sum())
+    return 4.0 * w.d * total
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the layer shards by head with no communication, "
-              "and multi-GPU runs are not part of this build", file=sys.stderr)
-        sys.exit(2)
 
+def run_workload(V, datagen, w, steps, warmup, keep_data=True):
+    """Generate the workload's inputs, run one layer to allocate every buffer,
+    then time `steps` layers after `warmup` untimed ones with HIP events on
+    the launch stream around each of the five stages."""
     import numpy as np
     import torch
-
-    if args.calibrate_copy:
-        n = args.calibrate_copy * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes_each_way": n * 4, "launches": 5}), flush=True)
-        return
-
-    import block_sparse_attention_13_amd as V
-    import datagen
-
-    w = datagen.WORKLOADS[args.workload]
-    if args.heads:
-        w = w.with_heads(args.heads)
     log(f"[bench] workload {w.name}: {w.description}")
     t0 = time.perf_counter()
     data = datagen.generate(w)
@@ -209,15 +218,15 @@ def main():
         if ev is not None:
             ev[5].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup} done")
+    log(f"[bench] warmup {warmup} done")
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
         step(events[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -229,13 +238,81 @@ def main():
         total.append(ev[0].elapsed_time(ev[5]))
     ms_step = float(np.mean(total))
     stage_ms = {n: round(float(np.mean(v)), 4) for n, v in per_stage.items()}
-    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/layer (wall {wall / args.steps * 1e3:.3f} ms); {stage_ms}")
+    log(f"[bench] timed {steps} steps: {ms_step:.3f} ms/layer (wall {wall / steps * 1e3:.3f} ms); {stage_ms}")
+    out = {"ms_step": ms_step, "stage_ms": stage_ms, "data": data if keep_data else None,
+           "valid_flops": valid_pair_flops(w, bufs["idx"].cpu().numpy())}
+    del bufs, q, k, v, wq, wk
+    torch.cuda.empty_cache()
+    return out
 
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long")
+    ap.add_argument("--heads", type=int, default=0, help="run only the first N heads (0 = all)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="time only the main workload (skip tiny, 480p, 720p, hc)")
+    ap.add_argument("--cpu-sample-tiles", type=int, default=1920)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB a few times (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the layer shards by head with no communication, "
+              "and multi-GPU runs are not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_each_way": n * 4, "launches": 5}), flush=True)
+        return
+
+    import block_sparse_attention_13_amd as V
+    import datagen
+
+    w = datagen.WORKLOADS[args.workload]
+    if args.heads:
+        w = w.with_heads(args.heads)
+    r = run_workload(V, datagen, w, args.steps, args.warmup)
+    ms_step, stage_ms, data = r["ms_step"], r["stage_ms"], r["data"]
     f_attn = attention_flops(w)
-    t_attn = stage_ms["sparse_attn"] * 1e-3
-    achieved = f_attn / t_attn / 1e12
+    achieved = f_attn / (stage_ms["sparse_attn"] * 1e-3) / 1e12
     sb = stage_bytes(w)
     hbm = {n: round(sb[n] / (stage_ms[n] * 1e-3) / 1e9, 1) for n in sb}
+
+    # The other synthetic workloads, each timed the same way (fewer steps):
+    # ms per layer and the attention kernel's effective TFLOP/s over whole
+    # tile pairs and over real (non-pad) query x key pairs.
+    per_config = {}
+    if not args.no_other_configs and not args.heads:
+        for name in ("tiny", "480p", "720p", "hc"):
+            if name == args.workload:
+                continue
+            wo = datagen.WORKLOADS[name]
+            ro = run_workload(V, datagen, wo, 5, 2, keep_data=False)
+            t_a = ro["stage_ms"]["sparse_attn"] * 1e-3
+            fo, fv = attention_flops(wo), ro["valid_flops"]
+            per_config[name] = {
+                "workload": wo.description, "ms_per_layer": round(ro["ms_step"], 4),
+                "attn_ms": round(ro["stage_ms"]["sparse_attn"], 4),
+                "attn_tflops": round(fo / t_a / 1e12, 1), "attn_frac_bf16_peak": round(fo / t_a / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "attn_tflops_valid_pairs": round(fv / t_a / 1e12, 1),
+                "stage_ms": ro["stage_ms"],
+            }
+            log(f"[bench] {name}: {per_config[name]['ms_per_layer']} ms/layer, attention "
+                f"{per_config[name]['attn_tflops']} TFLOP/s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -265,8 +342,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": attention_traffic(args.workload),
                      "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": attention_bytes(w),
-                     "kernel": "sparse_attn_fwd_kernel<128>", "flops_per_launch": f_attn},
+                     "kernel": "sparse_attn_fwd_kernel<128>", "flops_per_launch": f_attn,
+                     "counters": attention_mfma_counters(args.workload)},
         "cpu_baseline": cpu,
+        "per_config": per_config,
     }
     print(json.dumps(line), flush=True)
 
