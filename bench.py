@@ -246,6 +246,42 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True):
     return out
 
 
+def dense_reference(V, w, data, steps=2, warmup=1):
+    """Dense attention on the same inputs: every key tile kept (k = nT per
+    head) through the same tile-skipping kernel. Times the attention call
+    only, with HIP events on the launch stream."""
+    import numpy as np
+    import torch
+    dev = torch.device("cuda:0")
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(dev)
+    geom = V.Geometry(w.B, w.heads, w.d, w.grid, w.head_tiles())
+    nts = [geom.num_tiles(hd) for hd in range(w.heads)]
+    nT = geom.max_tiles()
+    q_t = V.tile_permute(to(data["q"]), geom)
+    k_t = V.tile_permute(to(data["k"]), geom)
+    v_t = V.tile_permute(to(data["v"]), geom, layout=V.CHANNEL_MAJOR)
+    idx = torch.arange(nT, dtype=torch.int32, device=dev).expand(w.B, w.heads, nT, nT).contiguous()
+    o_t = torch.empty_like(q_t)
+    lse = torch.empty((w.B, w.heads, nT, 128), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        V.sparse_attn_fwd(q_t, k_t, v_t, idx, geom, nts, o_t=o_t, lse=lse)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        V.sparse_attn_fwd(q_t, k_t, v_t, idx, geom, nts, o_t=o_t, lse=lse)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+    flops = 4.0 * w.d * 128 * 128 * sum(n * n for n in nts) * w.B
+    del q_t, k_t, v_t, idx, o_t, lse
+    torch.cuda.empty_cache()
+    return {"attn_ms": round(ms, 3), "attn_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "attn_frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kept_tiles": "all", "steps": steps}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +290,7 @@ def main():
     ap.add_argument("--workload", default="long")
     ap.add_argument("--heads", type=int, default=0, help="run only the first N heads (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense (every tile kept) reference")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="time only the main workload (skip tiny, 480p, 720p, hc)")
     ap.add_argument("--cpu-sample-tiles", type=int, default=1920)
@@ -314,6 +351,13 @@ def main():
             log(f"[bench] {name}: {per_config[name]['ms_per_layer']} ms/layer, attention "
                 f"{per_config[name]['attn_tflops']} TFLOP/s")
 
+    dense = None
+    if not args.no_dense and not args.heads:
+        log("[bench] dense reference: every key tile kept, same kernel")
+        dense = dense_reference(V, w, data)
+        dense["sparse_speedup"] = round(dense["attn_ms"] / stage_ms["sparse_attn"], 2)
+        log(f"[bench] dense: {dense}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
@@ -346,6 +390,7 @@ def main():
                      "counters": attention_mfma_counters(args.workload)},
         "cpu_baseline": cpu,
         "per_config": per_config,
+        "dense_reference": dense,
     }
     print(json.dumps(line), flush=True)
 
