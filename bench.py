@@ -240,16 +240,19 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True):
     stage_ms = {n: round(float(np.mean(v)), 4) for n, v in per_stage.items()}
     log(f"[bench] timed {steps} steps: {ms_step:.3f} ms/layer (wall {wall / steps * 1e3:.3f} ms); {stage_ms}")
     out = {"ms_step": ms_step, "stage_ms": stage_ms, "data": data if keep_data else None,
-           "valid_flops": valid_pair_flops(w, bufs["idx"].cpu().numpy())}
+           "valid_flops": valid_pair_flops(w, bufs["idx"].cpu().numpy()),
+           "bitmask": bufs["bitmask"] if keep_data else None}
     del bufs, q, k, v, wq, wk
     torch.cuda.empty_cache()
     return out
 
 
-def dense_reference(V, w, data, steps=2, warmup=1):
+def dense_reference(V, w, data, trip_bitmask=None, steps=2, warmup=1):
     """Dense attention on the same inputs: every key tile kept (k = nT per
     head) through the same tile-skipping kernel. Times the attention call
-    only, with HIP events on the launch stream."""
+    only, with HIP events on the launch stream. Then, from the dense LSE, the
+    teacher (max-pooled dense attention), the oracle tile mask (Top-k of the
+    teacher) and the tile recall of the layer's TripPool mask against it."""
     import numpy as np
     import torch
     dev = torch.device("cuda:0")
@@ -275,11 +278,34 @@ def dense_reference(V, w, data, steps=2, warmup=1):
     torch.cuda.synchronize()
     ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
     flops = 4.0 * w.d * 128 * 128 * sum(n * n for n in nts) * w.B
-    del q_t, k_t, v_t, idx, o_t, lse
+    del idx, o_t, v_t
+    res = {"attn_ms": round(ms, 3), "attn_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "attn_frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "kept_tiles": "all", "steps": steps}
+    if trip_bitmask is not None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        teacher = V.teacher_tile_max(q_t, k_t, lse, geom)
+        e1.record(stream)
+        ks = w.k_per_head()
+        _, oracle_bm = V.topk_mask(teacher, geom, ks)
+        rec = V.tile_recall(V.mask_overlap(trip_bitmask, oracle_bm, geom), geom, ks)
+        torch.cuda.synchronize()
+        t_ms = e0.elapsed_time(e1)
+        flat = [r for row in rec for r in row]
+        res["teacher"] = {
+            "ms": round(t_ms, 3),
+            "tflops_qk": round(0.5 * flops / (t_ms * 1e-3) / 1e12, 1),
+            "trippool_tile_recall_mean": round(float(np.mean(flat)), 4),
+            "trippool_tile_recall_min": round(float(np.min(flat)), 4),
+            "trippool_tile_recall_max": round(float(np.max(flat)), 4),
+            "chance_k_over_nT": round(float(np.mean([k / n for k, n in zip(ks, nts)])), 4),
+            "note": "random-init TripPool projections (no distillation): recall near chance is expected",
+        }
+        del teacher, oracle_bm
+    del q_t, k_t, lse
     torch.cuda.empty_cache()
-    return {"attn_ms": round(ms, 3), "attn_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
-            "attn_frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "kept_tiles": "all", "steps": steps}
+    return res
 
 
 def main():
@@ -354,7 +380,7 @@ def main():
     dense = None
     if not args.no_dense and not args.heads:
         log("[bench] dense reference: every key tile kept, same kernel")
-        dense = dense_reference(V, w, data)
+        dense = dense_reference(V, w, data, trip_bitmask=r["bitmask"])
         dense["sparse_speedup"] = round(dense["attn_ms"] / stage_ms["sparse_attn"], 2)
         log(f"[bench] dense: {dense}")
 

@@ -12,6 +12,13 @@ Python: the five steps of the layer are HIP kernels.
   sparse_attn_fwd  tiled Q, K, V + index lists -> tiled O (+ LSE)
   tile_unpermute   tiled -> raster
   layer_forward    the five calls in order
+
+Measuring a mask against the method's own target:
+  dense_index      index lists that keep every key tile (dense attention through sparse_attn_fwd)
+  teacher_tile_max max-pooled dense attention per (query tile, key tile); topk_mask of it is the
+                   oracle tile mask
+  mask_overlap     kept tiles two masks have in common, per (batch, head)
+  tile_recall      overlap / (k_hd * nT_hd)
 """
 
 from __future__ import annotations
@@ -26,7 +33,7 @@ from . import _lib
 from ._lib import VedaError
 
 __all__ = ["Geometry", "VedaError", "tile_permute", "tile_unpermute", "trippool_score", "topk_mask",
-           "sparse_attn_fwd", "layer_forward", "TILE_TOKENS", "TOKEN_MAJOR", "CHANNEL_MAJOR"]
+           "sparse_attn_fwd", "layer_forward", "dense_index", "teacher_tile_max", "mask_overlap", "tile_recall", "TILE_TOKENS", "TOKEN_MAJOR", "CHANNEL_MAJOR"]
 
 TILE_TOKENS = _lib.VEDA_TILE_TOKENS
 TOKEN_MAJOR = _lib.VEDA_TILED_TOKEN_MAJOR
@@ -245,3 +252,55 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.
                                          o_t=b.get("o_t"), lse=b.get("lse"))
     b["o"] = tile_unpermute(b["o_t"], geom, b.get("o"))
     return b
+
+
+def dense_index(geom: Geometry, device) -> Tuple[torch.Tensor, List[int]]:
+    """Index lists that keep every key tile of every head (idx[..., j] = j)
+    and the matching k per head: sparse_attn_fwd with these is dense
+    attention, and its LSE is the one teacher_tile_max needs."""
+    nT = geom.max_tiles()
+    idx = torch.arange(nT, dtype=torch.int32, device=device).expand(geom.B, geom.n_heads, nT, nT).contiguous()
+    return idx, [geom.num_tiles(hd) for hd in range(geom.n_heads)]
+
+
+def teacher_tile_max(q_t: torch.Tensor, k_t: torch.Tensor, lse_dense: torch.Tensor, geom: Geometry,
+                     scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Max-pooled dense attention: [B, heads, nT_max, nT_max] fp32, the
+    largest dense softmax probability between each query tile and key tile
+    (-inf outside the head's block). lse_dense is the LSE of sparse_attn_fwd
+    run with dense_index."""
+    tshape = _tiled_shape(geom, geom.head_dim)
+    _need(q_t, torch.bfloat16, tshape, "q_tiled")
+    _need(k_t, torch.bfloat16, tshape, "k_tiled")
+    _need(lse_dense, torch.float32, tshape[:4], "lse_dense")
+    nT = tshape[2]
+    if out is None:
+        out = torch.empty((geom.B, geom.n_heads, nT, nT), dtype=torch.float32, device=q_t.device)
+    _need(out, torch.float32, (geom.B, geom.n_heads, nT, nT), "teacher")
+    sc = float(scale) if scale is not None else 0.0
+    _lib.check(_lib.lib.veda_teacher_tile_max(geom.c, q_t.data_ptr(), k_t.data_ptr(), lse_dense.data_ptr(), sc,
+                                              out.data_ptr(), _stream(q_t)), "veda_teacher_tile_max")
+    return out
+
+
+def mask_overlap(bitmask_a: torch.Tensor, bitmask_b: torch.Tensor, geom: Geometry,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Common kept tiles of two masks: [B, heads] (int64 here; the counts are
+    far below 2^63), the sum over each head's query tiles of popcount(a & b)."""
+    nT = geom.max_tiles()
+    shape = (geom.B, geom.n_heads, nT, (nT + 31) // 32)
+    _need(bitmask_a, torch.uint32, shape, "bitmask_a")
+    _need(bitmask_b, torch.uint32, shape, "bitmask_b")
+    if out is None:
+        out = torch.empty((geom.B, geom.n_heads), dtype=torch.int64, device=bitmask_a.device)
+    _need(out, torch.int64, (geom.B, geom.n_heads), "counts")
+    _lib.check(_lib.lib.veda_mask_overlap(geom.c, bitmask_a.data_ptr(), bitmask_b.data_ptr(), out.data_ptr(),
+                                          _stream(bitmask_a)), "veda_mask_overlap")
+    return out
+
+
+def tile_recall(counts: torch.Tensor, geom: Geometry, k_per_head: Sequence[int]) -> List[List[float]]:
+    """Tile recall per (batch, head): common kept tiles / (k_hd * nT_hd)."""
+    c = counts.cpu().tolist()
+    return [[int(c[b][hd]) / (k_per_head[hd] * geom.num_tiles(hd)) for hd in range(geom.n_heads)]
+            for b in range(geom.B)]

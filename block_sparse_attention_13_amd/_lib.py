@@ -24,7 +24,8 @@ STATUS = {
 }
 
 EXPORTS = ["veda_status_str", "veda_num_tiles", "veda_max_tiles", "veda_tile_permute", "veda_trippool_score",
-           "veda_topk_mask", "veda_sparse_attn_fwd", "veda_tile_unpermute"]
+           "veda_topk_mask", "veda_sparse_attn_fwd", "veda_tile_unpermute", "veda_teacher_tile_max",
+           "veda_mask_overlap"]
 
 
 class VedaGrid(ctypes.Structure):
@@ -73,6 +74,10 @@ def _load():
     lib.veda_sparse_attn_fwd.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_void_p,
                                          POINTER(c_int32), c_int32, c_float, c_void_p, c_void_p, c_void_p]
     lib.veda_sparse_attn_fwd.restype = ctypes.c_int
+    lib.veda_teacher_tile_max.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p]
+    lib.veda_teacher_tile_max.restype = ctypes.c_int
+    lib.veda_mask_overlap.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.veda_mask_overlap.restype = ctypes.c_int
     return lib
 
 

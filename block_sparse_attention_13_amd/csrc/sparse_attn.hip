@@ -33,55 +33,14 @@
 // under the compute of tile i. Query tiles of a head are dealt out so each XCD
 // works on a contiguous run of neighbouring query tiles, whose key selections
 // overlap, while all XCDs share the same head's K/V in the MALL.
-#include "veda_internal.hpp"
+#include "attn_tiles.hpp"
 
 namespace veda {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float floatx2 __attribute__((ext_vector_type(2)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+using namespace attn;
 
-constexpr int kThreads = 512;           // 8 waves: 4 query groups x 2 key halves
-constexpr int kWaves = kThreads / 64;
-constexpr int kTok = VEDA_TILE_TOKENS;  // 128 keys / queries per tile
 constexpr float kRescaleSlack = 8.0f;   // log2 of the largest unnormalised P
-
-template <int D>
-struct AttnShape {
-  static constexpr int kTileElems = kTok * D;           // one K or V tile (bf16 elements)
-  static constexpr int kKPos = D / 8;                   // 16-byte positions per K row
-  static constexpr int kKRowsPerChunk = 64 / kKPos;     // K rows per 1-KiB DMA chunk
-  static constexpr int kChunks = kTileElems / 512;      // 1-KiB chunks per tile (K or V)
-  static constexpr int kChunksPerWave = 2 * kChunks / kWaves;
-  static constexpr int kDC = D / 16;                    // MFMA k-steps over the head dim
-  static constexpr int kDB = D / 32;                    // 32-row blocks of O^T
-  static_assert(kChunks % (kWaves / 2) == 0, "K and V chunks split over 4 waves each");
-};
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const floatx2 f = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
-}
-
-// Key row fed by lane l of a 32-key block: bits 2 and 3 of l swapped.
-__device__ __forceinline__ int key_perm(int l) { return (l & ~12) | ((l & 4) << 1) | ((l & 8) >> 1); }
-
-// Query tile handled by workgroup x of a head: the tiles of a head are split
-// into 8 contiguous runs, run r going to the workgroups x with x % 8 == r
-// (consecutive workgroups land on consecutive XCDs). Bijective for any n.
-__device__ __forceinline__ int32_t xcd_tile_order(int32_t x, int32_t n) {
-  const int32_t xcd = x % 8, pos = x / 8, q = n / 8, r = n % 8;
-  return xcd < r ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
-}
-
-typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 // LDS-DMA copy plan of one wave. A tile is 32 (D = 128) or 16 (D = 64)
 // chunks of 1 KiB; waves 0-3 copy K chunks, waves 4-7 V chunks, through
@@ -124,15 +83,6 @@ __device__ __forceinline__ DmaPlan<D> dma_plan(int wave, int lane, const uint16_
   return pl;
 }
 
-// One 1-KiB LDS-DMA copy: lane l loads 16 bytes at byte tile_bytes + voff
-// of a raw buffer over [base, base + bytes) (stride 0; reads past the end
-// would return 0) into LDS bytes 16l..16l+15 of dst.
-__device__ __forceinline__ void dma_copy(const uint16_t* base, int32_t bytes, uint32_t voff, uint32_t tile_bytes,
-                                         lds_u16* dst) {
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, bytes, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, tile_bytes, 0, 0);
-}
-
 template <int D>
 __device__ __forceinline__ void dma_issue(const DmaPlan<D>& pl, uint32_t tile_bytes, lds_u16* dst) {
 #pragma unroll
@@ -167,17 +117,6 @@ __device__ __forceinline__ void s_tile(floatx16 (&sacc)[2], const WaveState<D>& 
       sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(w.qf[dc]), sacc[kb], 0, 0, 0);
     }
   }
-}
-
-// Real-key bits of this wave's 64 keys of tile j, shifted so bit
-// 16(v/8) + 4((v/4)%2) + v%4 (+32 for kb = 1) is S^T element v of block kb;
-// 0 for an index outside the head (the tile then contributes nothing).
-__device__ __forceinline__ uint64_t real_key_bits(const GeoTable& g, const HeadGeo& hg, int32_t j, int half, int h) {
-  if (unsigned(j) >= unsigned(hg.nT)) return 0ull;
-  if (hg.all_full) return ~0ull;
-  const BoxExtent e = box_extent(g, hg, j);
-  if (box_is_full(hg, e)) return ~0ull;
-  return box_slot_mask64(hg, e, 64 * half) >> (8 * h);
 }
 
 // Mask and the running-max update of the online softmax (base 2, max moved
@@ -215,17 +154,6 @@ __device__ __forceinline__ void softmax_max(WaveState<D>& w, floatx16 (&sacc)[2]
 #pragma unroll
       for (int v = 0; v < 16; ++v) w.oacc[db][v] *= alpha;
   }
-}
-
-// K fragment of S^T step t (block kb = t / kDC, k-step dc = t % kDC) for
-// this lane: 16 bytes of key row 64half + 32kb + pi(l32), channels
-// 16dc + 8h .. +7, at its swizzled position.
-template <int D>
-__device__ __forceinline__ u32x4 k_frag(const uint16_t* ks, int t, int half, int h, int l32) {
-  using S = AttnShape<D>;
-  const int kb = t / S::kDC, dc = t % S::kDC;
-  const int r = 64 * half + 32 * kb + key_perm(l32);
-  return *reinterpret_cast<const u32x4*>(ks + r * D + (((2 * dc + h) ^ (r & (S::kKPos - 1))) * 8));
 }
 
 // V^T fragment of PV step t (block db = t / 4, kb = (t / 2) % 2, c2 = t % 2):

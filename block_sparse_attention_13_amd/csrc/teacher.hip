@@ -1,0 +1,191 @@
+// Tile-level teacher of the distillation and the overlap of two tile masks
+// (Veda page, "Attention Structure Distillation", Teacher: max-pooled full
+// attention gives a tile-level target; Principle 01 "Full-Attention Structure
+// Distillation"; "Empirical Study" 02: the oracle mask keeps each query
+// tile's highest-response key tiles, and tile recall compares masks).
+//
+// Teacher: T[b, hd, tq, j] is the largest dense softmax probability between
+// a real query of tile tq and a real key of tile j:
+//   T = max_{i in tq, m in j} exp(scale q_i.k_m - lse_i),
+// with lse_i the log-sum-exp of query i over every real key of the head (the
+// LSE of the attention forward with every key tile kept). exp is monotone,
+// so the block maximum is taken over the logits and exponentiated once.
+//
+// One workgroup (8 waves) handles one query tile and streams every key tile
+// of its head through three LDS buffers (LDS-DMA copies two tiles ahead).
+// Wave (qg, half) computes S^T for queries 32qg..32qg+31 and keys
+// 64half..64half+63 with 32x32x16 bf16 MFMAs (fp32 accumulation), takes the
+// maximum of scale*log2(e)*s - log2(e)*lse per lane, reduces it over the wave,
+// and the eight wave maxima of a key tile are combined through LDS.
+#include "attn_tiles.hpp"
+
+namespace veda {
+namespace {
+
+using namespace attn;
+
+template <int D>
+struct TeacherShape {
+  static constexpr int kChunksPerWave = AttnShape<D>::kChunks / kWaves;  // K chunks each wave copies
+};
+
+// Largest value over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_max(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void teacher_kernel(GeoTable g, const uint16_t* __restrict__ q_t,
+                                                             const uint16_t* __restrict__ k_t,
+                                                             const float* __restrict__ lse, float scale_log2,
+                                                             float* __restrict__ teacher) {
+  using S = AttnShape<D>;
+  using TS = TeacherShape<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf[3][S::kTileElems];
+  __shared__ float red[2][kWaves];
+
+  const int hd = blockIdx.y, b = blockIdx.z;
+  const HeadGeo hg = g.h[hd];
+  const int32_t tq = xcd_tile_order(blockIdx.x, g.nT_max);
+  const int64_t head_base = (int64_t(b) * g.heads + hd) * g.nT_max;
+  const int64_t tile_elems = S::kTileElems;
+  float* trow = teacher + (head_base + tq) * g.nT_max;
+  const int32_t nT = hg.nT;
+
+  // Key tiles past the head's last one, and whole rows of query tiles past
+  // it, hold -inf.
+  for (int j = (tq < nT ? nT : 0) + int(threadIdx.x); j < g.nT_max; j += kThreads) trow[j] = -__builtin_inff();
+  if (tq >= nT) return;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
+  const int qg = wave & 3, half = wave >> 2;
+  const int l32 = lane % 32, h = lane / 32;
+
+  // Q^T operand of this lane's query, and its base-2 LSE; a pad query gets
+  // +inf so that it never raises a maximum.
+  u32x4 qf[S::kDC];
+  {
+    const uint16_t* qrow = q_t + (head_base + tq) * tile_elems + (qg * 32 + l32) * D + 8 * h;
+#pragma unroll
+    for (int dc = 0; dc < S::kDC; ++dc) qf[dc] = *reinterpret_cast<const u32x4*>(qrow + 16 * dc);
+  }
+  const int slot = qg * 32 + l32;
+  const bool q_real = hg.all_full || slot_is_real(hg, box_extent(g, hg, tq), slot);
+  const float lse2 = q_real ? lse[(head_base + tq) * kTok + slot] * 1.44269504088896340736f : __builtin_inff();
+
+  // K-only LDS-DMA plan: wave w copies chunks w*cpw .. w*cpw + cpw - 1.
+  uint32_t off[TS::kChunksPerWave];
+#pragma unroll
+  for (int i = 0; i < TS::kChunksPerWave; ++i) {
+    const int c = wave * TS::kChunksPerWave + i;
+    const int r = c * S::kKRowsPerChunk + lane / S::kKPos, p = lane % S::kKPos;
+    off[i] = uint32_t(r * D + ((p ^ (r & (S::kKPos - 1))) * 8)) * 2u;
+  }
+  const uint16_t* k_head = k_t + head_base * tile_elems;
+  const int32_t k_bytes = g.nT_max * S::kTileElems * 2;
+  lds_u16* const lbuf = (lds_u16*)&kbuf[0][0];
+  auto copy_tile = [&](int32_t jt, int buf) {
+#pragma unroll
+    for (int i = 0; i < TS::kChunksPerWave; ++i)
+      dma_copy(k_head, k_bytes, off[i], uint32_t(jt) * uint32_t(S::kTileElems * 2),
+               lbuf + buf * S::kTileElems + (wave * TS::kChunksPerWave + i) * 512);
+  };
+
+  copy_tile(0, 0);
+  if (nT > 1) copy_tile(1, 1);
+  __builtin_amdgcn_s_waitcnt(0);  // Q, the LSE and the first copies have landed
+  __syncthreads();
+
+  const floatx16 zero = {};
+  int buf = 0;  // j % 3
+  for (int32_t j = 0; j < nT; ++j) {
+    // K of tile j+2 into the buffer of tile j-1 (read in the previous iteration).
+    if (j + 2 < nT) copy_tile(j + 2, buf == 0 ? 2 : buf - 1);
+    const uint16_t* ks = &kbuf[buf][0];
+    floatx16 sacc[2];
+#pragma unroll
+    for (int t = 0; t < 2 * S::kDC; ++t) {
+      const int kb = t / S::kDC, dc = t % S::kDC;
+      const u32x4 kf = k_frag<D>(ks, t, half, h, l32);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[dc]),
+                                                         dc == 0 ? zero : sacc[kb], 0, 0, 0);
+    }
+    // Pad keys of a border tile never raise the maximum.
+    const uint64_t wm = real_key_bits(g, hg, j, half, h);
+    if (wm != ~0ull) {
+      const uint32_t wlo = uint32_t(wm), whi = uint32_t(wm >> 32);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int bit = 16 * (v / 8) + 4 * ((v / 4) % 2) + (v % 4);
+          const uint32_t real = ((kb ? whi : wlo) >> bit) & 1u;
+          sacc[kb][v] += __uint_as_float((real - 1u) & 0xFF800000u);
+        }
+    }
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
+    // scale*log2(e)*s - log2(e)*lse is increasing in s, so the lane's maximum
+    // logit gives its maximum probability.
+    const float x = wave_max(__builtin_fmaf(mx, scale_log2, -lse2));
+    if (lane == 0) red[j & 1][wave] = x;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copy of tile j+2 has landed
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float m = red[j & 1][0];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[j & 1][w]);
+      trow[j] = __builtin_amdgcn_exp2f(m);
+    }
+    buf = buf == 2 ? 0 : buf + 1;
+  }
+}
+
+// Common set bits of two tile masks, per (batch, head): the sum over the
+// head's query tiles of popcount(a & b) over their words.
+__global__ __launch_bounds__(256) void mask_overlap_kernel(GeoTable g, const uint32_t* __restrict__ a,
+                                                           const uint32_t* __restrict__ bmask,
+                                                           unsigned long long* __restrict__ counts) {
+  const int hd = blockIdx.x, b = blockIdx.y;
+  const int32_t nT = g.h[hd].nT;
+  const int words = (g.nT_max + 31) / 32;
+  const int64_t base = (int64_t(b) * g.heads + hd) * g.nT_max * words;
+  unsigned long long c = 0;
+  for (int64_t e = threadIdx.x; e < int64_t(nT) * words; e += 256) c += __popc(a[base + e] & bmask[base + e]);
+  __shared__ unsigned long long part[256];
+  part[threadIdx.x] = c;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (int(threadIdx.x) < s) part[threadIdx.x] += part[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) counts[int64_t(b) * g.heads + hd] = part[0];
+}
+
+}  // namespace
+
+hipError_t launch_teacher(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t, const float* lse, float scale,
+                          float* teacher, hipStream_t s) {
+  const dim3 grid(g.nT_max, g.heads, g.B);
+  const float scale_log2 = scale * 1.44269504088896340736f;
+  if (g.d == 128)
+    teacher_kernel<128><<<grid, kThreads, 0, s>>>(g, q_t, k_t, lse, scale_log2, teacher);
+  else
+    teacher_kernel<64><<<grid, kThreads, 0, s>>>(g, q_t, k_t, lse, scale_log2, teacher);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_overlap(const GeoTable& g, const uint32_t* a, const uint32_t* b, unsigned long long* counts,
+                               hipStream_t s) {
+  mask_overlap_kernel<<<dim3(g.heads, g.B), 256, 0, s>>>(g, a, b, counts);
+  return hipGetLastError();
+}
+
+}  // namespace veda

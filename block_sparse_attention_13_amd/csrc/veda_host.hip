@@ -213,4 +213,30 @@ int veda_sparse_attn_fwd(const veda_geom* g, const void* q_tiled, const void* k_
       static_cast<hipStream_t>(stream)));
 }
 
+int veda_teacher_tile_max(const veda_geom* g, const void* q_tiled, const void* k_tiled, const float* lse_dense,
+                          float softmax_scale, float* teacher, void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!q_tiled || !k_tiled || !lse_dense || !teacher) return VEDA_ERR_NULL;
+  for (const void* p : {q_tiled, k_tiled, static_cast<const void*>(lse_dense), static_cast<const void*>(teacher)})
+    if (!aligned16(p)) return VEDA_ERR_ALIGN;
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) softmax_scale = 1.0f / std::sqrt(float(t.d));
+  VEDA_TRY(check_device());
+  return launched(veda::launch_teacher(t, static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_tiled),
+                                       lse_dense, softmax_scale, teacher, static_cast<hipStream_t>(stream)));
+}
+
+int veda_mask_overlap(const veda_geom* g, const uint32_t* bitmask_a, const uint32_t* bitmask_b, uint64_t* counts,
+                      void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!bitmask_a || !bitmask_b || !counts) return VEDA_ERR_NULL;
+  for (const void* p : {static_cast<const void*>(bitmask_a), static_cast<const void*>(bitmask_b),
+                        static_cast<const void*>(counts)})
+    if (!aligned16(p)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_device());
+  return launched(veda::launch_mask_overlap(t, bitmask_a, bitmask_b, reinterpret_cast<unsigned long long*>(counts),
+                                            static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -106,6 +106,10 @@ hipError_t launch_tile_scores(const GeoTable& g, const uint16_t* feat_q, const u
                               float* scores, hipStream_t s);
 hipError_t launch_topk(const GeoTable& g, const float* scores, int32_t k_max, int32_t* idx, uint32_t* bitmask,
                        hipStream_t s);
+hipError_t launch_teacher(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t, const float* lse, float scale,
+                          float* teacher, hipStream_t s);
+hipError_t launch_mask_overlap(const GeoTable& g, const uint32_t* a, const uint32_t* b, unsigned long long* counts,
+                               hipStream_t s);
 hipError_t launch_sparse_attn(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t, const uint16_t* v_t,
                               const int32_t* idx, int32_t k_max, float scale, uint16_t* o_t, float* lse,
                               hipStream_t s);

@@ -11,6 +11,11 @@
  *   veda_sparse_attn_fwd       flash-attention forward over the selected K/V tiles only
  *   veda_tile_unpermute        tiled O -> raster O
  *
+ * Two more calls measure the mask against the method's own target:
+ *   veda_teacher_tile_max      max-pooled dense attention per (query tile, key tile); its
+ *                              veda_topk_mask is the oracle tile mask
+ *   veda_mask_overlap          common kept tiles of two masks (tile recall)
+ *
  * Conventions shared by every call
  * --------------------------------
  * Tensors are DEVICE pointers allocated and owned by the caller; the library
@@ -187,6 +192,32 @@ int veda_sparse_attn_fwd(const veda_geom* g, const void* q_tiled, const void* k_
  */
 int veda_tile_unpermute(const veda_geom* g, const void* x_tiled, void* x_raster,
                         veda_raster_strides s, void* stream);
+
+/*
+ * Tile-level teacher (Veda page, "Attention Structure Distillation", Teacher: max-pooled full
+ * attention as tile-level supervision; Principle 01; "Empirical Study" 02: the oracle mask keeps the
+ * highest-response key tiles of each query tile):
+ *   T[b, hd, tq, j] = max over real queries i of tile tq and real keys m of tile j of
+ *                     exp(scale * q_i . k_m - lse_i),
+ * the largest dense softmax probability between the two tiles (bf16 MFMA products, fp32 accumulation).
+ *   q_tiled, k_tiled  in   tiled bf16, token-major [B, heads, nT_max, 128, d]
+ *   lse_dense         in   fp32 [B, heads, nT_max, 128]: the lse output of veda_sparse_attn_fwd run with
+ *                          every key tile kept (k_hd = nT_hd, idx[..., j] = j), same softmax_scale
+ *   softmax_scale     in   <= 0 selects 1/sqrt(d)
+ *   teacher           out  fp32 [B, heads, nT_max, nT_max], values in (0, 1]; -inf outside the head's
+ *                          nT_hd x nT_hd block. veda_topk_mask(teacher) gives the oracle tile mask.
+ */
+int veda_teacher_tile_max(const veda_geom* g, const void* q_tiled, const void* k_tiled, const float* lse_dense,
+                          float softmax_scale, float* teacher, void* stream);
+
+/*
+ * Overlap of two tile masks (tile recall of a mask against an oracle mask is
+ * counts / (k_hd * nT_hd)).
+ *   bitmask_a, bitmask_b  in   uint32 [B, heads, nT_max, ceil(nT_max/32)] from veda_topk_mask
+ *   counts                out  uint64 [B, heads]: sum over the head's query tiles of popcount(a & b)
+ */
+int veda_mask_overlap(const veda_geom* g, const uint32_t* bitmask_a, const uint32_t* bitmask_b, uint64_t* counts,
+                      void* stream);
 
 #ifdef __cplusplus
 }

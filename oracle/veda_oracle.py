@@ -292,6 +292,61 @@ def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float
 
 
 # --------------------------------------------------------------------------
+# Teacher, oracle mask and tile recall ([Veda] "Attention Structure
+# Distillation", Teacher: max-pooling the full attention map gives tile-level
+# supervision; Principle 01 "Full-Attention Structure Distillation";
+# "Empirical Study" 02: the oracle mask keeps each query tile's
+# highest-response key tiles, and tile recall measures how many of them a
+# mask keeps)
+# --------------------------------------------------------------------------
+
+def teacher_tile_max(q: np.ndarray, k: np.ndarray, grid: Grid, tile: Tile, scale: float,
+                     query_tiles: Sequence[int] = None) -> np.ndarray:
+    """Max-pooled full attention: T[i, j] is the largest dense softmax
+    probability between a real query of tile i and a real key of tile j.
+
+    q, k: [N, d] raster order. Each query's softmax runs over all N real
+    keys (no mask), in float64. Rows of tiles not in `query_tiles` (default:
+    all) are NaN. Reading: the pooling window is one (query tile, key tile)
+    block of the attention map, and pad slots take no part.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    vol = tile[0] * tile[1] * tile[2]
+    tile_of = tiled_position(grid, tile) // vol
+    nT = num_tiles(grid, tile)
+    T = np.full((nT, nT), np.nan)
+    tiles = range(nT) if query_tiles is None else query_tiles
+    for i in tiles:
+        qi = np.flatnonzero(tile_of == i)
+        u = (q[qi] @ k.T) * scale
+        m = u.max(axis=1, keepdims=True)
+        p = np.exp(u - m)
+        p /= p.sum(axis=1, keepdims=True)
+        best = p.max(axis=0)                       # per key: its largest probability over the tile's queries
+        for j in range(nT):
+            T[i, j] = best[tile_of == j].max()
+    return T
+
+
+def mask_overlap(bitmask_a: np.ndarray, bitmask_b: np.ndarray) -> int:
+    """Number of (query tile, key tile) pairs kept by both masks."""
+    both = np.asarray(bitmask_a, dtype=np.uint32) & np.asarray(bitmask_b, dtype=np.uint32)
+    return int(np.unpackbits(both.view(np.uint8)).sum())
+
+
+def tile_recall(idx_mask: np.ndarray, idx_oracle: np.ndarray) -> float:
+    """Share of the oracle mask's kept tiles that the mask also keeps
+    (index lists [nT, k]; entries < 0 ignored)."""
+    hit = total = 0
+    for row_m, row_o in zip(idx_mask, idx_oracle):
+        o = set(int(x) for x in row_o if x >= 0)
+        hit += len(o & set(int(x) for x in row_m if x >= 0))
+        total += len(o)
+    return hit / total
+
+
+# --------------------------------------------------------------------------
 # The whole layer, one head at a time
 # --------------------------------------------------------------------------
 

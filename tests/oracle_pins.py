@@ -357,6 +357,65 @@ def check_attention_monotone_and_bounded(O, seed=8):
             assert np.all(o[n] <= rows.max(axis=0) + 1e-12) and np.all(o[n] >= rows.min(axis=0) - 1e-12)
 
 
+# ------------------------------------------------------- teacher and recall
+
+def check_teacher_matches_pooled_softmax(O, seed=9):
+    """Teacher = block max-pooling of the full softmax map: build the dense
+    probability matrix with torch.softmax (float64, CPU), lay it out in tiled
+    order with the brute-force positions (pad rows and columns -inf), and
+    max-pool each (query tile, key tile) block with amax; compare."""
+    import torch
+    rng = np.random.default_rng(seed)
+    grid, tile, d = (2, 3, 8), (1, 2, 4), 16            # padded: 8 boxes of 8 slots, 48 tokens
+    N, vol = 48, 8
+    q, k = (_bf16_vals(rng, (N, d), 2.0) for _ in range(2))
+    scale = 0.7
+    P = torch.softmax(torch.from_numpy(q.astype(np.float64)) @ torch.from_numpy(k.astype(np.float64)).T * scale,
+                      dim=-1)
+    pos, total = brute_force_positions(grid, tile)
+    nT = total // vol
+    Pt = torch.full((total, total), -math.inf, dtype=torch.float64)
+    idx = torch.from_numpy(pos)
+    Pt[idx[:, None], idx[None, :]] = P
+    want = Pt.reshape(nT, vol, nT, vol).amax(dim=(1, 3)).numpy()
+    got = O.teacher_tile_max(q, k, grid, tile, scale)
+    assert got.shape == (nT, nT)
+    assert np.max(np.abs(got - want)) < 1e-14
+    sub = O.teacher_tile_max(q, k, grid, tile, scale, query_tiles=[3])
+    assert np.array_equal(sub[3], got[3]) and np.all(np.isnan(np.delete(sub, 3, axis=0)))
+
+
+def check_teacher_uniform_keys(O):
+    """Identical keys give every query the uniform distribution 1/N, so every
+    block maximum is exactly 1/N; a key that dominates every query's logits
+    gives probability ~1 in its tile's column and ~0 elsewhere."""
+    grid, tile, d = (2, 4, 4), (1, 4, 4), 4              # 2 full boxes of 16 slots, 32 tokens
+    N = 32
+    q = np.linspace(-1, 1, N * d).reshape(N, d).astype(np.float32)
+    k = np.tile(np.array([[0.5, -0.25, 1.0, 2.0]], np.float32), (N, 1))
+    T = O.teacher_tile_max(q, k, grid, tile, 1.0)
+    assert np.allclose(T, 1.0 / N, rtol=1e-13, atol=0)
+    k2 = np.zeros((N, d), np.float32)
+    k2[5] = 40.0                                         # raster token 5 = (t 0, y 1, x 1): box 0
+    q2 = np.ones((N, d), np.float32)
+    T2 = O.teacher_tile_max(q2, k2, grid, tile, 1.0)
+    # logits: 160 for token 5, 0 for the 31 others: p = 1 / (1 + 31 e^-160) and e^-160 / (1 + 31 e^-160)
+    assert np.all(T2[:, 0] == 1.0)
+    assert np.allclose(T2[:, 1], math.exp(-160.0) / (1 + 31 * math.exp(-160.0)), rtol=1e-12, atol=0)
+
+
+def check_recall_golden(O):
+    """Tile recall and mask overlap on hand-made masks: query tile 0 keeps
+    {0, 1} against an oracle {1, 2}; tile 1 keeps {2, 3} against {2, 3}: 3 of
+    the oracle's 4 kept tiles, so recall 3/4 and overlap 3."""
+    m = np.array([[0, 1], [2, 3]])
+    o = np.array([[1, 2], [2, 3]])
+    assert O.tile_recall(m, o) == 0.75
+    assert O.tile_recall(o, o) == 1.0
+    assert O.mask_overlap(O.bitmask(m, 4), O.bitmask(o, 4)) == 3
+    assert O.mask_overlap(O.bitmask(m, 40), O.bitmask(np.array([[2, 3], [0, 1]]), 40)) == 0
+
+
 ALL_SMALL_CHECKS = [
     check_permutation_golden,
     lambda O: check_permutation_bruteforce(O, [((2, 3, 4), (1, 2, 2)), ((4, 16, 16), (2, 8, 8)),
@@ -376,4 +435,7 @@ ALL_SMALL_CHECKS = [
     check_attention_renormalisation,
     check_attention_zero_query,
     check_attention_monotone_and_bounded,
+    check_teacher_matches_pooled_softmax,
+    check_teacher_uniform_keys,
+    check_recall_golden,
 ]

@@ -21,7 +21,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     from block_sparse_attention_13_amd import _lib
     declared = _declared_functions()
-    assert len(declared) == 8, declared
+    assert len(declared) == 10, declared
     assert sorted(_lib.EXPORTS) == declared
     for name in declared:
         assert hasattr(_lib.lib, name), name
@@ -101,6 +101,11 @@ def test_call_errors_precede_any_device_work():
     assert L.veda_sparse_attn_fwd(g.c, FAKE, FAKE, FAKE, FAKE, _lib.int_array([9]), 8, 0.0, FAKE, None, None) == -4
     assert L.veda_sparse_attn_fwd(g.c, FAKE, None, FAKE, FAKE, ks, 4, 0.0, FAKE, None, None) == -1
     assert L.veda_sparse_attn_fwd(g.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE, FAKE + 4, None) == -5
+    assert L.veda_teacher_tile_max(g.c, FAKE, FAKE, None, 0.0, FAKE, None) == -1
+    assert L.veda_teacher_tile_max(g.c, FAKE, FAKE, FAKE, 0.0, FAKE + 4, None) == -5
+    assert L.veda_teacher_tile_max(_geom(tiles=((2, 2, 2),)).c, FAKE, FAKE, FAKE, 0.0, FAKE, None) == -3
+    assert L.veda_mask_overlap(g.c, FAKE, None, FAKE, None) == -1
+    assert L.veda_mask_overlap(g.c, FAKE, FAKE, FAKE + 8, None) == -5
 
 
 def test_valid_call_without_gpu_reports_device_error():

@@ -1,0 +1,116 @@
+"""Teacher (max-pooled dense attention), oracle tile mask and tile recall:
+HIP path vs the CPU oracle on the same seeded host bytes.
+
+Tolerance of the teacher: T = exp(scale q.k - lse) with lse from the dense
+pass of the attention kernel, whose LSE is within 2e-3 of the exact value;
+the logits themselves are exact bf16 products summed in fp32. So
+|log T_gpu - log T_ref| <= 5e-3 wherever T_ref is a normal fp32 number.
+The oracle mask is Top-k of T: the GPU mask must be exactly Top-k of the GPU
+teacher (same select, pinned elsewhere), and may differ from Top-k of the
+oracle's teacher only at near-ties, i.e. between entries whose oracle
+values lie within that tolerance of the row's k-th value. The overlap
+counts are integers and are compared bit for bit."""
+
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle as O
+from gpu_harness import bits_of, geometry, say, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+W = datagen.WORKLOADS
+LOG_TOL = 5e-3
+
+
+def _lib():
+    import block_sparse_attention_13_amd as V
+    return V
+
+
+def _sample(nT, count, seed):
+    if count is None or count >= nT:
+        return list(range(nT))
+    rng = np.random.default_rng(seed)
+    return sorted(set([0, nT - 1] + rng.choice(nT, size=count, replace=False).tolist()))
+
+
+@pytest.mark.parametrize("wname,heads,qtiles", [("tiny", None, None), ("480p", 2, 10), ("hc", 3, 6)])
+def test_teacher_oracle_mask_and_recall(wname, heads, qtiles):
+    V = _lib()
+    w = W[wname] if heads is None else W[wname].with_heads(heads)
+    say(f"[teacher] workload {w.name} heads {w.heads}")
+    data = datagen.generate(w)
+    geom = geometry(w)
+    ks = w.k_per_head()
+    q, k, v = (to_dev_bf16(data[n]) for n in ("q", "k", "v"))
+    out = V.layer_forward(q, k, v, to_dev_bf16(data["wq"]), to_dev_bf16(data["wk"]), geom, ks)
+    idx_d, ks_d = V.dense_index(geom, q.device)
+    _, lse_d = V.sparse_attn_fwd(out["q_t"], out["k_t"], out["v_t"], idx_d, geom, ks_d)
+    T = V.teacher_tile_max(out["q_t"], out["k_t"], lse_d, geom)
+    o_idx, o_bm = V.topk_mask(T, geom, ks)
+    counts = V.mask_overlap(out["bitmask"], o_bm, geom)
+    torch.cuda.synchronize()
+    nT_max = geom.max_tiles()
+    scale = 1.0 / math.sqrt(w.d)
+    Tc = T.cpu().numpy()
+    trip_bm, orc_bm = bits_of(out["bitmask"]), bits_of(o_bm)
+    counts_c = counts.cpu().numpy().astype(np.uint64)
+    for hd in range(w.heads):
+        nT = geom.num_tiles(hd)
+        Th = Tc[0, hd]
+        assert np.all(np.isneginf(Th[:nT, nT:])) and np.all(np.isneginf(Th[nT:])), ("teacher pad", hd)
+        assert np.all((Th[:nT, :nT] > 0) & (Th[:nT, :nT] <= 1.0)), ("teacher range", hd)
+        # overlap counts, bit for bit, over the GPU's own masks
+        want = O.mask_overlap(trip_bm[0, hd, :nT], orc_bm[0, hd, :nT])
+        assert int(counts_c[0, hd]) == want, ("overlap", hd, int(counts_c[0, hd]), want)
+        # the oracle mask is exactly Top-k of the GPU teacher
+        kk = ks[hd]
+        gidx = o_idx[0, hd].cpu().numpy()
+        assert np.array_equal(gidx[:nT, :kk], O.topk(Th[:nT, :nT].astype(np.float32), kk)), ("topk of teacher", hd)
+        # teacher against the oracle on sampled query tiles
+        tiles = _sample(nT, qtiles, hd)
+        qh, kh_ = (O.bf16_bits_to_float(data[n][0, :, hd, :]) for n in ("q", "k"))
+        Tr = O.teacher_tile_max(qh, kh_, w.grid, w.head_tiles()[hd], scale, query_tiles=tiles)
+        worst = 0.0
+        ties = 0
+        for t in tiles:
+            ref, got = Tr[t], Th[t, :nT].astype(np.float64)
+            ok = ref > 1e-37
+            err = np.abs(np.log(got[ok]) - np.log(ref[ok]))
+            worst = max(worst, float(err.max()))
+            assert err.max() <= LOG_TOL, (hd, t, float(err.max()))
+            sel_g = set(gidx[t, :kk].tolist())
+            sel_r = set(np.sort(np.argsort(-ref, kind="stable")[:kk]).tolist())
+            kth = np.sort(ref)[::-1][kk - 1]
+            for j in sel_g ^ sel_r:
+                assert abs(math.log(ref[j]) - math.log(kth)) <= 2 * LOG_TOL, ("mask not a near-tie", hd, t, j)
+                ties += 1
+        recall = int(counts_c[0, hd]) / (kk * nT)
+        say(f"[teacher] {w.name} head {hd}: log-error {worst:.2e}, near-tie swaps {ties}, "
+            f"TripPool tile recall {recall:.3f} (k/nT = {kk / nT:.3f})")
+
+
+def test_mask_overlap_counts_random_bits():
+    """Overlap kernel on random words (bits beyond nT included): per
+    (batch, head), the popcount of a & b over the head's query-tile rows."""
+    V = _lib()
+    w = dataclasses.replace(W["hc"].with_heads(3), B=2)
+    geom = geometry(w)
+    nT = geom.max_tiles()
+    words = (nT + 31) // 32
+    rng = np.random.default_rng(5)
+    a = rng.integers(0, 1 << 32, size=(w.B, w.heads, nT, words), dtype=np.uint64).astype(np.uint32)
+    b = rng.integers(0, 1 << 32, size=(w.B, w.heads, nT, words), dtype=np.uint64).astype(np.uint32)
+    ta = torch.from_numpy(a.view(np.int32)).cuda().view(torch.uint32)
+    tb = torch.from_numpy(b.view(np.int32)).cuda().view(torch.uint32)
+    got = V.mask_overlap(ta, tb, geom).cpu().numpy().astype(np.uint64)
+    for bb in range(w.B):
+        for hd in range(w.heads):
+            n = geom.num_tiles(hd)
+            assert int(got[bb, hd]) == O.mask_overlap(a[bb, hd, :n], b[bb, hd, :n]), (bb, hd)

@@ -57,6 +57,15 @@ MUTANTS = {
          "keys = np.concatenate([members[j] for j in sel[(i + 1) % len(sel)] if j >= 0])"),
     "output not normalised":
         ("o[qi] = (e @ v[keys]) / z", "o[qi] = (e @ v[keys]) / z.max()"),
+    "teacher averages the block instead of its maximum":
+        ("T[i, j] = best[tile_of == j].max()", "T[i, j] = best[tile_of == j].mean()"),
+    "teacher skips the softmax normalisation":
+        ("p /= p.sum(axis=1, keepdims=True)", "p = p"),
+    "teacher pools over query tiles by the key's tile":
+        ("qi = np.flatnonzero(tile_of == i)", "qi = np.flatnonzero(tile_of == (i + 1) % nT)"),
+    "mask overlap counts either mask":
+        ("both = np.asarray(bitmask_a, dtype=np.uint32) & np.asarray(bitmask_b, dtype=np.uint32)",
+         "both = np.asarray(bitmask_a, dtype=np.uint32) | np.asarray(bitmask_b, dtype=np.uint32)"),
 }
 
 
