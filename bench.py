@@ -308,6 +308,39 @@ def dense_reference(V, w, data, trip_bitmask=None, steps=2, warmup=1):
     return res
 
 
+def tile_search_report(V, datagen, name="720p"):
+    """Head-aware tile search on one workload's inputs (synthetic stand-in
+    for calibration samples): every candidate tile shape through the whole
+    layer, per-head squared error against dense attention, per-head argmin.
+    Reports the wall time of the search and how much the chosen shapes
+    lower the error against the static (4,4,8) tiling."""
+    import collections
+    import numpy as np
+    import torch
+    w = datagen.WORKLOADS[name]
+    data = datagen.generate(w)
+    dev = torch.device("cuda:0")
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(dev)
+    q, k, v, wq, wk = (to(data[n]) for n in ("q", "k", "v", "wq", "wk"))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    res = V.tile_search(q, k, v, wq, wk, w.grid, w.keep)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    cands = res["candidates"]
+    err = res["err"].sum(axis=1)                       # [n_candidates, heads]
+    static = cands.index((4, 4, 8))
+    ratio = err.min(axis=0) / err[static]
+    hist = collections.Counter("x".join(map(str, b)) for b in res["best"])
+    del q, k, v, wq, wk, res
+    torch.cuda.empty_cache()
+    return {"workload": w.description, "candidates": len(cands), "wall_s": round(wall, 3),
+            "best_tile_histogram": dict(hist.most_common()),
+            "error_vs_static_448_mean": round(float(ratio.mean()), 4),
+            "error_vs_static_448_min": round(float(ratio.min()), 4),
+            "note": "random-init TripPool projections; synthetic inputs stand in for calibration samples"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -317,6 +350,7 @@ def main():
     ap.add_argument("--heads", type=int, default=0, help="run only the first N heads (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense (every tile kept) reference")
+    ap.add_argument("--no-tile-search", action="store_true", help="skip the head-aware tile search report")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="time only the main workload (skip tiny, 480p, 720p, hc)")
     ap.add_argument("--cpu-sample-tiles", type=int, default=1920)
@@ -377,6 +411,12 @@ def main():
             log(f"[bench] {name}: {per_config[name]['ms_per_layer']} ms/layer, attention "
                 f"{per_config[name]['attn_tflops']} TFLOP/s")
 
+    search = None
+    if not args.no_tile_search and not args.heads:
+        log("[bench] head-aware tile search on the 720p workload")
+        search = tile_search_report(V, datagen)
+        log(f"[bench] tile search: {search}")
+
     dense = None
     if not args.no_dense and not args.heads:
         log("[bench] dense reference: every key tile kept, same kernel")
@@ -417,6 +457,7 @@ def main():
         "cpu_baseline": cpu,
         "per_config": per_config,
         "dense_reference": dense,
+        "tile_search": search,
     }
     print(json.dumps(line), flush=True)
 

@@ -19,11 +19,17 @@ Measuring a mask against the method's own target:
                    oracle tile mask
   mask_overlap     kept tiles two masks have in common, per (batch, head)
   tile_recall      overlap / (k_hd * nT_hd)
+
+Head-aware tile search:
+  head_sq_error    per-head squared difference of two raster tensors
+  candidate_tiles  tile shapes (power-of-two edges, product 128) that fit a grid
+  tile_search      per head, the candidate tiling whose sparse output is closest to dense attention
 """
 
 from __future__ import annotations
 
 import dataclasses
+import fractions
 import math
 from typing import Dict, List, Optional, Sequence, Tuple
 
@@ -33,7 +39,8 @@ from . import _lib
 from ._lib import VedaError
 
 __all__ = ["Geometry", "VedaError", "tile_permute", "tile_unpermute", "trippool_score", "topk_mask",
-           "sparse_attn_fwd", "layer_forward", "dense_index", "teacher_tile_max", "mask_overlap", "tile_recall", "TILE_TOKENS", "TOKEN_MAJOR", "CHANNEL_MAJOR"]
+           "sparse_attn_fwd", "layer_forward", "dense_index", "teacher_tile_max", "mask_overlap", "tile_recall",
+           "head_sq_error", "candidate_tiles", "tile_search", "TILE_TOKENS", "TOKEN_MAJOR", "CHANNEL_MAJOR"]
 
 TILE_TOKENS = _lib.VEDA_TILE_TOKENS
 TOKEN_MAJOR = _lib.VEDA_TILED_TOKEN_MAJOR
@@ -304,3 +311,72 @@ def tile_recall(counts: torch.Tensor, geom: Geometry, k_per_head: Sequence[int])
     c = counts.cpu().tolist()
     return [[int(c[b][hd]) / (k_per_head[hd] * geom.num_tiles(hd)) for hd in range(geom.n_heads)]
             for b in range(geom.B)]
+
+
+def head_sq_error(a: torch.Tensor, b: torch.Tensor, geom: Geometry,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp64 [B, heads]: sum over tokens and channels of (a - b)^2 for two raster
+    bf16 tensors [B, N, heads, d] (any strides with unit channel stride)."""
+    sa = _raster_strides(a, geom, "a")
+    sb = _raster_strides(b, geom, "b")
+    if out is None:
+        out = torch.empty((geom.B, geom.n_heads), dtype=torch.float64, device=a.device)
+    _need(out, torch.float64, (geom.B, geom.n_heads), "err")
+    _lib.check(_lib.lib.veda_head_sq_error(geom.c, a.data_ptr(), sa, b.data_ptr(), sb, out.data_ptr(), _stream(a)),
+               "veda_head_sq_error")
+    return out
+
+
+def candidate_tiles(grid: Sequence[int]) -> List[Tuple[int, int, int]]:
+    """Every (pt, ph, pw) of powers of two with pt * ph * pw = 128 whose edges
+    do not exceed the grid's (T, H, W) and whose tile count stays within the
+    library's limit."""
+    T, H, W = grid
+    out = []
+    for a in range(8):
+        for b_ in range(8 - a):
+            pt, ph, pw = 1 << a, 1 << b_, 1 << (7 - a - b_)
+            if pt <= T and ph <= H and pw <= W:
+                n = -(-T // pt) * -(-H // ph) * -(-W // pw)
+                if n <= _lib.VEDA_MAX_TILES:
+                    out.append((pt, ph, pw))
+    return out
+
+
+def _k_of(keep, n: int) -> int:
+    f = keep if isinstance(keep, fractions.Fraction) else fractions.Fraction(str(keep))
+    return max(1, min(n, math.ceil(f * n)))
+
+
+def tile_search(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
+                grid: Sequence[int], keep, candidates: Optional[Sequence[Tuple[int, int, int]]] = None,
+                scale: Optional[float] = None) -> Dict[str, object]:
+    """Head-aware tile search on calibration inputs: for every candidate tile
+    shape, run the whole layer with that shape on every head (k_hd =
+    ceil(keep * nT_hd)) and measure each head's ||O_dense - O_sparse||_F^2
+    against dense attention; each head takes the candidate with the smallest
+    error summed over the batch.
+
+    Returns {"candidates", "err" (fp64 [n_candidates, B, heads], host),
+    "best" (one tile shape per head), "o_dense"}."""
+    B, N, Hh, d = q.shape
+    cands = list(candidates) if candidates is not None else candidate_tiles(grid)
+    if not cands:
+        raise ValueError("no candidate tile shape fits the grid")
+    g0 = Geometry(B, Hh, d, tuple(grid), [cands[0]] * Hh)
+    q_t = tile_permute(q, g0)
+    k_t = tile_permute(k, g0)
+    v_t = tile_permute(v, g0, layout=CHANNEL_MAJOR)
+    idx, ks_all = dense_index(g0, q.device)
+    o_t, _ = sparse_attn_fwd(q_t, k_t, v_t, idx, g0, ks_all, scale, with_lse=False)
+    o_dense = tile_unpermute(o_t, g0)
+    del q_t, k_t, v_t, idx, o_t
+    errs = []
+    for tile in cands:
+        g = Geometry(B, Hh, d, tuple(grid), [tuple(tile)] * Hh)
+        ks = [_k_of(keep, g.num_tiles(hd)) for hd in range(Hh)]
+        o = layer_forward(q, k, v, w_q, w_k, g, ks, scale)["o"]
+        errs.append(head_sq_error(o, o_dense, g).cpu())
+    err = torch.stack(errs).numpy()
+    best_i = err.sum(axis=1).argmin(axis=0)
+    return {"candidates": cands, "err": err, "best": [tuple(cands[i]) for i in best_i], "o_dense": o_dense}

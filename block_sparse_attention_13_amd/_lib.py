@@ -25,7 +25,7 @@ STATUS = {
 
 EXPORTS = ["veda_status_str", "veda_num_tiles", "veda_max_tiles", "veda_tile_permute", "veda_trippool_score",
            "veda_topk_mask", "veda_sparse_attn_fwd", "veda_tile_unpermute", "veda_teacher_tile_max",
-           "veda_mask_overlap"]
+           "veda_mask_overlap", "veda_head_sq_error"]
 
 
 class VedaGrid(ctypes.Structure):
@@ -53,7 +53,7 @@ class VedaError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m block_sparse_attention_13_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python block_sparse_attention_13_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     lib.veda_status_str.argtypes = [ctypes.c_int]
     lib.veda_status_str.restype = ctypes.c_char_p
@@ -78,6 +78,9 @@ def _load():
     lib.veda_teacher_tile_max.restype = ctypes.c_int
     lib.veda_mask_overlap.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_void_p]
     lib.veda_mask_overlap.restype = ctypes.c_int
+    lib.veda_head_sq_error.argtypes = [POINTER(VedaGeom), c_void_p, VedaRasterStrides, c_void_p, VedaRasterStrides,
+                                       c_void_p, c_void_p]
+    lib.veda_head_sq_error.restype = ctypes.c_int
     return lib
 
 

@@ -1,6 +1,7 @@
 """Build libveda.so (HIP kernels + C ABI) for gfx950, in-tree.
 
-Usage: python -m block_sparse_attention_13_amd.build   (or build() from Python)
+Usage: python block_sparse_attention_13_amd/build.py   (or build() from Python; importing the
+package first would load the library this rebuilds)
 """
 
 from __future__ import annotations
@@ -14,7 +15,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libveda.so")
-SOURCES = ["veda_host.hip", "permute.hip", "trippool.hip", "topk.hip", "sparse_attn.hip", "teacher.hip"]
+SOURCES = ["veda_host.hip", "permute.hip", "trippool.hip", "topk.hip", "sparse_attn.hip", "teacher.hip", "metrics.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [

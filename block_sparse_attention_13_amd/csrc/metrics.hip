@@ -1,0 +1,65 @@
+// Squared error between two raster tensors per (batch, head): the objective
+// of the head-aware tile search (Veda page, "Head-Aware Tile Search": each
+// head takes the tiling that minimises the squared Frobenius norm of the
+// difference between the full-attention output and the sparse output on
+// calibration samples).
+//
+// One workgroup per (batch, head) reads both [N, d] slices with 16-byte loads
+// and sums (a - b)^2 in fp64 per thread, then over the workgroup in a fixed
+// tree order, so the result is deterministic. HBM-bound; the library keeps no
+// scratch, so each head's sum stays inside one workgroup.
+#include "veda_internal.hpp"
+
+namespace veda {
+namespace {
+
+constexpr int kSqThreads = 1024;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__global__ __launch_bounds__(kSqThreads) void head_sq_error_kernel(GeoTable g, const uint16_t* __restrict__ a,
+                                                                  int64_t sab, int64_t san, int64_t sah,
+                                                                  const uint16_t* __restrict__ b, int64_t sbb,
+                                                                  int64_t sbn, int64_t sbh, double* __restrict__ err) {
+  const int hd = blockIdx.x, bb = blockIdx.y;
+  const int chunks = g.d / 8;                        // 16-byte pieces per token row
+  const int64_t N = int64_t(g.T) * g.H * g.W;
+  const int64_t total = N * chunks;
+  const uint16_t* pa = a + bb * sab + hd * sah;
+  const uint16_t* pb = b + bb * sbb + hd * sbh;
+  double acc = 0.0;
+  for (int64_t e = threadIdx.x; e < total; e += kSqThreads) {
+    const int64_t n = e / chunks;
+    const int c = int(e % chunks) * 8;
+    const uint4 va = *reinterpret_cast<const uint4*>(pa + n * san + c);
+    const uint4 vb = *reinterpret_cast<const uint4*>(pb + n * sbn + c);
+    const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double d0 = double(bf16_lo(wa[i])) - double(bf16_lo(wb[i]));
+      const double d1 = double(bf16_hi(wa[i])) - double(bf16_hi(wb[i]));
+      acc = __builtin_fma(d0, d0, acc);
+      acc = __builtin_fma(d1, d1, acc);
+    }
+  }
+  __shared__ double part[kSqThreads];
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = kSqThreads / 2; s > 0; s >>= 1) {
+    if (int(threadIdx.x) < s) part[threadIdx.x] += part[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) err[int64_t(bb) * g.heads + hd] = part[0];
+}
+
+}  // namespace
+
+hipError_t launch_head_sq_error(const GeoTable& g, const uint16_t* a, int64_t sab, int64_t san, int64_t sah,
+                                const uint16_t* b, int64_t sbb, int64_t sbn, int64_t sbh, double* err,
+                                hipStream_t s) {
+  head_sq_error_kernel<<<dim3(g.heads, g.B), kSqThreads, 0, s>>>(g, a, sab, san, sah, b, sbb, sbn, sbh, err);
+  return hipGetLastError();
+}
+
+}  // namespace veda

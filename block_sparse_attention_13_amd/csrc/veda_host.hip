@@ -239,4 +239,18 @@ int veda_mask_overlap(const veda_geom* g, const uint32_t* bitmask_a, const uint3
                                             static_cast<hipStream_t>(stream)));
 }
 
+int veda_head_sq_error(const veda_geom* g, const void* a_raster, veda_raster_strides sa, const void* b_raster,
+                       veda_raster_strides sb, double* err, void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!a_raster || !b_raster || !err) return VEDA_ERR_NULL;
+  if (!aligned16(a_raster) || !aligned16(b_raster) || !aligned16(err)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_strides(sa));
+  VEDA_TRY(check_strides(sb));
+  VEDA_TRY(check_device());
+  return launched(veda::launch_head_sq_error(t, static_cast<const uint16_t*>(a_raster), sa.b, sa.n, sa.h,
+                                             static_cast<const uint16_t*>(b_raster), sb.b, sb.n, sb.h, err,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

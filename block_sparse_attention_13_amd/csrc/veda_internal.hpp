@@ -110,6 +110,9 @@ hipError_t launch_teacher(const GeoTable& g, const uint16_t* q_t, const uint16_t
                           float* teacher, hipStream_t s);
 hipError_t launch_mask_overlap(const GeoTable& g, const uint32_t* a, const uint32_t* b, unsigned long long* counts,
                                hipStream_t s);
+hipError_t launch_head_sq_error(const GeoTable& g, const uint16_t* a, int64_t sab, int64_t san, int64_t sah,
+                                const uint16_t* b, int64_t sbb, int64_t sbn, int64_t sbh, double* err,
+                                hipStream_t s);
 hipError_t launch_sparse_attn(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t, const uint16_t* v_t,
                               const int32_t* idx, int32_t k_max, float scale, uint16_t* o_t, float* lse,
                               hipStream_t s);

@@ -15,6 +15,7 @@
  *   veda_teacher_tile_max      max-pooled dense attention per (query tile, key tile); its
  *                              veda_topk_mask is the oracle tile mask
  *   veda_mask_overlap          common kept tiles of two masks (tile recall)
+ *   veda_head_sq_error         squared output error per head (objective of the head-aware tile search)
  *
  * Conventions shared by every call
  * --------------------------------
@@ -218,6 +219,17 @@ int veda_teacher_tile_max(const veda_geom* g, const void* q_tiled, const void* k
  */
 int veda_mask_overlap(const veda_geom* g, const uint32_t* bitmask_a, const uint32_t* bitmask_b, uint64_t* counts,
                       void* stream);
+
+/*
+ * Squared error per (batch, head) between two raster tensors (Veda page, "Head-Aware Tile Search":
+ * each head takes the tiling that minimises ||O_full - O_sparse||_F^2 on calibration samples):
+ *   err[b, hd] = sum over tokens n and channels c of (a[b, n, hd, c] - b[b, n, hd, c])^2,
+ * summed in fp64 in a fixed order (deterministic).
+ *   a_raster, b_raster  in   raster bf16 tensors [B, N, heads, d], strides sa, sb (elements)
+ *   err                 out  fp64 [B, heads]
+ */
+int veda_head_sq_error(const veda_geom* g, const void* a_raster, veda_raster_strides sa, const void* b_raster,
+                       veda_raster_strides sb, double* err, void* stream);
 
 #ifdef __cplusplus
 }

@@ -347,6 +347,29 @@ def tile_recall(idx_mask: np.ndarray, idx_oracle: np.ndarray) -> float:
 
 
 # --------------------------------------------------------------------------
+# Head-aware tile search ([Veda] "Head-Aware Tile Search": candidate tile
+# shapes keep p_t*p_h*p_w = 128; each head takes the one that minimises the
+# squared Frobenius norm of O_full - O_sparse on calibration samples;
+# Principle 02 "Head-Conditioned Tile Geometry")
+# --------------------------------------------------------------------------
+
+def tile_search_errors(q: np.ndarray, k: np.ndarray, v: np.ndarray, wq: np.ndarray, wk: np.ndarray,
+                       grid: Grid, candidates: Sequence[Tile], k_of, scale: float = None) -> np.ndarray:
+    """||O_dense - O_sparse(tile)||_F^2 of one head for every candidate tile,
+    where O_sparse runs the whole layer (tiling, TripPool estimator, Top-k
+    with k = k_of(nT)) and O_dense is full softmax attention."""
+    d = q.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o_dense, _ = dense_attention(q, k, v, scale)
+    errs = []
+    for tile in candidates:
+        r = head_forward(q, k, v, wq, wk, grid, tile, k_of(num_tiles(grid, tile)), scale)
+        errs.append(float(((r["o"] - o_dense) ** 2).sum()))
+    return np.array(errs)
+
+
+# --------------------------------------------------------------------------
 # The whole layer, one head at a time
 # --------------------------------------------------------------------------
 

@@ -416,6 +416,40 @@ def check_recall_golden(O):
     assert O.mask_overlap(O.bitmask(m, 40), O.bitmask(np.array([[2, 3], [0, 1]]), 40)) == 0
 
 
+# --------------------------------------------------------------- tile search
+
+def check_tile_search_errors(O, seed=10):
+    """The search objective through an independent route: for one candidate,
+    keep the oracle's own tile lists but redo the attention as torch
+    scaled_dot_product_attention with a boolean token mask built from the
+    brute-force tiled positions, against unmasked SDPA, and sum the squared
+    difference. With every tile kept the error vanishes for every candidate."""
+    import torch
+    rng = np.random.default_rng(seed)
+    grid, d, r = (2, 4, 16), 16, 8                         # 128 tokens
+    N = 128
+    q, k, v = (_bf16_vals(rng, (N, d)) for _ in range(3))
+    wq, wk = (_bf16_vals(rng, (3 * d, r), 0.2) for _ in range(2))
+    cands = [(1, 4, 8), (2, 2, 8), (1, 1, 16)]             # volume 32 boxes: tile volume need not be 128 here
+    keep = lambda n: max(1, n // 2)
+    errs = O.tile_search_errors(q, k, v, wq, wk, grid, cands, keep)
+    t = lambda a: torch.from_numpy(a.astype(np.float64))[None, None]
+    dense = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v))[0, 0]
+    for ci, tile in enumerate(cands):
+        vol = tile[0] * tile[1] * tile[2]
+        res = O.head_forward(q, k, v, wq, wk, grid, tile, keep(O.num_tiles(grid, tile)))
+        pos, _ = brute_force_positions(grid, tile)
+        tile_of = pos // vol
+        allowed = np.zeros((N, N), bool)
+        for n in range(N):
+            allowed[n] = np.isin(tile_of, res["idx"][tile_of[n]])
+        o = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v),
+                                                             attn_mask=torch.from_numpy(allowed)[None, None])[0, 0]
+        want = float(((o - dense) ** 2).sum())
+        assert abs(errs[ci] - want) <= 1e-9 * max(want, 1e-30), (tile, errs[ci], want)
+    assert np.all(O.tile_search_errors(q, k, v, wq, wk, grid, cands, lambda n: n) < 1e-20)
+
+
 ALL_SMALL_CHECKS = [
     check_permutation_golden,
     lambda O: check_permutation_bruteforce(O, [((2, 3, 4), (1, 2, 2)), ((4, 16, 16), (2, 8, 8)),
@@ -438,4 +472,5 @@ ALL_SMALL_CHECKS = [
     check_teacher_matches_pooled_softmax,
     check_teacher_uniform_keys,
     check_recall_golden,
+    check_tile_search_errors,
 ]

@@ -21,7 +21,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     from block_sparse_attention_13_amd import _lib
     declared = _declared_functions()
-    assert len(declared) == 10, declared
+    assert len(declared) == 11, declared
     assert sorted(_lib.EXPORTS) == declared
     for name in declared:
         assert hasattr(_lib.lib, name), name
@@ -106,6 +106,8 @@ def test_call_errors_precede_any_device_work():
     assert L.veda_teacher_tile_max(_geom(tiles=((2, 2, 2),)).c, FAKE, FAKE, FAKE, 0.0, FAKE, None) == -3
     assert L.veda_mask_overlap(g.c, FAKE, None, FAKE, None) == -1
     assert L.veda_mask_overlap(g.c, FAKE, FAKE, FAKE + 8, None) == -5
+    assert L.veda_head_sq_error(g.c, FAKE, s, None, s, FAKE, None) == -1
+    assert L.veda_head_sq_error(g.c, FAKE, s, FAKE, _lib.VedaRasterStrides(1024, 130, 128), FAKE, None) == -5
 
 
 def test_valid_call_without_gpu_reports_device_error():

@@ -63,6 +63,8 @@ MUTANTS = {
         ("p /= p.sum(axis=1, keepdims=True)", "p = p"),
     "teacher pools over query tiles by the key's tile":
         ("qi = np.flatnonzero(tile_of == i)", "qi = np.flatnonzero(tile_of == (i + 1) % nT)"),
+    "tile search sums absolute differences":
+        ("errs.append(float(((r[\"o\"] - o_dense) ** 2).sum()))", "errs.append(float(np.abs(r[\"o\"] - o_dense).sum()))"),
     "mask overlap counts either mask":
         ("both = np.asarray(bitmask_a, dtype=np.uint32) & np.asarray(bitmask_b, dtype=np.uint32)",
          "both = np.asarray(bitmask_a, dtype=np.uint32) | np.asarray(bitmask_b, dtype=np.uint32)"),
