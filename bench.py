@@ -341,6 +341,55 @@ def tile_search_report(V, datagen, name="720p"):
             "note": "random-init TripPool projections; synthetic inputs stand in for calibration samples"}
 
 
+def distill_report(V, datagen, name="480p", steps=300, lr=3e-3):
+    """Distil the estimator's projections toward the teacher on one sample of
+    a workload (calibration stand-in) and report the loss, the time per
+    training step (estimator, KL and gradient, two Adam updates) and the
+    tile recall of the estimator's mask against the oracle mask, before and
+    after, on that sample and on a held-out sample of the same generator."""
+    import dataclasses
+    import numpy as np
+    import torch
+    dev = torch.device("cuda:0")
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(dev)
+
+    def prepare(w):
+        data = datagen.generate(w)
+        g = V.Geometry(w.B, w.heads, w.d, w.grid, w.head_tiles())
+        q, k, v, wq, wk = (to(data[n]) for n in ("q", "k", "v", "wq", "wk"))
+        out = V.layer_forward(q, k, v, wq, wk, g, w.k_per_head())
+        idx_d, ks_d = V.dense_index(g, dev)
+        _, lse = V.sparse_attn_fwd(out["q_t"], out["k_t"], out["v_t"], idx_d, g, ks_d)
+        teacher = V.teacher_tile_max(out["q_t"], out["k_t"], lse, g)
+        _, oracle_bm = V.topk_mask(teacher, g, w.k_per_head())
+        return g, out["q_t"], out["k_t"], teacher, oracle_bm, wq, wk
+
+    def recall(g, q_t, k_t, wq, wk, oracle_bm, ks):
+        est = V.trippool_score(q_t, k_t, wq, wk, g)
+        _, bm = V.topk_mask(est["scores"], g, ks)
+        return float(np.mean(V.tile_recall(V.mask_overlap(bm, oracle_bm, g), g, ks)))
+
+    w = datagen.WORKLOADS[name]
+    ks = w.k_per_head()
+    g, q_t, k_t, teacher, obm, wq, wk = prepare(w)
+    g2, q2, k2, _, obm2, _, _ = prepare(dataclasses.replace(w, seed=w.seed + 100))
+    before = (recall(g, q_t, k_t, wq, wk, obm, ks), recall(g2, q2, k2, wq, wk, obm2, ks))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    res = V.distill_train(q_t, k_t, teacher, wq, wk, g, steps, lr)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    after = (recall(g, q_t, k_t, res["w_q"], res["w_k"], obm, ks),
+             recall(g2, q2, k2, res["w_q"], res["w_k"], obm2, ks))
+    return {"workload": w.description, "steps": steps, "lr": lr, "ms_per_step": round(dt / steps * 1e3, 3),
+            "mean_kl_first": round(res["loss"][0], 4), "mean_kl_last": round(res["loss"][-1], 4),
+            "tile_recall_before": round(before[0], 4), "tile_recall_after": round(after[0], 4),
+            "heldout_tile_recall_before": round(before[1], 4), "heldout_tile_recall_after": round(after[1], 4),
+            "chance_k_over_nT": round(float(np.mean([k / g.num_tiles(h) for h, k in enumerate(ks)])), 4),
+            "note": "synthetic sample of the 480p generator as calibration data; held-out = same generator, "
+                    "other seed"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -351,6 +400,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense (every tile kept) reference")
     ap.add_argument("--no-tile-search", action="store_true", help="skip the head-aware tile search report")
+    ap.add_argument("--no-distill", action="store_true", help="skip the estimator distillation report")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="time only the main workload (skip tiny, 480p, 720p, hc)")
     ap.add_argument("--cpu-sample-tiles", type=int, default=1920)
@@ -417,6 +467,12 @@ def main():
         search = tile_search_report(V, datagen)
         log(f"[bench] tile search: {search}")
 
+    distill = None
+    if not args.no_distill and not args.heads:
+        log("[bench] distilling the estimator on the 480p workload")
+        distill = distill_report(V, datagen)
+        log(f"[bench] distillation: {distill}")
+
     dense = None
     if not args.no_dense and not args.heads:
         log("[bench] dense reference: every key tile kept, same kernel")
@@ -458,6 +514,7 @@ def main():
         "per_config": per_config,
         "dense_reference": dense,
         "tile_search": search,
+        "distillation": distill,
     }
     print(json.dumps(line), flush=True)
 

@@ -24,6 +24,12 @@ Head-aware tile search:
   head_sq_error    per-head squared difference of two raster tensors
   candidate_tiles  tile shapes (power-of-two edges, product 128) that fit a grid
   tile_search      per head, the candidate tiling whose sparse output is closest to dense attention
+
+Distilling the estimator toward the teacher:
+  distill_kl       KL(teacher row || softmax(scores)) per query tile, and d/d scores
+  distill_grad     the gradient back to W_q, W_k
+  adam_step        one Adam update of fp32 master weights and their bf16 copy
+  distill_train    estimator -> KL -> gradient -> Adam, for a number of steps
 """
 
 from __future__ import annotations
@@ -40,7 +46,8 @@ from ._lib import VedaError
 
 __all__ = ["Geometry", "VedaError", "tile_permute", "tile_unpermute", "trippool_score", "topk_mask",
            "sparse_attn_fwd", "layer_forward", "dense_index", "teacher_tile_max", "mask_overlap", "tile_recall",
-           "head_sq_error", "candidate_tiles", "tile_search", "TILE_TOKENS", "TOKEN_MAJOR", "CHANNEL_MAJOR"]
+           "head_sq_error", "candidate_tiles", "tile_search", "distill_kl", "distill_grad", "adam_step",
+           "distill_train", "TILE_TOKENS", "TOKEN_MAJOR", "CHANNEL_MAJOR"]
 
 TILE_TOKENS = _lib.VEDA_TILE_TOKENS
 TOKEN_MAJOR = _lib.VEDA_TILED_TOKEN_MAJOR
@@ -380,3 +387,91 @@ def tile_search(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.Te
     err = torch.stack(errs).numpy()
     best_i = err.sum(axis=1).argmin(axis=0)
     return {"candidates": cands, "err": err, "best": [tuple(cands[i]) for i in best_i], "o_dense": o_dense}
+
+
+def distill_kl(scores: torch.Tensor, teacher: torch.Tensor, geom: Geometry, grad_scale: float = 1.0,
+               kl_rows: Optional[torch.Tensor] = None, d_scores: Optional[torch.Tensor] = None
+               ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per query tile: KL(teacher row normalised || softmax(scores row)) over
+    the head's key tiles ([B, heads, nT_max] fp32) and grad_scale times its
+    gradient with respect to the scores ([B, heads, nT_max, nT_max])."""
+    nT = geom.max_tiles()
+    shape = (geom.B, geom.n_heads, nT, nT)
+    _need(scores, torch.float32, shape, "scores")
+    _need(teacher, torch.float32, shape, "teacher")
+    if kl_rows is None:
+        kl_rows = torch.empty(shape[:3], dtype=torch.float32, device=scores.device)
+    if d_scores is None:
+        d_scores = torch.empty(shape, dtype=torch.float32, device=scores.device)
+    _need(kl_rows, torch.float32, shape[:3], "kl_rows")
+    _need(d_scores, torch.float32, shape, "d_scores")
+    _lib.check(_lib.lib.veda_distill_kl(geom.c, scores.data_ptr(), teacher.data_ptr(), float(grad_scale),
+                                        kl_rows.data_ptr(), d_scores.data_ptr(), _stream(scores)), "veda_distill_kl")
+    return kl_rows, d_scores
+
+
+def distill_grad(est: Dict[str, torch.Tensor], d_scores: torch.Tensor, geom: Geometry,
+                 out: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    """Gradient of the distillation loss with respect to W_q and W_k ([heads,
+    3d, r] fp32), through the estimator outputs `est` (stats_q, stats_k,
+    feat_q, feat_k from trippool_score). Also returns d_feat_q, d_feat_k."""
+    r = est["feat_q"].shape[-1]
+    d, nT, B, Hh = geom.head_dim, geom.max_tiles(), geom.B, geom.n_heads
+    _need(d_scores, torch.float32, (B, Hh, nT, nT), "d_scores")
+    dev = d_scores.device
+    if out is None:
+        out = {"d_feat_q": torch.empty((B, Hh, nT, r), dtype=torch.float32, device=dev),
+               "d_feat_k": torch.empty((B, Hh, nT, r), dtype=torch.float32, device=dev),
+               "d_w_q": torch.empty((Hh, 3 * d, r), dtype=torch.float32, device=dev),
+               "d_w_k": torch.empty((Hh, 3 * d, r), dtype=torch.float32, device=dev)}
+    for n, shp in (("d_feat_q", (B, Hh, nT, r)), ("d_feat_k", (B, Hh, nT, r)), ("d_w_q", (Hh, 3 * d, r)),
+                   ("d_w_k", (Hh, 3 * d, r))):
+        _need(out[n], torch.float32, shp, n)
+    for n, shp in (("stats_q", (B, Hh, nT, 3 * d)), ("stats_k", (B, Hh, nT, 3 * d)), ("feat_q", (B, Hh, nT, r)),
+                   ("feat_k", (B, Hh, nT, r))):
+        _need(est[n], torch.bfloat16, shp, n)
+    _lib.check(_lib.lib.veda_distill_grad(
+        geom.c, int(r), est["stats_q"].data_ptr(), est["stats_k"].data_ptr(), est["feat_q"].data_ptr(),
+        est["feat_k"].data_ptr(), d_scores.data_ptr(), out["d_feat_q"].data_ptr(), out["d_feat_k"].data_ptr(),
+        out["d_w_q"].data_ptr(), out["d_w_k"].data_ptr(), _stream(d_scores)), "veda_distill_grad")
+    return out
+
+
+def adam_step(w: torch.Tensor, grad: torch.Tensor, m: torch.Tensor, v: torch.Tensor, step: int, lr: float,
+              betas: Tuple[float, float] = (0.9, 0.999), eps: float = 1e-8,
+              w_bf16: Optional[torch.Tensor] = None) -> None:
+    """One bias-corrected Adam step on fp32 master weights (in place), and
+    their bf16 copy when given."""
+    for name, t in (("w", w), ("grad", grad), ("m", m), ("v", v)):
+        _need(t, torch.float32, tuple(w.shape), name)
+    if w_bf16 is not None:
+        _need(w_bf16, torch.bfloat16, tuple(w.shape), "w_bf16")
+    _lib.check(_lib.lib.veda_adam_step(w.numel(), w.data_ptr(), grad.data_ptr(), m.data_ptr(), v.data_ptr(),
+                                       int(step), float(lr), float(betas[0]), float(betas[1]), float(eps),
+                                       w_bf16.data_ptr() if w_bf16 is not None else None, _stream(w)),
+               "veda_adam_step")
+
+
+def distill_train(q_t: torch.Tensor, k_t: torch.Tensor, teacher: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
+                  geom: Geometry, steps: int, lr: float = 1e-2, betas: Tuple[float, float] = (0.9, 0.999),
+                  eps: float = 1e-8) -> Dict[str, object]:
+    """Distil the head-specific projections toward the teacher on fixed
+    calibration tiles: each step runs the estimator with the bf16 weights,
+    the KL objective (mean over query tiles) and its gradient, then Adam on
+    fp32 master copies. Returns the trained bf16 weights and the loss after
+    each step (mean KL per query tile, from the step's forward)."""
+    wq_m, wk_m = w_q.float().contiguous(), w_k.float().contiguous()
+    wq_b, wk_b = w_q.clone(), w_k.clone()
+    mq, vq, mk, vk = (torch.zeros_like(wq_m) for _ in range(4))
+    rows = sum(geom.num_tiles(hd) for hd in range(geom.n_heads)) * geom.B
+    losses = []
+    est, grads, kl, ds = None, None, None, None
+    for step in range(1, steps + 1):
+        est = trippool_score(q_t, k_t, wq_b, wk_b, geom, est)
+        kl, ds = distill_kl(est["scores"], teacher, geom, 1.0 / rows, kl, ds)
+        grads = distill_grad(est, ds, geom, grads)
+        adam_step(wq_m, grads["d_w_q"], mq, vq, step, lr, betas, eps, wq_b)
+        adam_step(wk_m, grads["d_w_k"], mk, vk, step, lr, betas, eps, wk_b)
+        losses.append(kl)
+        kl = None
+    return {"w_q": wq_b, "w_k": wk_b, "loss": [float(x.cpu().numpy().astype("float64").sum()) / rows for x in losses]}

@@ -25,7 +25,8 @@ STATUS = {
 
 EXPORTS = ["veda_status_str", "veda_num_tiles", "veda_max_tiles", "veda_tile_permute", "veda_trippool_score",
            "veda_topk_mask", "veda_sparse_attn_fwd", "veda_tile_unpermute", "veda_teacher_tile_max",
-           "veda_mask_overlap", "veda_head_sq_error"]
+           "veda_mask_overlap", "veda_head_sq_error", "veda_distill_kl", "veda_distill_grad",
+           "veda_adam_step"]
 
 
 class VedaGrid(ctypes.Structure):
@@ -81,6 +82,14 @@ def _load():
     lib.veda_head_sq_error.argtypes = [POINTER(VedaGeom), c_void_p, VedaRasterStrides, c_void_p, VedaRasterStrides,
                                        c_void_p, c_void_p]
     lib.veda_head_sq_error.restype = ctypes.c_int
+    lib.veda_distill_kl.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_void_p]
+    lib.veda_distill_kl.restype = ctypes.c_int
+    lib.veda_distill_grad.argtypes = [POINTER(VedaGeom), c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.veda_distill_grad.restype = ctypes.c_int
+    lib.veda_adam_step.argtypes = [c_int64, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_float, c_float,
+                                   c_float, c_void_p, c_void_p]
+    lib.veda_adam_step.restype = ctypes.c_int
     return lib
 
 

@@ -15,7 +15,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libveda.so")
-SOURCES = ["veda_host.hip", "permute.hip", "trippool.hip", "topk.hip", "sparse_attn.hip", "teacher.hip", "metrics.hip"]
+SOURCES = ["veda_host.hip", "permute.hip", "trippool.hip", "topk.hip", "sparse_attn.hip", "teacher.hip", "metrics.hip", "distill.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [

@@ -253,4 +253,54 @@ int veda_head_sq_error(const veda_geom* g, const void* a_raster, veda_raster_str
                                              static_cast<hipStream_t>(stream)));
 }
 
+int veda_distill_kl(const veda_geom* g, const float* scores, const float* teacher, float grad_scale, float* kl_rows,
+                    float* d_scores, void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!scores || !teacher || !kl_rows || !d_scores) return VEDA_ERR_NULL;
+  for (const void* p : {static_cast<const void*>(scores), static_cast<const void*>(teacher),
+                        static_cast<const void*>(kl_rows), static_cast<const void*>(d_scores)})
+    if (!aligned16(p)) return VEDA_ERR_ALIGN;
+  if (!std::isfinite(grad_scale)) return VEDA_ERR_SHAPE;
+  VEDA_TRY(check_device());
+  return launched(veda::launch_distill_kl(t, scores, teacher, grad_scale, kl_rows, d_scores,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int veda_distill_grad(const veda_geom* g, int32_t rank, const void* stats_q, const void* stats_k, const void* feat_q,
+                      const void* feat_k, const float* d_scores, float* d_feat_q, float* d_feat_k, float* d_w_q,
+                      float* d_w_k, void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (rank != 32 && rank != 64) return VEDA_ERR_SHAPE;
+  if (!stats_q || !stats_k || !feat_q || !feat_k || !d_scores || !d_feat_q || !d_feat_k || !d_w_q || !d_w_k)
+    return VEDA_ERR_NULL;
+  for (const void* p : {stats_q, stats_k, feat_q, feat_k, static_cast<const void*>(d_scores),
+                        static_cast<const void*>(d_feat_q), static_cast<const void*>(d_feat_k),
+                        static_cast<const void*>(d_w_q), static_cast<const void*>(d_w_k)})
+    if (!aligned16(p)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_device());
+  return launched(veda::launch_distill_grad(
+      t, rank, static_cast<const uint16_t*>(stats_q), static_cast<const uint16_t*>(stats_k),
+      static_cast<const uint16_t*>(feat_q), static_cast<const uint16_t*>(feat_k), d_scores, d_feat_q, d_feat_k, d_w_q,
+      d_w_k, static_cast<hipStream_t>(stream)));
+}
+
+int veda_adam_step(int64_t n, float* w_master, const float* grad, float* m, float* v, int32_t step, float lr,
+                   float beta1, float beta2, float eps, void* w_bf16, void* stream) {
+  if (!w_master || !grad || !m || !v) return VEDA_ERR_NULL;
+  if (n <= 0 || step < 1 || !std::isfinite(lr) || !(beta1 >= 0.0f && beta1 < 1.0f) ||
+      !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps > 0.0f) || !std::isfinite(eps))
+    return VEDA_ERR_SHAPE;
+  for (const void* p : {static_cast<const void*>(w_master), static_cast<const void*>(grad),
+                        static_cast<const void*>(m), static_cast<const void*>(v)})
+    if (!aligned16(p)) return VEDA_ERR_ALIGN;
+  if (w_bf16 && !aligned16(w_bf16)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_device());
+  const float bc1 = float(1.0 - std::pow(double(beta1), double(step)));
+  const float bc2 = float(1.0 - std::pow(double(beta2), double(step)));
+  return launched(veda::launch_adam(n, w_master, grad, m, v, lr, beta1, beta2, eps, bc1, bc2,
+                                    static_cast<uint16_t*>(w_bf16), static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

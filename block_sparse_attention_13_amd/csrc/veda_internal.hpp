@@ -113,6 +113,13 @@ hipError_t launch_mask_overlap(const GeoTable& g, const uint32_t* a, const uint3
 hipError_t launch_head_sq_error(const GeoTable& g, const uint16_t* a, int64_t sab, int64_t san, int64_t sah,
                                 const uint16_t* b, int64_t sbb, int64_t sbn, int64_t sbh, double* err,
                                 hipStream_t s);
+hipError_t launch_distill_kl(const GeoTable& g, const float* scores, const float* teacher, float grad_scale,
+                             float* kl_rows, float* d_scores, hipStream_t s);
+hipError_t launch_distill_grad(const GeoTable& g, int32_t r, const uint16_t* stats_q, const uint16_t* stats_k,
+                               const uint16_t* feat_q, const uint16_t* feat_k, const float* d_scores,
+                               float* d_feat_q, float* d_feat_k, float* d_wq, float* d_wk, hipStream_t s);
+hipError_t launch_adam(int64_t n, float* w, const float* grad, float* m, float* v, float lr, float beta1, float beta2,
+                       float eps, float bc1, float bc2, uint16_t* w_bf16, hipStream_t s);
 hipError_t launch_sparse_attn(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t, const uint16_t* v_t,
                               const int32_t* idx, int32_t k_max, float scale, uint16_t* o_t, float* lse,
                               hipStream_t s);

@@ -17,6 +17,11 @@
  *   veda_mask_overlap          common kept tiles of two masks (tile recall)
  *   veda_head_sq_error         squared output error per head (objective of the head-aware tile search)
  *
+ * Distilling the estimator's projections toward the teacher:
+ *   veda_distill_kl            KL(teacher row || softmax(scores)) per query tile and its gradient
+ *   veda_distill_grad          that gradient back to W_q and W_k
+ *   veda_adam_step             one Adam update of fp32 master weights (+ their bf16 copy)
+ *
  * Conventions shared by every call
  * --------------------------------
  * Tensors are DEVICE pointers allocated and owned by the caller; the library
@@ -230,6 +235,45 @@ int veda_mask_overlap(const veda_geom* g, const uint32_t* bitmask_a, const uint3
  */
 int veda_head_sq_error(const veda_geom* g, const void* a_raster, veda_raster_strides sa, const void* b_raster,
                        veda_raster_strides sb, double* err, void* stream);
+
+/*
+ * Distillation objective (Veda page, "Theoretical Rationale" 4, "Distillation Objective": the
+ * estimator's soft tile distribution is aligned with the max-pooled full-attention target by a KL
+ * divergence before Top-k; Principle 01). Per (b, hd, query tile tq < nT_hd), over key tiles j < nT_hd:
+ *   A_tgt = teacher / sum_j teacher,  A_pred = softmax_j(scores),
+ *   kl_rows = sum_j A_tgt (log A_tgt - log A_pred),  d_scores = grad_scale * (A_pred - A_tgt).
+ *   scores      in   fp32 [B, heads, nT_max, nT_max] (veda_trippool_score)
+ *   teacher     in   fp32 [B, heads, nT_max, nT_max] (veda_teacher_tile_max)
+ *   grad_scale  in   factor on the gradient (e.g. 1 / number of rows for a mean loss); finite
+ *   kl_rows     out  fp32 [B, heads, nT_max]; 0 for query tiles >= nT_hd
+ *   d_scores    out  fp32 [B, heads, nT_max, nT_max]; 0 outside the head's block
+ * fp32 throughout, fixed summation order.
+ */
+int veda_distill_kl(const veda_geom* g, const float* scores, const float* teacher, float grad_scale, float* kl_rows,
+                    float* d_scores, void* stream);
+
+/*
+ * Gradient of the distillation loss with respect to the head-specific projections, through
+ * scores = feat_q . feat_k and feat = stats @ W (the bf16 rounding of feat taken as the identity):
+ *   d_feat_q = d_scores @ feat_k,  d_feat_k = d_scores^T @ feat_q   (per b, hd; fp32 [B, heads, nT_max, rank],
+ *                                                                   0 for tiles >= nT_hd)
+ *   d_w_q = sum_b stats_q^T @ d_feat_q,  d_w_k likewise             (fp32 [heads, 3d, rank])
+ *   stats_q, stats_k, feat_q, feat_k  in  bf16, as written by veda_trippool_score with this rank
+ * fp32 accumulation in ascending order of the contraction index (reproducible bit for bit).
+ */
+int veda_distill_grad(const veda_geom* g, int32_t rank, const void* stats_q, const void* stats_k, const void* feat_q,
+                      const void* feat_k, const float* d_scores, float* d_feat_q, float* d_feat_k, float* d_w_q,
+                      float* d_w_k, void* stream);
+
+/*
+ * One Adam step (bias-corrected) on n fp32 master weights, in place:
+ *   m = beta1 m + (1 - beta1) g;  v = beta2 v + (1 - beta2) g^2;
+ *   w -= lr * (m / (1 - beta1^step)) / (sqrt(v / (1 - beta2^step)) + eps)
+ * and, when w_bf16 is not NULL, its bf16 copy (round to nearest even) for veda_trippool_score.
+ * step >= 1; 0 <= beta < 1; eps > 0. Error VEDA_ERR_SHAPE otherwise.
+ */
+int veda_adam_step(int64_t n, float* w_master, const float* grad, float* m, float* v, int32_t step, float lr,
+                   float beta1, float beta2, float eps, void* w_bf16, void* stream);
 
 #ifdef __cplusplus
 }

@@ -9,4 +9,5 @@ from .veda_oracle import (bf16_round, bf16_bits_to_float, float_to_bf16_bits, ti
                           num_tiles, tiled_position, tile_permute, tile_unpermute, trippool,
                           fp32_dot_rows, project, tile_scores, topk_row_bruteforce, topk,
                           bitmask, sparse_attention, dense_attention, head_forward,
-                          teacher_tile_max, mask_overlap, tile_recall, tile_search_errors)
+                          teacher_tile_max, mask_overlap, tile_recall, tile_search_errors,
+                          distill_kl, distill_grad, distill_loss, adam_step)

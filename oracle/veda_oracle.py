@@ -370,6 +370,57 @@ def tile_search_errors(q: np.ndarray, k: np.ndarray, v: np.ndarray, wq: np.ndarr
 
 
 # --------------------------------------------------------------------------
+# Distillation objective ([Veda] "Theoretical Rationale" 4, "Distillation
+# Objective": the estimator's soft tile distribution is aligned with the
+# max-pooled full-attention target by D_KL(A_tgt || A_pred) before Top-k;
+# Principle 01 "Full-Attention Structure Distillation")
+# --------------------------------------------------------------------------
+
+def distill_kl(S: np.ndarray, T: np.ndarray, grad_scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
+    """One head's rows (query tiles) over its key tiles: A_tgt = T row
+    normalised to sum 1, A_pred = softmax(S row); returns the per-row KL
+    divergence and grad_scale * dKL/dS = grad_scale * (A_pred - A_tgt).
+    Readings: the target is the teacher row normalised (the pages give no
+    other normalisation); the estimator's distribution is the softmax of its
+    scores at temperature 1."""
+    S = np.asarray(S, np.float64)
+    T = np.asarray(T, np.float64)
+    a_t = T / T.sum(axis=1, keepdims=True)
+    m = S.max(axis=1, keepdims=True)
+    log_p = S - m - np.log(np.exp(S - m).sum(axis=1, keepdims=True))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        terms = np.where(a_t > 0, a_t * (np.log(a_t) - log_p), 0.0)
+    return terms.sum(axis=1), grad_scale * (np.exp(log_p) - a_t)
+
+
+def distill_grad(stats_q: np.ndarray, stats_k: np.ndarray, feat_q: np.ndarray, feat_k: np.ndarray,
+                 dS: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Back from dL/dS through S = F_q F_k^T and F = stats W to dL/dW_q and
+    dL/dW_k (one head, one batch element), in float64."""
+    dS = np.asarray(dS, np.float64)
+    dFq = dS @ np.asarray(feat_k, np.float64)
+    dFk = dS.T @ np.asarray(feat_q, np.float64)
+    return np.asarray(stats_q, np.float64).T @ dFq, np.asarray(stats_k, np.float64).T @ dFk
+
+
+def distill_loss(stats_q: np.ndarray, stats_k: np.ndarray, wq: np.ndarray, wk: np.ndarray, T: np.ndarray) -> float:
+    """Summed KL of one head with the features computed exactly (no bf16
+    rounding): the function whose derivative distill_kl + distill_grad give."""
+    S = (np.asarray(stats_q, np.float64) @ wq) @ (np.asarray(stats_k, np.float64) @ wk).T
+    return float(distill_kl(S, T)[0].sum())
+
+
+def adam_step(w: np.ndarray, g: np.ndarray, m: np.ndarray, v: np.ndarray, step: int, lr: float,
+              beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8):
+    """Bias-corrected Adam (Kingma and Ba), float64; returns new (w, m, v)."""
+    m = beta1 * m + (1 - beta1) * g
+    v = beta2 * v + (1 - beta2) * g * g
+    mh = m / (1 - beta1 ** step)
+    vh = v / (1 - beta2 ** step)
+    return w - lr * mh / (np.sqrt(vh) + eps), m, v
+
+
+# --------------------------------------------------------------------------
 # The whole layer, one head at a time
 # --------------------------------------------------------------------------
 

@@ -450,6 +450,61 @@ def check_tile_search_errors(O, seed=10):
     assert np.all(O.tile_search_errors(q, k, v, wq, wk, grid, cands, lambda n: n) < 1e-20)
 
 
+# ------------------------------------------------------------- distillation
+
+def check_distill_gradient_finite_differences(O, seed=11):
+    """dL/dW from distill_kl + distill_grad against central finite differences
+    of the exact loss (float64, features unrounded)."""
+    rng = np.random.default_rng(seed)
+    n, c, r = 7, 12, 4
+    sq, sk = rng.standard_normal((n, c)), rng.standard_normal((n, c))
+    wq, wk = 0.5 * rng.standard_normal((c, r)), 0.5 * rng.standard_normal((c, r))
+    T = rng.uniform(0.01, 1.0, (n, n))
+    fq, fk = sq @ wq, sk @ wk
+    _, dS = O.distill_kl(fq @ fk.T, T)
+    gq, gk = O.distill_grad(sq, sk, fq, fk, dS)
+    h = 1e-6
+    for w, g, which in ((wq, gq, 0), (wk, gk, 1)):
+        num = np.zeros_like(w)
+        for idx in np.ndindex(*w.shape):
+            wp, wm = w.copy(), w.copy()
+            wp[idx] += h
+            wm[idx] -= h
+            lp = O.distill_loss(sq, sk, wp, wk, T) if which == 0 else O.distill_loss(sq, sk, wq, wp, T)
+            lm = O.distill_loss(sq, sk, wm, wk, T) if which == 0 else O.distill_loss(sq, sk, wq, wm, T)
+            num[idx] = (lp - lm) / (2 * h)
+        assert np.max(np.abs(num - g)) <= 1e-6 * max(1.0, np.max(np.abs(g))), (which, np.max(np.abs(num - g)))
+
+
+def check_distill_kl_closed_forms(O):
+    """KL vanishes when the scores are the teacher's logarithm plus a per-row
+    constant; a two-tile row has KL = a log(a/p) + (1-a) log((1-a)/(1-p));
+    gradient rows sum to zero; grad_scale scales only the gradient."""
+    T = np.array([[0.2, 0.5, 0.3], [1e-3, 2.0, 0.7]])
+    S = np.log(T) + np.array([[4.0], [-1.5]])
+    kl, dS = O.distill_kl(S, T)
+    assert np.all(np.abs(kl) < 1e-14) and np.max(np.abs(dS)) < 1e-14
+    a, p = 0.25, 1 / (1 + math.exp(-0.7))
+    kl2, dS2 = O.distill_kl(np.array([[0.7, 0.0]]), np.array([[1.0, 3.0]]), grad_scale=2.0)
+    want = a * math.log(a / p) + (1 - a) * math.log((1 - a) / (1 - p))
+    assert abs(kl2[0] - want) < 1e-14 and abs(dS2[0, 0] - 2 * (p - a)) < 1e-14
+    rng = np.random.default_rng(12)
+    _, d3 = O.distill_kl(rng.standard_normal((5, 9)), rng.uniform(0.1, 1, (5, 9)))
+    assert np.max(np.abs(d3.sum(axis=1))) < 1e-14
+
+
+def check_adam_first_steps(O):
+    """First Adam step moves every weight by lr * g / (|g| + eps) (bias
+    correction makes m_hat = g, v_hat = g^2); a second step with the same
+    gradient moves it by the same amount again."""
+    g = np.array([0.3, -2.0, 1e-3])
+    w0 = np.array([1.0, 2.0, 3.0])
+    w1, m, v = O.adam_step(w0, g, np.zeros(3), np.zeros(3), 1, 0.1, eps=1e-8)
+    assert np.allclose(w1, w0 - 0.1 * g / (np.abs(g) + 1e-8), rtol=0, atol=1e-15)
+    w2, _, _ = O.adam_step(w1, g, m, v, 2, 0.1, eps=1e-8)
+    assert np.allclose(w2, w1 - 0.1 * g / (np.abs(g) + 1e-8), rtol=0, atol=1e-12)
+
+
 ALL_SMALL_CHECKS = [
     check_permutation_golden,
     lambda O: check_permutation_bruteforce(O, [((2, 3, 4), (1, 2, 2)), ((4, 16, 16), (2, 8, 8)),
@@ -473,4 +528,7 @@ ALL_SMALL_CHECKS = [
     check_teacher_uniform_keys,
     check_recall_golden,
     check_tile_search_errors,
+    check_distill_gradient_finite_differences,
+    check_distill_kl_closed_forms,
+    check_adam_first_steps,
 ]

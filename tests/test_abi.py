@@ -21,7 +21,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     from block_sparse_attention_13_amd import _lib
     declared = _declared_functions()
-    assert len(declared) == 11, declared
+    assert len(declared) == 14, declared
     assert sorted(_lib.EXPORTS) == declared
     for name in declared:
         assert hasattr(_lib.lib, name), name
@@ -107,6 +107,13 @@ def test_call_errors_precede_any_device_work():
     assert L.veda_mask_overlap(g.c, FAKE, None, FAKE, None) == -1
     assert L.veda_mask_overlap(g.c, FAKE, FAKE, FAKE + 8, None) == -5
     assert L.veda_head_sq_error(g.c, FAKE, s, None, s, FAKE, None) == -1
+    assert L.veda_distill_kl(g.c, FAKE, None, 1.0, FAKE, FAKE, None) == -1
+    assert L.veda_distill_kl(g.c, FAKE, FAKE, float("inf"), FAKE, FAKE, None) == -2
+    assert L.veda_distill_grad(g.c, 48, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert L.veda_distill_grad(g.c, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, None) == -5
+    assert L.veda_adam_step(16, FAKE, FAKE, FAKE, FAKE, 0, 1e-3, 0.9, 0.999, 1e-8, None, None) == -2
+    assert L.veda_adam_step(16, FAKE, FAKE, FAKE, FAKE, 1, 1e-3, 1.0, 0.999, 1e-8, None, None) == -2
+    assert L.veda_adam_step(16, FAKE, None, FAKE, FAKE, 1, 1e-3, 0.9, 0.999, 1e-8, None, None) == -1
     assert L.veda_head_sq_error(g.c, FAKE, s, FAKE, _lib.VedaRasterStrides(1024, 130, 128), FAKE, None) == -5
 
 

@@ -65,6 +65,14 @@ MUTANTS = {
         ("qi = np.flatnonzero(tile_of == i)", "qi = np.flatnonzero(tile_of == (i + 1) % nT)"),
     "tile search sums absolute differences":
         ("errs.append(float(((r[\"o\"] - o_dense) ** 2).sum()))", "errs.append(float(np.abs(r[\"o\"] - o_dense).sum()))"),
+    "distillation gradient with the wrong sign":
+        ("return terms.sum(axis=1), grad_scale * (np.exp(log_p) - a_t)", "return terms.sum(axis=1), grad_scale * (a_t - np.exp(log_p))"),
+    "distillation target not normalised":
+        ("a_t = T / T.sum(axis=1, keepdims=True)", "a_t = T"),
+    "distillation gradient through the wrong feature side":
+        ("dFq = dS @ np.asarray(feat_k, np.float64)", "dFq = dS @ np.asarray(feat_q, np.float64)"),
+    "adam without bias correction":
+        ("mh = m / (1 - beta1 ** step)", "mh = m"),
     "mask overlap counts either mask":
         ("both = np.asarray(bitmask_a, dtype=np.uint32) & np.asarray(bitmask_b, dtype=np.uint32)",
          "both = np.asarray(bitmask_a, dtype=np.uint32) | np.asarray(bitmask_b, dtype=np.uint32)"),
