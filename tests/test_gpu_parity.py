@@ -105,6 +105,7 @@ def check_head(w, data, out, hd, ks, tiles, b=0, check_attention=True):
     ("480p", None, 24),
     ("720p", [0, 1, 2, 21, 39], 12),
     ("hc", [0, 1, 2, 3, 4, 5, 38, 39], 12),
+    ("long", [0, 17, 39], 8),     # the benchmarked 245,760-token layer, full size
 ])
 def test_layer_matches_oracle(name, heads, tiles_per_head):
     w = W[name]
