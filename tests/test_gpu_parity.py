@@ -194,6 +194,35 @@ def test_single_tile_kept():
         check_head(w, data, out, hd, ks, list(range(8)))
 
 
+@pytest.mark.parametrize("grid,tiles,d,r", [
+    ((1, 1, 1), [(1, 8, 16), (8, 4, 4)], 64, 32),      # one real token: one box of 127 pad slots
+    ((1, 1, 3), [(1, 8, 16), (2, 8, 8)], 128, 64),     # three real tokens in one box
+    ((3, 1, 2), [(2, 8, 8), (8, 4, 4)], 64, 64),       # boxes with 4 and 2 real tokens
+])
+def test_grids_smaller_than_a_tile(grid, tiles, d, r):
+    """Degenerate grids: every box is mostly pad slots; the attention of a
+    query covers only the few real keys of its head."""
+    w = _random_workload(grid, tiles, d, r, heads=2, seed=13)
+    data = datagen.generate(w)
+    ks = [w.tiles_per_head()[hd] for hd in range(2)]
+    say(f"[degenerate] grid {grid} tiles {tiles} -> {w.tiles_per_head()} boxes")
+    geom, out, _ = run_layer(w, data, k_per_head=ks)
+    for hd in range(2):
+        check_head(w, data, out, hd, ks, list(range(w.tiles_per_head()[hd])))
+
+
+def test_largest_tile_count():
+    """A head at the library's limit of 8192 tiles (1,048,576 tokens) through
+    the whole layer; the oracle checks sampled query tiles."""
+    V = _lib()
+    w = _random_workload((64, 128, 128), [(4, 4, 8)], 64, 32, heads=1, seed=17, k=16)
+    assert w.tiles_per_head() == [8192] == [V._lib.VEDA_MAX_TILES]
+    say("[max] 8192 tiles, 1,048,576 tokens")
+    data = datagen.generate(w)
+    geom, out, _ = run_layer(w, data)
+    check_head(w, data, out, 0, w.k_per_head(), _sample_tiles(8192, 6, 1))
+
+
 def test_equal_scores_keep_the_lower_tile():
     """Duplicate key tiles give exactly equal scores: the lower index must win
     end to end, and the lists must match the oracle's."""
