@@ -29,13 +29,24 @@ struct TeacherShape {
   static constexpr int kChunksPerWave = AttnShape<D>::kChunks / kWaves;  // K chunks each wave copies
 };
 
-// Largest value over the 64 lanes of a wave.
+// Largest value over the 64 lanes of a wave, in registers: DPP butterflies
+// inside each 16-lane row (quad swaps, then the half-row and row mirrors),
+// then the four row results read out as scalars.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_max(float x) {
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), kCtrl, 0xF, 0xF,
+                                                              false)));
+}
 __device__ __forceinline__ float wave_max(float x) {
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
+  x = dpp_max<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x = dpp_max<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x = dpp_max<0x141>(x);  // row_half_mirror
+  x = dpp_max<0x140>(x);  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 template <int D>
@@ -102,17 +113,26 @@ __global__ __launch_bounds__(kThreads, 2) void teacher_kernel(GeoTable g, const 
 
   const floatx16 zero = {};
   int buf = 0;  // j % 3
+  // K fragments of the current tile; those of tile j+1 are read right after
+  // tile j's MFMAs are issued (tile j+1 has been resident since the previous
+  // iteration's barrier), so the LDS latency hides under the MFMAs.
+  u32x4 kf[2 * S::kDC];
+#pragma unroll
+  for (int t = 0; t < 2 * S::kDC; ++t) kf[t] = k_frag<D>(&kbuf[0][0], t, half, h, l32);
   for (int32_t j = 0; j < nT; ++j) {
+    const int next = buf == 2 ? 0 : buf + 1;
     // K of tile j+2 into the buffer of tile j-1 (read in the previous iteration).
-    if (j + 2 < nT) copy_tile(j + 2, buf == 0 ? 2 : buf - 1);
-    const uint16_t* ks = &kbuf[buf][0];
+    if (j + 2 < nT) copy_tile(j + 2, next == 2 ? 0 : next + 1);
     floatx16 sacc[2];
 #pragma unroll
     for (int t = 0; t < 2 * S::kDC; ++t) {
-      const int kb = t / S::kDC, dc = t % S::kDC;
-      const u32x4 kf = k_frag<D>(ks, t, half, h, l32);
-      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[dc]),
+      const int kb = t % 2, dc = t / 2;  // alternate the two accumulators
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[kb * S::kDC + dc]), as_bf16x8(qf[dc]),
                                                          dc == 0 ? zero : sacc[kb], 0, 0, 0);
+    }
+    if (j + 1 < nT) {
+#pragma unroll
+      for (int t = 0; t < 2 * S::kDC; ++t) kf[t] = k_frag<D>(&kbuf[next][0], t, half, h, l32);
     }
     // Pad keys of a border tile never raise the maximum.
     const uint64_t wm = real_key_bits(g, hg, j, half, h);
@@ -144,7 +164,7 @@ __global__ __launch_bounds__(kThreads, 2) void teacher_kernel(GeoTable g, const 
       for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[j & 1][w]);
       trow[j] = __builtin_amdgcn_exp2f(m);
     }
-    buf = buf == 2 ? 0 : buf + 1;
+    buf = next;
   }
 }
 
