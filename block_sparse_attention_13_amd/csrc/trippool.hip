@@ -11,8 +11,8 @@
 //     the same wave projects them with the head's W (held in LDS for the whole
 //     workgroup, 3 workgroups per CU): lane j owns output feature j and
 //     accumulates over the 3d channels in order.
-//   tile_scores_kernel  S = feat_q . feat_k^T per head, 64 x 64 outputs per
-//     workgroup, 4 x 4 per thread, fp32 accumulated over the r channels in order.
+//   tile_scores_kernel  S = feat_q . feat_k^T per head, 128 x 128 outputs per
+//     workgroup, 8 x 8 per thread, fp32 accumulated over the r channels in order.
 // Every accumulation runs in a fixed ascending order with one rounding per
 // step (products of bf16 values are exact in fp32), so the results are
 // reproducible bit for bit and independent of the launch shape.
@@ -143,18 +143,20 @@ __global__ __launch_bounds__(kThreads) void trippool_features_kernel(
   }
 }
 
-constexpr int kScoreTile = 64;
+constexpr int kScoreTile = 128;   // scores per workgroup: 128 x 128, 8 x 8 per thread
+constexpr int kScorePad = 4;      // LDS row padding (floats): spreads the transposing stores over banks
 
 template <int R>
 __global__ __launch_bounds__(kThreads) void tile_scores_kernel(GeoTable g, const uint16_t* __restrict__ feat_q,
                                                               const uint16_t* __restrict__ feat_k,
                                                               float* __restrict__ scores) {
-  __shared__ float fq_s[R][kScoreTile];  // transposed: [channel][row]
-  __shared__ float fk_s[R][kScoreTile];
+  __shared__ __attribute__((aligned(16))) float fq_s[R][kScoreTile + kScorePad];  // transposed: [channel][row]
+  __shared__ __attribute__((aligned(16))) float fk_s[R][kScoreTile + kScorePad];
   const int hd = blockIdx.y, b = blockIdx.z;
   const HeadGeo hg = g.h[hd];
-  const int i0 = blockIdx.x / ((g.nT_max + kScoreTile - 1) / kScoreTile) * kScoreTile;
-  const int j0 = blockIdx.x % ((g.nT_max + kScoreTile - 1) / kScoreTile) * kScoreTile;
+  const int nb = (g.nT_max + kScoreTile - 1) / kScoreTile;
+  const int i0 = blockIdx.x / nb * kScoreTile;
+  const int j0 = blockIdx.x % nb * kScoreTile;
   const int64_t head_row = (int64_t(b) * g.heads + hd) * g.nT_max;
   for (int e = threadIdx.x; e < kScoreTile * R; e += kThreads) {
     const int r = e / R, c = e % R;
@@ -164,39 +166,44 @@ __global__ __launch_bounds__(kThreads) void tile_scores_kernel(GeoTable g, const
   }
   __syncthreads();
   const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
-  float acc[4][4];
+  float acc[8][8];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[a][c] = 0.0f;
-#pragma unroll 8
+    for (int c = 0; c < 8; ++c) acc[a][c] = 0.0f;
+#pragma unroll 4
   for (int c = 0; c < R; ++c) {
-    const float4 qa = *reinterpret_cast<const float4*>(&fq_s[c][ty * 4]);
-    const float4 kb = *reinterpret_cast<const float4*>(&fk_s[c][tx * 4]);
-    const float qv[4] = {qa.x, qa.y, qa.z, qa.w};
-    const float kv[4] = {kb.x, kb.y, kb.z, kb.w};
+    const float4 q0 = *reinterpret_cast<const float4*>(&fq_s[c][ty * 8]);
+    const float4 q1 = *reinterpret_cast<const float4*>(&fq_s[c][ty * 8 + 4]);
+    const float4 k0 = *reinterpret_cast<const float4*>(&fk_s[c][tx * 8]);
+    const float4 k1 = *reinterpret_cast<const float4*>(&fk_s[c][tx * 8 + 4]);
+    const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    const float kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2) acc[a][k2] = __builtin_fmaf(qv[a], kv[k2], acc[a][k2]);
+      for (int k2 = 0; k2 < 8; ++k2) acc[a][k2] = __builtin_fmaf(qv[a], kv[k2], acc[a][k2]);
   }
   const float ninf = -__builtin_inff();
   const bool vec_ok = (g.nT_max % 4) == 0;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int i = i0 + ty * 4 + a;
+  for (int a = 0; a < 8; ++a) {
+    const int i = i0 + ty * 8 + a;
     if (i >= g.nT_max) continue;
     float* out = scores + (head_row + i) * g.nT_max;
-    const int j = j0 + tx * 4;
-    float v[4];
 #pragma unroll
-    for (int k2 = 0; k2 < 4; ++k2) v[k2] = (i < hg.nT && j + k2 < hg.nT) ? acc[a][k2] : ninf;
-    if (vec_ok && j + 3 < g.nT_max) {
-      *reinterpret_cast<float4*>(out + j) = make_float4(v[0], v[1], v[2], v[3]);
-    } else {
+    for (int half = 0; half < 2; ++half) {
+      const int j = j0 + tx * 8 + 4 * half;
+      float v[4];
 #pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2)
-        if (j + k2 < g.nT_max) out[j + k2] = v[k2];
+      for (int k2 = 0; k2 < 4; ++k2) v[k2] = (i < hg.nT && j + k2 < hg.nT) ? acc[a][4 * half + k2] : ninf;
+      if (vec_ok && j + 3 < g.nT_max) {
+        *reinterpret_cast<float4*>(out + j) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2)
+          if (j + k2 < g.nT_max) out[j + k2] = v[k2];
+      }
     }
   }
 }
