@@ -29,6 +29,8 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+PEAK_FP32_VALU_TFLOPS = 157.3   # MI355X fp32 vector FMA (256 CUs x 2.4 GHz x 256 flop/clk)
+HIP_ATTR_CLOCK_KHZ = 5          # hipDeviceAttributeClockRate in the ROCm 7 HIP headers
 
 
 def log(*a):
@@ -39,6 +41,51 @@ def attention_flops(w) -> float:
     """Whole 128x128 tile pairs on the selected tiles, QK^T and PV, 2 flop per MAC."""
     pairs = sum(n * k for n, k in zip(w.tiles_per_head(), w.k_per_head())) * w.B
     return 4.0 * w.d * 128 * 128 * pairs
+
+
+def estimator_flops(w) -> float:
+    """Projections of the Q and K statistics (3d -> r) and the tile scores
+    (nT x nT dot products of length r), 2 flop per multiply-add."""
+    nts = w.tiles_per_head()
+    proj = sum(2 * 2 * n * 3 * w.d * w.r for n in nts)
+    scores = sum(2 * n * n * w.r for n in nts)
+    return float((proj + scores) * w.B)
+
+
+def device_report() -> dict:
+    """Device 0 as the HIP runtime reports it (name, architecture, compute
+    units, HBM size, peak shader clock) and the bf16 MFMA peak those imply at
+    4096 flop per compute unit per clock."""
+    import ctypes
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    out = {"name": p.name, "arch": p.gcnArchName, "compute_units": p.multi_processor_count,
+           "hbm_gib": round(p.total_memory / 2**30, 1)}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")   # the runtime torch has already loaded
+        v = ctypes.c_int()
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), HIP_ATTR_CLOCK_KHZ, 0) == 0:
+            out["peak_clock_mhz"] = v.value / 1000.0
+            out["bf16_peak_tflops_implied"] = round(p.multi_processor_count * v.value * 1e3 * 4096 / 1e12, 1)
+    except OSError:
+        pass
+    return out
+
+
+def layer_floor(w, stage_ms: dict) -> dict:
+    """Speed-of-light time of each stage, the larger of its arithmetic at the
+    unit's peak and its algorithmic HBM bytes at 8 TB/s, and the layer's
+    roofline fraction: the sum of the floors over the measured time."""
+    sb = stage_bytes(w)
+    sb["sparse_attn"] = attention_bytes(w)
+    fl = {"permute_x3": 0.0, "trippool_score": estimator_flops(w) / PEAK_FP32_VALU_TFLOPS,
+          "topk": 0.0, "sparse_attn": attention_flops(w) / PEAK_BF16_TFLOPS, "unpermute": 0.0}
+    floor = {n: max(fl[n] / 1e9, sb[n] / (PEAK_HBM_GBS * 1e6)) for n in fl}   # ms
+    total = sum(floor.values())
+    return {"floor_ms": {n: round(v, 4) for n, v in floor.items()}, "floor_ms_layer": round(total, 3),
+            "frac": round(total / sum(stage_ms[n] for n in floor), 4),
+            "note": "estimator priced at the fp32 vector peak (it runs on the VALU), attention at the bf16 "
+                    "MFMA peak, every other stage at HBM bandwidth"}
 
 
 def stage_bytes(w) -> dict:
@@ -172,10 +219,12 @@ def valid_pair_flops(w, idx_cpu) -> float:
     return 4.0 * w.d * total
 
 
-def run_workload(V, datagen, w, steps, warmup, keep_data=True):
+def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0):
     """Generate the workload's inputs, run one layer to allocate every buffer,
     then time `steps` layers after `warmup` untimed ones with HIP events on
-    the launch stream around each of the five stages."""
+    the launch stream around each of the five stages. With `flush_mib`, time
+    the same steps a second time with a write of that many MiB before each
+    step (outside the events), so that no input is still in L2 or MALL."""
     import numpy as np
     import torch
     log(f"[bench] workload {w.name}: {w.description}")
@@ -223,25 +272,39 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True):
     torch.cuda.synchronize()
     log(f"[bench] warmup {warmup} done")
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for s in range(steps):
-        step(events[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    per_stage = {name: [] for name in stages}
-    total = []
-    for ev in events:
-        for i, name in enumerate(stages):
-            per_stage[name].append(ev[i].elapsed_time(ev[i + 1]))
-        total.append(ev[0].elapsed_time(ev[5]))
-    ms_step = float(np.mean(total))
-    stage_ms = {n: round(float(np.mean(v)), 4) for n, v in per_stage.items()}
-    log(f"[bench] timed {steps} steps: {ms_step:.3f} ms/layer (wall {wall / steps * 1e3:.3f} ms); {stage_ms}")
-    out = {"ms_step": ms_step, "stage_ms": stage_ms, "data": data if keep_data else None,
-           "valid_flops": valid_pair_flops(w, bufs["idx"].cpu().numpy()),
-           "bitmask": bufs["bitmask"] if keep_data else None}
+    def timed(flush=None):
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        for s in range(steps):
+            if flush is not None:
+                flush.fill_(s & 0x7F)
+            step(events[s])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        per_stage = {name: [] for name in stages}
+        total = []
+        for ev in events:
+            for i, name in enumerate(stages):
+                per_stage[name].append(ev[i].elapsed_time(ev[i + 1]))
+            total.append(ev[0].elapsed_time(ev[5]))
+        res = {"ms_step": float(np.mean(total)), "ms_step_median": float(np.median(total)),
+               "ms_step_min": float(np.min(total)),
+               "stage_ms": {n: round(float(np.mean(v)), 4) for n, v in per_stage.items()},
+               "stage_ms_median": {n: round(float(np.median(v)), 4) for n, v in per_stage.items()},
+               "stage_ms_min": {n: round(float(np.min(v)), 4) for n, v in per_stage.items()}}
+        log(f"[bench] timed {steps} steps{' (flushed)' if flush is not None else ''}: {res['ms_step']:.3f} "
+            f"ms/layer (median {res['ms_step_median']:.3f}, min {res['ms_step_min']:.3f}, wall "
+            f"{wall / steps * 1e3:.3f} ms); {res['stage_ms']}")
+        return res
+
+    out = timed()
+    if flush_mib:
+        flush = torch.empty(flush_mib << 20, dtype=torch.uint8, device=dev)
+        out["flushed"] = timed(flush)
+        del flush
+    out.update({"data": data if keep_data else None, "valid_flops": valid_pair_flops(w, bufs["idx"].cpu().numpy()),
+                "bitmask": bufs["bitmask"] if keep_data else None})
     del bufs, q, k, v, wq, wk
     torch.cuda.empty_cache()
     return out
@@ -448,18 +511,36 @@ def main():
             if name == args.workload:
                 continue
             wo = datagen.WORKLOADS[name]
-            ro = run_workload(V, datagen, wo, 5, 2, keep_data=False)
+            ro = run_workload(V, datagen, wo, 5, 2, keep_data=False, flush_mib=512)
             t_a = ro["stage_ms"]["sparse_attn"] * 1e-3
             fo, fv = attention_flops(wo), ro["valid_flops"]
+            rf = ro["flushed"]
             per_config[name] = {
                 "workload": wo.description, "ms_per_layer": round(ro["ms_step"], 4),
+                "ms_per_layer_median": round(ro["ms_step_median"], 4), "ms_per_layer_min": round(ro["ms_step_min"], 4),
                 "attn_ms": round(ro["stage_ms"]["sparse_attn"], 4),
                 "attn_tflops": round(fo / t_a / 1e12, 1), "attn_frac_bf16_peak": round(fo / t_a / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "attn_tflops_valid_pairs": round(fv / t_a / 1e12, 1),
                 "stage_ms": ro["stage_ms"],
+                "cache_flushed": {"ms_per_layer": round(rf["ms_step"], 4), "stage_ms": rf["stage_ms"],
+                                  "flush": "512 MiB device write before each step, outside the timed events"},
+                "layer_roofline": layer_floor(wo, ro["stage_ms"]),
             }
             log(f"[bench] {name}: {per_config[name]['ms_per_layer']} ms/layer, attention "
                 f"{per_config[name]['attn_tflops']} TFLOP/s")
+
+    # One GPU's share of the layer when its 40 heads are split over eight
+    # GPUs by head (5 heads, all 245,760 tokens): the shard runs alone here.
+    shard = None
+    if not args.no_other_configs and not args.heads and w.heads >= 8:
+        ws = w.with_heads(w.heads // 8)
+        rs = run_workload(V, datagen, ws, 5, 2, keep_data=False)
+        t_a = rs["stage_ms"]["sparse_attn"] * 1e-3
+        shard = {"workload": ws.description, "heads": ws.heads, "ms_per_layer": round(rs["ms_step"], 4),
+                 "ms_per_layer_median": round(rs["ms_step_median"], 4), "stage_ms": rs["stage_ms"],
+                 "attn_tflops": round(attention_flops(ws) / t_a / 1e12, 1),
+                 "note": "one GPU's head shard of the layer under an 8-way head split; no exchange is timed"}
+        log(f"[bench] head shard: {shard}")
 
     search = None
     if not args.no_tile_search and not args.heads:
@@ -503,8 +584,14 @@ def main():
                    "tiles_per_head": max(w.tiles_per_head()), "k": max(w.k_per_head()), "rank": w.r},
         "attn_tflops": round(achieved, 1),
         "attn_frac_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "ms_per_layer_median": round(r["ms_step_median"], 3),
+        "ms_per_layer_min": round(r["ms_step_min"], 3),
         "stage_ms": stage_ms,
+        "stage_ms_median": r["stage_ms_median"],
+        "stage_ms_min": r["stage_ms_min"],
         "stage_hbm_gbs": hbm,
+        "layer_roofline": layer_floor(w, stage_ms),
+        "device": device_report(),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": attention_traffic(args.workload),
                      "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": attention_bytes(w),
@@ -512,6 +599,7 @@ def main():
                      "counters": attention_mfma_counters(args.workload)},
         "cpu_baseline": cpu,
         "per_config": per_config,
+        "head_shard": shard,
         "dense_reference": dense,
         "tile_search": search,
         "distillation": distill,

@@ -88,7 +88,12 @@ class Workload:
         return [(n * num + den - 1) // den for n in self.tiles_per_head()]
 
     def with_heads(self, heads: int) -> "Workload":
-        return dataclasses.replace(self, heads=heads)
+        """The first `heads` heads of this workload (same seeds, so each head's
+        inputs are the bytes it has in the full workload)."""
+        if heads == self.heads:
+            return self
+        desc = self.description.replace(f"{self.heads} heads", f"heads 0-{heads - 1} of {self.heads}", 1)
+        return dataclasses.replace(self, heads=heads, description=desc)
 
 
 WORKLOADS: Dict[str, Workload] = {
