@@ -2,9 +2,10 @@
 """Benchmark of one Veda tile-sparse attention layer on one MI355X.
 
 A step is the whole layer on one batch of seeded synthetic input already
-resident in HBM: tile permute of Q, K and V; TripPool estimator (stats,
-projections, tile scores); head-aware Top-k; tile-skipping attention forward;
-tile unpermute of O. Default workload: 245,760 tokens (64x48x80 latents),
+resident in HBM: tile permute of Q, K and V, the Q and K permutes also
+taking each tile's TripPool statistics (stage "permute_x3"); head-specific
+projections and tile scores ("project_score"); head-aware Top-k;
+tile-skipping attention forward; tile unpermute of O. Default workload: 245,760 tokens (64x48x80 latents),
 40 heads, d = 128, tile (4,4,8) -> 1920 tiles, k = 96 (95% sparse).
 
 Prints one JSON line: ms per layer (the value), the attention kernel's
@@ -78,7 +79,7 @@ def layer_floor(w, stage_ms: dict) -> dict:
     roofline fraction: the sum of the floors over the measured time."""
     sb = stage_bytes(w)
     sb["sparse_attn"] = attention_bytes(w)
-    fl = {"permute_x3": 0.0, "trippool_score": estimator_flops(w) / PEAK_FP32_VALU_TFLOPS,
+    fl = {"permute_x3": 0.0, "project_score": estimator_flops(w) / PEAK_FP32_VALU_TFLOPS,
           "topk": 0.0, "sparse_attn": attention_flops(w) / PEAK_BF16_TFLOPS, "unpermute": 0.0}
     floor = {n: max(fl[n] / 1e9, sb[n] / (PEAK_HBM_GBS * 1e6)) for n in fl}   # ms
     total = sum(floor.values())
@@ -100,8 +101,8 @@ def stage_bytes(w) -> dict:
     kmax = max(w.k_per_head())
     idx = B * Hh * nT * kmax * 4 + B * Hh * nT * ((nT + 31) // 32) * 4
     return {
-        "permute_x3": 3 * (raster + tiled),
-        "trippool_score": 2 * tiled + 2 * stats + 2 * feats + scores + 2 * Hh * 3 * d * w.r * 2,
+        "permute_x3": 3 * (raster + tiled) + 2 * stats,
+        "project_score": 2 * stats + 2 * feats + scores + 2 * Hh * 3 * d * w.r * 2,
         "topk": scores + idx,
         "unpermute": tiled + raster,
     }
@@ -242,18 +243,18 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0):
     torch.cuda.synchronize()
     log("[bench] first layer done")
 
-    stages = ["permute_x3", "trippool_score", "topk", "sparse_attn", "unpermute"]
+    stages = ["permute_x3", "project_score", "topk", "sparse_attn", "unpermute"]
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        V.tile_permute(q, geom, bufs["q_t"])
-        V.tile_permute(k, geom, bufs["k_t"])
+        V.tile_permute_stats(q, geom, bufs["q_t"], bufs["stats_q"])
+        V.tile_permute_stats(k, geom, bufs["k_t"], bufs["stats_k"])
         V.tile_permute(v, geom, bufs["v_t"], layout=V.CHANNEL_MAJOR)
         if ev is not None:
             ev[1].record(stream)
-        V.trippool_score(bufs["q_t"], bufs["k_t"], wq, wk, geom,
-                         {n: bufs[n] for n in ("stats_q", "stats_k", "feat_q", "feat_k", "scores")})
+        V.trippool_project_score(bufs["stats_q"], bufs["stats_k"], wq, wk, geom,
+                                 {n: bufs[n] for n in ("feat_q", "feat_k", "scores")})
         if ev is not None:
             ev[2].record(stream)
         V.topk_mask(bufs["scores"], geom, ks, idx=bufs["idx"], bitmask=bufs["bitmask"])

@@ -11,7 +11,10 @@ Python: the five steps of the layer are HIP kernels.
   topk_mask        scores -> ascending index lists (+ bitmask) per query tile
   sparse_attn_fwd  tiled Q, K, V + index lists -> tiled O (+ LSE)
   tile_unpermute   tiled -> raster
-  layer_forward    the five calls in order
+  tile_permute_stats      raster Q or K -> token-major tiles + TripPool stats, one pass
+  trippool_project_score  stats + W_q, W_k -> features, tile scores
+  layer_forward    the layer: tile_permute_stats of Q and K, tile_permute of V,
+                   trippool_project_score, topk_mask, sparse_attn_fwd, tile_unpermute
 
 Measuring a mask against the method's own target:
   dense_index      index lists that keep every key tile (dense attention through sparse_attn_fwd)
@@ -44,7 +47,8 @@ import torch
 from . import _lib
 from ._lib import VedaError
 
-__all__ = ["Geometry", "VedaError", "tile_permute", "tile_unpermute", "trippool_score", "topk_mask",
+__all__ = ["Geometry", "VedaError", "tile_permute", "tile_permute_stats", "tile_unpermute", "trippool_score",
+           "trippool_project_score", "topk_mask",
            "sparse_attn_fwd", "layer_forward", "dense_index", "teacher_tile_max", "mask_overlap", "tile_recall",
            "head_sq_error", "candidate_tiles", "tile_search", "distill_kl", "distill_grad", "adam_step",
            "distill_train", "TILE_TOKENS", "TOKEN_MAJOR", "CHANNEL_MAJOR"]
@@ -141,6 +145,26 @@ def tile_permute(x: torch.Tensor, geom: Geometry, out: Optional[torch.Tensor] = 
     return out
 
 
+def tile_permute_stats(x: torch.Tensor, geom: Geometry, out: Optional[torch.Tensor] = None,
+                       stats: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Token-major tile_permute of Q or K and the TripPool statistics of each
+    tile in one pass: (x_tiled [B, heads, nT_max, 128, d], stats [B, heads,
+    nT_max, 3d] bf16), the same bytes as tile_permute and trippool_score's
+    stats_q / stats_k."""
+    s = _raster_strides(x, geom, "x")
+    shape = _tiled_shape(geom, geom.head_dim)
+    sshape = (geom.B, geom.n_heads, geom.max_tiles(), 3 * geom.head_dim)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=x.device)
+    if stats is None:
+        stats = torch.empty(sshape, dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, shape, "out")
+    _need(stats, torch.bfloat16, sshape, "stats")
+    _lib.check(_lib.lib.veda_tile_permute_stats(geom.c, x.data_ptr(), s, out.data_ptr(), stats.data_ptr(),
+                                                _stream(x)), "veda_tile_permute_stats")
+    return out, stats
+
+
 def tile_unpermute(xt: torch.Tensor, geom: Geometry, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Scatter a tiled tensor back to raster order [B, N, heads, d]."""
     _need(xt, torch.bfloat16, _tiled_shape(geom, geom.head_dim), "x_tiled")
@@ -184,6 +208,37 @@ def trippool_score(q_t: torch.Tensor, k_t: torch.Tensor, w_q: torch.Tensor, w_k:
         geom.c, q_t.data_ptr(), k_t.data_ptr(), w_q.data_ptr(), w_k.data_ptr(), int(r),
         out["stats_q"].data_ptr(), out["stats_k"].data_ptr(), out["feat_q"].data_ptr(), out["feat_k"].data_ptr(),
         out["scores"].data_ptr(), _stream(q_t)), "veda_trippool_score")
+    return out
+
+
+def trippool_project_score(stats_q: torch.Tensor, stats_k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
+                           geom: Geometry, out: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    """Projections and tile scores from statistics already computed (by
+    tile_permute_stats): feat_q, feat_k [B, heads, nT_max, r] bf16 and scores
+    [B, heads, nT_max, nT_max] fp32, as trippool_score."""
+    d, nT = geom.head_dim, geom.max_tiles()
+    B, Hh = geom.B, geom.n_heads
+    _need(stats_q, torch.bfloat16, (B, Hh, nT, 3 * d), "stats_q")
+    _need(stats_k, torch.bfloat16, (B, Hh, nT, 3 * d), "stats_k")
+    if w_q.dim() != 3:
+        raise ValueError("w_q must be [heads, 3d, r]")
+    r = w_q.shape[2]
+    _need(w_q, torch.bfloat16, (Hh, 3 * d, r), "w_q")
+    _need(w_k, torch.bfloat16, (Hh, 3 * d, r), "w_k")
+    dev = stats_q.device
+    if out is None:
+        out = {
+            "feat_q": torch.empty((B, Hh, nT, r), dtype=torch.bfloat16, device=dev),
+            "feat_k": torch.empty((B, Hh, nT, r), dtype=torch.bfloat16, device=dev),
+            "scores": torch.empty((B, Hh, nT, nT), dtype=torch.float32, device=dev),
+        }
+    for name, shape, dt in (("feat_q", (B, Hh, nT, r), torch.bfloat16), ("feat_k", (B, Hh, nT, r), torch.bfloat16),
+                            ("scores", (B, Hh, nT, nT), torch.float32)):
+        _need(out[name], dt, shape, name)
+    _lib.check(_lib.lib.veda_trippool_project_score(
+        geom.c, stats_q.data_ptr(), stats_k.data_ptr(), w_q.data_ptr(), w_k.data_ptr(), int(r),
+        out["feat_q"].data_ptr(), out["feat_k"].data_ptr(), out["scores"].data_ptr(), _stream(stats_q)),
+        "veda_trippool_project_score")
     return out
 
 
@@ -250,16 +305,16 @@ def sparse_attn_fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, idx
 def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
                   geom: Geometry, k_per_head: Sequence[int], scale: Optional[float] = None,
                   buffers: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
-    """One Veda attention layer: permute Q/K/V, TripPool scores, Top-k mask,
+    """One Veda attention layer: permute Q/K/V (the TripPool statistics of Q
+    and K taken in the same pass), projections and tile scores, Top-k mask,
     tile-skipping attention, unpermute. `buffers` (from a previous call)
     reuses every output allocation. Returns all intermediates and `o`."""
     b = buffers if buffers is not None else {}
-    b["q_t"] = tile_permute(q, geom, b.get("q_t"))
-    b["k_t"] = tile_permute(k, geom, b.get("k_t"))
+    b["q_t"], b["stats_q"] = tile_permute_stats(q, geom, b.get("q_t"), b.get("stats_q"))
+    b["k_t"], b["stats_k"] = tile_permute_stats(k, geom, b.get("k_t"), b.get("stats_k"))
     b["v_t"] = tile_permute(v, geom, b.get("v_t"), layout=CHANNEL_MAJOR)
-    est = trippool_score(b["q_t"], b["k_t"], w_q, w_k, geom,
-                         {n: b[n] for n in ("stats_q", "stats_k", "feat_q", "feat_k", "scores")}
-                         if "scores" in b else None)
+    est = trippool_project_score(b["stats_q"], b["stats_k"], w_q, w_k, geom,
+                                 {n: b[n] for n in ("feat_q", "feat_k", "scores")} if "scores" in b else None)
     b.update(est)
     b["idx"], b["bitmask"] = topk_mask(b["scores"], geom, k_per_head, idx=b.get("idx"), bitmask=b.get("bitmask"))
     b["o_t"], b["lse"] = sparse_attn_fwd(b["q_t"], b["k_t"], b["v_t"], b["idx"], geom, k_per_head, scale,
@@ -465,9 +520,12 @@ def distill_train(q_t: torch.Tensor, k_t: torch.Tensor, teacher: torch.Tensor, w
     mq, vq, mk, vk = (torch.zeros_like(wq_m) for _ in range(4))
     rows = sum(geom.num_tiles(hd) for hd in range(geom.n_heads)) * geom.B
     losses = []
-    est, grads, kl, ds = None, None, None, None
+    est = trippool_score(q_t, k_t, wq_b, wk_b, geom)   # the statistics do not depend on W: taken once
+    grads, kl, ds = None, None, None
     for step in range(1, steps + 1):
-        est = trippool_score(q_t, k_t, wq_b, wk_b, geom, est)
+        if step > 1:
+            est.update(trippool_project_score(est["stats_q"], est["stats_k"], wq_b, wk_b, geom,
+                                              {n: est[n] for n in ("feat_q", "feat_k", "scores")}))
         kl, ds = distill_kl(est["scores"], teacher, geom, 1.0 / rows, kl, ds)
         grads = distill_grad(est, ds, geom, grads)
         adam_step(wq_m, grads["d_w_q"], mq, vq, step, lr, betas, eps, wq_b)

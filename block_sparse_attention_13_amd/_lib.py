@@ -26,7 +26,7 @@ STATUS = {
 EXPORTS = ["veda_status_str", "veda_num_tiles", "veda_max_tiles", "veda_tile_permute", "veda_trippool_score",
            "veda_topk_mask", "veda_sparse_attn_fwd", "veda_tile_unpermute", "veda_teacher_tile_max",
            "veda_mask_overlap", "veda_head_sq_error", "veda_distill_kl", "veda_distill_grad",
-           "veda_adam_step"]
+           "veda_adam_step", "veda_tile_permute_stats", "veda_trippool_project_score"]
 
 
 class VedaGrid(ctypes.Structure):
@@ -64,6 +64,12 @@ def _load():
     lib.veda_max_tiles.restype = ctypes.c_int
     lib.veda_tile_permute.argtypes = [POINTER(VedaGeom), c_void_p, VedaRasterStrides, c_void_p, c_int32, c_void_p]
     lib.veda_tile_permute.restype = ctypes.c_int
+    lib.veda_tile_permute_stats.argtypes = [POINTER(VedaGeom), c_void_p, VedaRasterStrides, c_void_p, c_void_p,
+                                            c_void_p]
+    lib.veda_tile_permute_stats.restype = ctypes.c_int
+    lib.veda_trippool_project_score.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                                c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.veda_trippool_project_score.restype = ctypes.c_int
     lib.veda_tile_unpermute.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, VedaRasterStrides, c_void_p]
     lib.veda_tile_unpermute.restype = ctypes.c_int
     lib.veda_trippool_score.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,

@@ -4,7 +4,8 @@
 // the attention kernel takes V channel-major so its tiles can be copied into
 // LDS as they are.
 //
-// Pure data movement, bound by HBM bandwidth. One workgroup moves one
+// Data movement, bound by HBM bandwidth (the Q/K variant also reduces each
+// tile to its TripPool statistics on the way). One workgroup moves one
 // 128-token box of one (batch, head): each token row is d bf16 values
 // (256 B for d = 128), moved as 16-byte vectors so that every wave touches
 // whole 256-byte segments on both sides. All loads of a thread are issued
@@ -58,6 +59,89 @@ __global__ __launch_bounds__(kThreads) void tile_permute_kernel(GeoTable g, cons
   }
 #pragma unroll
   for (int p = 0; p < M::kPasses; ++p) dst[(row0 + p * M::kRowsPerPass) * M::kChunks + chunk] = val[p];
+}
+
+// Token-major permute of Q or K fused with the TripPool statistics of each
+// tile (Veda page, "Attention Structure Distillation", Estimator: average,
+// maximum and minimum per tile; "Theoretical Rationale" 2): the tile is moved
+// as above and also kept in LDS, where threads 0..d-1 each sum one channel
+// over the real slots in slot order (fp32 from +0, then a correctly rounded
+// divide by the real-token count and a round to bf16) and threads d..2d-1
+// take that channel's maximum and minimum (IEEE total order, -0 below +0).
+// This spares a second pass over the tiled tensor.
+template <int D>
+__global__ __launch_bounds__(kThreads) void tile_permute_stats_kernel(GeoTable g, const uint16_t* __restrict__ x,
+                                                                     int64_t sb, int64_t sn, int64_t sh,
+                                                                     uint16_t* __restrict__ xt,
+                                                                     uint16_t* __restrict__ stats) {
+  using M = RowMap<D>;
+  static_assert(2 * D <= kThreads, "one thread per channel and statistic group");
+  __shared__ uint4 tile_s[VEDA_TILE_TOKENS * M::kChunks];
+  const int32_t tau = blockIdx.x, hd = blockIdx.y, b = blockIdx.z;
+  const HeadGeo hg = g.h[hd];
+  const int chunk = threadIdx.x % M::kChunks;
+  const int row0 = threadIdx.x / M::kChunks;
+  const int64_t tile_row = (int64_t(b) * g.heads + hd) * g.nT_max + tau;
+  uint4* dst = reinterpret_cast<uint4*>(xt + tile_row * VEDA_TILE_TOKENS * D);
+  uint16_t* st_out = stats + tile_row * 3 * D;
+  if (tau >= hg.nT) {  // tile beyond this head's grid: defined zeros
+#pragma unroll
+    for (int p = 0; p < M::kPasses; ++p) dst[(row0 + p * M::kRowsPerPass) * M::kChunks + chunk] = make_uint4(0, 0, 0, 0);
+    for (int c = threadIdx.x; c < 3 * D; c += kThreads) st_out[c] = 0;
+    return;
+  }
+  const BoxExtent e = box_extent(g, hg, tau);
+  const uint16_t* src = x + int64_t(b) * sb + int64_t(hd) * sh + chunk * 8;
+  uint4 val[M::kPasses];
+#pragma unroll
+  for (int p = 0; p < M::kPasses; ++p) {
+    const int64_t n = raster_of_slot(g, hg, e, row0 + p * M::kRowsPerPass);
+    val[p] = n >= 0 ? *reinterpret_cast<const uint4*>(src + n * sn) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int p = 0; p < M::kPasses; ++p) {
+    const int r = row0 + p * M::kRowsPerPass;
+    dst[r * M::kChunks + chunk] = val[p];
+    tile_s[r * M::kChunks + chunk] = val[p];
+  }
+  __syncthreads();
+
+  const int c = threadIdx.x % D;
+  const uint16_t* col = reinterpret_cast<const uint16_t*>(tile_s) + c;  // slot s of channel c at col[s * D]
+  const bool full = box_is_full(hg, e);
+  if (int(threadIdx.x) < D) {
+    float sum = 0.0f;
+    if (full) {
+#pragma unroll 16
+      for (int sl = 0; sl < VEDA_TILE_TOKENS; ++sl) sum = sum + bf16_to_f32(col[sl * D]);
+    } else {
+      for (int sl = 0; sl < VEDA_TILE_TOKENS; ++sl)
+        if (slot_is_real(hg, e, sl)) sum = sum + bf16_to_f32(col[sl * D]);
+    }
+    // sum / n in double then to float is the correctly rounded float quotient
+    // (53 >= 2*24 + 2, so the double rounding is innocuous).
+    const int32_t n_real = e.vt * e.vh * e.vw;
+    st_out[c] = f32_to_bf16_rne(float(double(sum) / double(n_real)));
+  } else if (int(threadIdx.x) < 2 * D) {
+    int32_t mx = -(1 << 20), mn = 1 << 20;
+    if (full) {
+#pragma unroll 16
+      for (int sl = 0; sl < VEDA_TILE_TOKENS; ++sl) {
+        const int32_t key = total_order_key(col[sl * D]);
+        mx = max(mx, key);
+        mn = min(mn, key);
+      }
+    } else {
+      for (int sl = 0; sl < VEDA_TILE_TOKENS; ++sl) {
+        if (!slot_is_real(hg, e, sl)) continue;
+        const int32_t key = total_order_key(col[sl * D]);
+        mx = max(mx, key);
+        mn = min(mn, key);
+      }
+    }
+    st_out[D + c] = from_total_order_key(mx);
+    st_out[2 * D + c] = from_total_order_key(mn);
+  }
 }
 
 // Channel-major tiles [.., d, 128]: each thread moves an 8-slot x 8-channel
@@ -142,6 +226,16 @@ hipError_t launch_tile_permute(const GeoTable& g, const uint16_t* x, int64_t sb,
     tile_permute_kernel<128><<<grid, kThreads, 0, s>>>(g, x, sb, sn, sh, xt);
   else
     tile_permute_kernel<64><<<grid, kThreads, 0, s>>>(g, x, sb, sn, sh, xt);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_permute_stats(const GeoTable& g, const uint16_t* x, int64_t sb, int64_t sn, int64_t sh,
+                                     uint16_t* xt, uint16_t* stats, hipStream_t s) {
+  const dim3 grid(g.nT_max, g.heads, g.B);
+  if (g.d == 128)
+    tile_permute_stats_kernel<128><<<grid, kThreads, 0, s>>>(g, x, sb, sn, sh, xt, stats);
+  else
+    tile_permute_stats_kernel<64><<<grid, kThreads, 0, s>>>(g, x, sb, sn, sh, xt, stats);
   return hipGetLastError();
 }
 

@@ -3,14 +3,16 @@
 // head-specific Q/K projections to tile scores; "Theoretical Rationale" 2,
 // "Tile Statistics").
 //
-// Two kernels:
+// Three kernels:
 //   trippool_features_kernel  one wave per tile: each lane owns d/64
 //     channels and walks the 128 slots in order (fp32 sum, total-order
 //     max/min over real slots); a wave load is one whole token row, so the
 //     stream from HBM is coalesced. The 3d statistics are staged in LDS and
 //     the same wave projects them with the head's W (held in LDS for the whole
-//     workgroup, 3 workgroups per CU): lane j owns output feature j and
+//     workgroup, 2 workgroups per CU at d = 128): lane j owns output feature j and
 //     accumulates over the 3d channels in order.
+//   trippool_project_kernel  the projection alone, from statistics that the
+//     fused permute (permute.hip) computed while it tiled Q and K.
 //   tile_scores_kernel  S = feat_q . feat_k^T per head, 128 x 128 outputs per
 //     workgroup, 8 x 8 per thread, fp32 accumulated over the r channels in order.
 // Every accumulation runs in a fixed ascending order with one rounding per
@@ -26,13 +28,16 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kTilesPerWave = 4;
 constexpr int kTilesPerBlock = kWaves * kTilesPerWave;
 
-// Order-preserving integer key of a bf16 value in the IEEE total order (-0 < +0).
-__device__ __forceinline__ int32_t total_order_key(uint32_t b) {
-  const int32_t mag = int32_t(b & 0x7FFFu);
-  return (b & 0x8000u) ? -mag - 1 : mag;
-}
-__device__ __forceinline__ uint16_t from_total_order_key(int32_t k) {
-  return k >= 0 ? uint16_t(k) : uint16_t(0x8000u | uint32_t(-k - 1));
+// Head-specific projection of one tile's statistics st[0..C): lane j < R
+// accumulates sum_c st[c] * W[c][j] in ascending c (fp32 FMA from +0; the
+// products of bf16 values are exact) and rounds the sum to bf16.
+template <int C, int R>
+__device__ __forceinline__ void project_tile(const float* st, const uint16_t* w_s, int lane, uint16_t* f_out) {
+  if (lane < R) {
+    float acc = 0.0f;
+    for (int c = 0; c < C; ++c) acc = __builtin_fmaf(st[c], bf16_to_f32(w_s[c * R + lane]), acc);
+    f_out[lane] = f32_to_bf16_rne(acc);
+  }
 }
 
 template <int D, int R>
@@ -131,15 +136,83 @@ __global__ __launch_bounds__(kThreads) void trippool_features_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // Projection: lane j < r accumulates sum_c st[c] * W[c][j] in ascending c.
-    if (lane < R) {
-      float acc = 0.0f;
-      for (int c = 0; c < C; ++c) acc = __builtin_fmaf(st_s[wave][c], bf16_to_f32(w_s[c * R + lane]), acc);
-      f_out[lane] = f32_to_bf16_rne(acc);
-    }
+    project_tile<C, R>(st_s[wave], w_s, lane, f_out);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+// Projections alone, from statistics already in HBM (written by the permute
+// that computes them on the fly). Lane i owns tile i of the workgroup's 256
+// and keeps all r sums of that tile in registers, so its r FMA chains run
+// side by side; every lane walks the 3d channels in the same ascending order,
+// reading W row c (the head's W sits in LDS) with uniform addresses, which
+// LDS broadcasts. Each sum still takes one channel at a time in ascending
+// order from +0, exactly as project_tile does.
+constexpr int kProjTiles = kThreads;
+
+template <int D, int R>
+__global__ __launch_bounds__(kThreads) void trippool_project_kernel(
+    GeoTable g, const uint16_t* __restrict__ stats_q, const uint16_t* __restrict__ stats_k,
+    const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wk, uint16_t* __restrict__ feat_q,
+    uint16_t* __restrict__ feat_k) {
+  constexpr int C = 3 * D;
+  __shared__ __attribute__((aligned(16))) uint16_t w_s[C * R];
+
+  const int hd = blockIdx.y;
+  const int side = blockIdx.z & 1;  // 0 = Q, 1 = K
+  const int b = blockIdx.z >> 1;
+  const HeadGeo hg = g.h[hd];
+  const uint16_t* stats = side ? stats_k : stats_q;
+  const uint16_t* w = (side ? wk : wq) + int64_t(hd) * C * R;
+  uint16_t* feat = side ? feat_k : feat_q;
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(w);
+    uint4* dst = reinterpret_cast<uint4*>(w_s);
+    for (int i = threadIdx.x; i < C * R / 8; i += kThreads) dst[i] = src[i];
+  }
+  __syncthreads();
+
+  const int32_t tau = blockIdx.x * kProjTiles + threadIdx.x;
+  const bool real = tau < hg.nT;
+  // Lanes past the head's tiles read tile 0's statistics (in bounds) and
+  // store zeros.
+  const int64_t row = (int64_t(b) * g.heads + hd) * g.nT_max + (real ? tau : 0);
+  const uint4* st = reinterpret_cast<const uint4*>(stats + row * C);
+  float acc[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) acc[j] = 0.0f;
+  for (int c8 = 0; c8 < C / 8; ++c8) {
+    const uint4 sv = st[c8];
+    const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      const float x = __uint_as_float((cc & 1) ? (sw[cc / 2] & 0xFFFF0000u) : (sw[cc / 2] << 16));
+      const uint4* wrow = reinterpret_cast<const uint4*>(w_s + (c8 * 8 + cc) * R);
+#pragma unroll
+      for (int j8 = 0; j8 < R / 8; ++j8) {
+        const uint4 wv = wrow[j8];
+        const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float wf = __uint_as_float((e & 1) ? (ww[e / 2] & 0xFFFF0000u) : (ww[e / 2] << 16));
+          acc[8 * j8 + e] = __builtin_fmaf(x, wf, acc[8 * j8 + e]);
+        }
+      }
+    }
+  }
+  if (tau >= g.nT_max) return;
+  uint4* out = reinterpret_cast<uint4*>(feat + ((int64_t(b) * g.heads + hd) * g.nT_max + tau) * R);
+#pragma unroll
+  for (int j8 = 0; j8 < R / 8; ++j8) {
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = real ? (uint32_t(f32_to_bf16_rne(acc[8 * j8 + 2 * e])) |
+                     (uint32_t(f32_to_bf16_rne(acc[8 * j8 + 2 * e + 1])) << 16))
+                  : 0u;
+    out[j8] = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -222,6 +295,21 @@ hipError_t launch_trippool_features(const GeoTable& g, const uint16_t* q_t, cons
     trippool_features_kernel<64, 64><<<grid, kThreads, 0, s>>>(g, q_t, k_t, wq, wk, stats_q, stats_k, feat_q, feat_k);
   else
     trippool_features_kernel<64, 32><<<grid, kThreads, 0, s>>>(g, q_t, k_t, wq, wk, stats_q, stats_k, feat_q, feat_k);
+  return hipGetLastError();
+}
+
+hipError_t launch_trippool_project(const GeoTable& g, const uint16_t* stats_q, const uint16_t* stats_k,
+                                   const uint16_t* wq, const uint16_t* wk, int32_t r, uint16_t* feat_q,
+                                   uint16_t* feat_k, hipStream_t s) {
+  const dim3 grid((g.nT_max + kProjTiles - 1) / kProjTiles, g.heads, 2 * g.B);
+  if (g.d == 128 && r == 64)
+    trippool_project_kernel<128, 64><<<grid, kThreads, 0, s>>>(g, stats_q, stats_k, wq, wk, feat_q, feat_k);
+  else if (g.d == 128 && r == 32)
+    trippool_project_kernel<128, 32><<<grid, kThreads, 0, s>>>(g, stats_q, stats_k, wq, wk, feat_q, feat_k);
+  else if (g.d == 64 && r == 64)
+    trippool_project_kernel<64, 64><<<grid, kThreads, 0, s>>>(g, stats_q, stats_k, wq, wk, feat_q, feat_k);
+  else
+    trippool_project_kernel<64, 32><<<grid, kThreads, 0, s>>>(g, stats_q, stats_k, wq, wk, feat_q, feat_k);
   return hipGetLastError();
 }
 

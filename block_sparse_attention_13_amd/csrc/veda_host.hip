@@ -149,6 +149,19 @@ int veda_tile_permute(const veda_geom* g, const void* x_raster, veda_raster_stri
                                             static_cast<hipStream_t>(stream)));
 }
 
+int veda_tile_permute_stats(const veda_geom* g, const void* x_raster, veda_raster_strides s, void* x_tiled,
+                            void* stats, void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!x_raster || !x_tiled || !stats) return VEDA_ERR_NULL;
+  if (!aligned16(x_raster) || !aligned16(x_tiled) || !aligned16(stats)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_strides(s));
+  VEDA_TRY(check_device());
+  return launched(veda::launch_tile_permute_stats(t, static_cast<const uint16_t*>(x_raster), s.b, s.n, s.h,
+                                                  static_cast<uint16_t*>(x_tiled), static_cast<uint16_t*>(stats),
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 int veda_tile_unpermute(const veda_geom* g, const void* x_tiled, void* x_raster, veda_raster_strides s,
                         void* stream) {
   GeoTable t;
@@ -180,6 +193,26 @@ int veda_trippool_score(const veda_geom* g, const void* q_tiled, const void* k_t
       t, static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_tiled),
       static_cast<const uint16_t*>(w_q), static_cast<const uint16_t*>(w_k), rank, static_cast<uint16_t*>(stats_q),
       static_cast<uint16_t*>(stats_k), static_cast<uint16_t*>(feat_q), static_cast<uint16_t*>(feat_k), st)));
+  return launched(veda::launch_tile_scores(t, static_cast<const uint16_t*>(feat_q),
+                                           static_cast<const uint16_t*>(feat_k), rank, scores, st));
+}
+
+int veda_trippool_project_score(const veda_geom* g, const void* stats_q, const void* stats_k, const void* w_q,
+                                const void* w_k, int32_t rank, void* feat_q, void* feat_k, float* scores,
+                                void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!stats_q || !stats_k || !w_q || !w_k || !feat_q || !feat_k || !scores) return VEDA_ERR_NULL;
+  if (rank != 32 && rank != 64) return VEDA_ERR_SHAPE;
+  for (const void* p : {stats_q, stats_k, w_q, w_k, static_cast<const void*>(feat_q),
+                        static_cast<const void*>(feat_k), static_cast<const void*>(scores)})
+    if (!aligned16(p)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_device());
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  VEDA_TRY(launched(veda::launch_trippool_project(
+      t, static_cast<const uint16_t*>(stats_q), static_cast<const uint16_t*>(stats_k),
+      static_cast<const uint16_t*>(w_q), static_cast<const uint16_t*>(w_k), rank, static_cast<uint16_t*>(feat_q),
+      static_cast<uint16_t*>(feat_k), st)));
   return launched(veda::launch_tile_scores(t, static_cast<const uint16_t*>(feat_q),
                                            static_cast<const uint16_t*>(feat_k), rank, scores, st));
 }

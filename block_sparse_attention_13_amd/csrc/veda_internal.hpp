@@ -94,14 +94,28 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return uint16_t(u >> 16);
 }
 
+// Order-preserving integer key of a bf16 value in the IEEE total order (-0 < +0).
+__device__ __forceinline__ int32_t total_order_key(uint32_t b) {
+  const int32_t mag = int32_t(b & 0x7FFFu);
+  return (b & 0x8000u) ? -mag - 1 : mag;
+}
+__device__ __forceinline__ uint16_t from_total_order_key(int32_t k) {
+  return k >= 0 ? uint16_t(k) : uint16_t(0x8000u | uint32_t(-k - 1));
+}
+
 // Host-side launchers, one per kernel family (each defined next to its kernel).
 hipError_t launch_tile_permute(const GeoTable& g, const uint16_t* x, int64_t sb, int64_t sn, int64_t sh,
                                uint16_t* xt, bool channel_major, hipStream_t s);
+hipError_t launch_tile_permute_stats(const GeoTable& g, const uint16_t* x, int64_t sb, int64_t sn, int64_t sh,
+                                     uint16_t* xt, uint16_t* stats, hipStream_t s);
 hipError_t launch_tile_unpermute(const GeoTable& g, const uint16_t* xt, uint16_t* x, int64_t sb, int64_t sn,
                                  int64_t sh, hipStream_t s);
 hipError_t launch_trippool_features(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t,
                                     const uint16_t* wq, const uint16_t* wk, int32_t r, uint16_t* stats_q,
                                     uint16_t* stats_k, uint16_t* feat_q, uint16_t* feat_k, hipStream_t s);
+hipError_t launch_trippool_project(const GeoTable& g, const uint16_t* stats_q, const uint16_t* stats_k,
+                                   const uint16_t* wq, const uint16_t* wk, int32_t r, uint16_t* feat_q,
+                                   uint16_t* feat_k, hipStream_t s);
 hipError_t launch_tile_scores(const GeoTable& g, const uint16_t* feat_q, const uint16_t* feat_k, int32_t r,
                               float* scores, hipStream_t s);
 hipError_t launch_topk(const GeoTable& g, const float* scores, int32_t k_max, int32_t* idx, uint32_t* bitmask,

@@ -11,6 +11,11 @@
  *   veda_sparse_attn_fwd       flash-attention forward over the selected K/V tiles only
  *   veda_tile_unpermute        tiled O -> raster O
  *
+ * The same layer in fewer passes over HBM, with identical results:
+ *   veda_tile_permute_stats    x2  raster Q/K -> tiles and each tile's TripPool stats in one pass
+ *   veda_trippool_project_score    stats -> head-specific projections -> tile scores
+ *   (then veda_tile_permute of V, veda_topk_mask, veda_sparse_attn_fwd, veda_tile_unpermute)
+ *
  * Two more calls measure the mask against the method's own target:
  *   veda_teacher_tile_max      max-pooled dense attention per (query tile, key tile); its
  *                              veda_topk_mask is the oracle tile mask
@@ -130,6 +135,22 @@ int veda_tile_permute(const veda_geom* g, const void* x_raster, veda_raster_stri
                       void* x_tiled, int32_t layout, void* stream);
 
 /*
+ * Token-major re-tiling of Q or K fused with the TripPool statistics of each
+ * tile (Veda page, "Architecture", Principle 02 "Head-Conditioned Tile
+ * Geometry"; "Attention Structure Distillation", Estimator: average, maximum
+ * and minimum per tile). One pass over the raster tensor writes both outputs:
+ *   x_raster  in   raster bf16 tensor, strides `s` (elements)
+ *   x_tiled   out  bf16 [B, heads, nT_max, 128, d], exactly as veda_tile_permute with
+ *                  VEDA_TILED_TOKEN_MAJOR writes it
+ *   stats     out  bf16 [B, heads, nT_max, 3d], exactly the stats_q (or stats_k) that
+ *                  veda_trippool_score computes from x_tiled (0 for tiles >= nT_hd)
+ * Errors: a null pointer (VEDA_ERR_NULL), a pointer not 16-byte aligned or a stride not a
+ * multiple of 8 (VEDA_ERR_ALIGN), and the geometry checks of every call.
+ */
+int veda_tile_permute_stats(const veda_geom* g, const void* x_raster, veda_raster_strides s,
+                            void* x_tiled, void* stats, void* stream);
+
+/*
  * TripPool estimator (Veda page, "Attention Structure Distillation",
  * Estimator: average, maximum and minimum per tile, then head-specific Q/K
  * projections score each query-tile x key-tile pair; "Theoretical
@@ -150,6 +171,22 @@ int veda_trippool_score(const veda_geom* g, const void* q_tiled, const void* k_t
                         const void* w_q, const void* w_k, int32_t rank,
                         void* stats_q, void* stats_k, void* feat_q, void* feat_k,
                         float* scores, void* stream);
+
+/*
+ * The projection and scoring half of veda_trippool_score, from statistics
+ * already computed (by veda_tile_permute_stats of Q and of K). Same page and
+ * passage as veda_trippool_score.
+ *   stats_q, stats_k  in   bf16 [B, heads, nT_max, 3d], [avg | max | min]
+ *   w_q, w_k          in   bf16 [heads, 3d, rank]
+ *   rank              in   r: 32 or 64 (else VEDA_ERR_SHAPE)
+ *   feat_q, feat_k    out  bf16 [B, heads, nT_max, rank], as veda_trippool_score
+ *   scores            out  fp32 [B, heads, nT_max, nT_max], as veda_trippool_score
+ * Given the statistics veda_trippool_score would compute, the outputs are
+ * identical to its outputs, bit for bit.
+ */
+int veda_trippool_project_score(const veda_geom* g, const void* stats_q, const void* stats_k,
+                                const void* w_q, const void* w_k, int32_t rank,
+                                void* feat_q, void* feat_k, float* scores, void* stream);
 
 /*
  * Head-aware Top-k tile mask (Veda page, "Attention Structure Distillation",

@@ -21,7 +21,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     from block_sparse_attention_13_amd import _lib
     declared = _declared_functions()
-    assert len(declared) == 14, declared
+    assert len(declared) == 16, declared
     assert sorted(_lib.EXPORTS) == declared
     for name in declared:
         assert hasattr(_lib.lib, name), name
@@ -88,6 +88,13 @@ def test_call_errors_precede_any_device_work():
     assert L.veda_tile_permute(g.c, FAKE, s, FAKE, 2, None) == -2
     assert L.veda_tile_permute(g.c, FAKE, s, FAKE, -1, None) == -2
     assert L.veda_tile_unpermute(g.c, FAKE, None, s, None) == -1
+    assert L.veda_tile_permute_stats(g.c, FAKE, s, FAKE, None, None) == -1
+    assert L.veda_tile_permute_stats(g.c, FAKE, s, FAKE, FAKE + 8, None) == -5
+    assert L.veda_tile_permute_stats(g.c, FAKE, _lib.VedaRasterStrides(1024, 128, 132), FAKE, FAKE, None) == -5
+    assert L.veda_tile_permute_stats(_geom(d=96).c, FAKE, s, FAKE, FAKE, None) == -2
+    assert L.veda_trippool_project_score(g.c, FAKE, FAKE, FAKE, FAKE, 16, FAKE, FAKE, FAKE, None) == -2
+    assert L.veda_trippool_project_score(g.c, FAKE, None, FAKE, FAKE, 64, FAKE, FAKE, FAKE, None) == -1
+    assert L.veda_trippool_project_score(g.c, FAKE, FAKE, FAKE, FAKE, 32, FAKE, FAKE, FAKE + 4, None) == -5
     ks = _lib.int_array([3])
     assert L.veda_trippool_score(g.c, FAKE, FAKE, FAKE, FAKE, 48, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2
     assert L.veda_trippool_score(g.c, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, None, FAKE, None) == -1
@@ -127,6 +134,8 @@ def test_valid_call_without_gpu_reports_device_error():
     g = _geom()
     s = _lib.VedaRasterStrides(8 * 16 * 128, 128, 128)
     assert _lib.lib.veda_tile_permute(g.c, FAKE, s, FAKE, _lib.VEDA_TILED_CHANNEL_MAJOR, None) == -6
+    assert _lib.lib.veda_tile_permute_stats(g.c, FAKE, s, FAKE, FAKE, None) == -6
+    assert _lib.lib.veda_trippool_project_score(g.c, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, None) == -6
 
 
 def test_python_wrappers_validate_before_calling():

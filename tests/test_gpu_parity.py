@@ -158,6 +158,42 @@ def test_unpermute_inverts_permute_with_strided_raster():
     torch.cuda.synchronize()
     assert xc.shape == (w.B, w.heads, g.max_tiles(), w.d, 128)
     assert torch.equal(xc.view(torch.int16), xt.transpose(3, 4).contiguous().view(torch.int16))
+    # the one-pass permute + statistics on the same strided input
+    xs, st = V.tile_permute_stats(x, g)
+    wz = torch.zeros((w.heads, 3 * w.d, 64), dtype=torch.bfloat16, device="cuda")
+    two = V.trippool_score(xt, xt, wz, wz, g)
+    torch.cuda.synchronize()
+    assert torch.equal(xs.view(torch.int16), xt.view(torch.int16))
+    assert torch.equal(st.view(torch.int16), two["stats_q"].view(torch.int16))
+
+
+@pytest.mark.parametrize("wname,heads,B,custom", [
+    ("hc", 6, 2, None),                                            # three tile shapes, ragged boxes
+    ("tiny", None, 1, None),                                       # d = 64, r = 32
+    (None, None, 1, ((3, 9, 17), [(1, 8, 16), (8, 4, 4)], 64, 64)),  # d = 64, r = 64, mostly pad
+])
+def test_one_pass_estimator_matches_two_pass(wname, heads, B, custom):
+    """layer_forward takes the statistics while it permutes Q and K
+    (tile_permute_stats + trippool_project_score); the two-pass route
+    (tile_permute + trippool_score) must give the same bytes."""
+    V = _lib()
+    if custom is None:
+        w = W[wname] if heads is None else W[wname].with_heads(heads)
+        w = dataclasses.replace(w, B=B)
+    else:
+        grid, tiles, d, r = custom
+        w = _random_workload(grid, tiles, d, r, heads=2 * len(tiles), seed=5, k=1)
+    say(f"[one-pass] {w.description} B {w.B}")
+    data = datagen.generate(w)
+    geom, out, (q, k, v, wq, wk) = run_layer(w, data)
+    q_t, k_t = V.tile_permute(q, geom), V.tile_permute(k, geom)
+    two = V.trippool_score(q_t, k_t, wq, wk, geom)
+    torch.cuda.synchronize()
+    assert torch.equal(out["q_t"].view(torch.int16), q_t.view(torch.int16))
+    assert torch.equal(out["k_t"].view(torch.int16), k_t.view(torch.int16))
+    for name in ("stats_q", "stats_k", "feat_q", "feat_k"):
+        assert torch.equal(out[name].view(torch.int16), two[name].view(torch.int16)), name
+    assert torch.equal(out["scores"].view(torch.int32), two["scores"].view(torch.int32))
 
 
 def _random_workload(grid, tiles, d, r, heads, seed, keep=None, k=None):
