@@ -172,8 +172,9 @@ __device__ __forceinline__ u32x4 v_frag(const uint16_t* vs, int t, int half, int
 // step, one LDS-DMA chunk, so the VALU work and the copies run while the
 // matrix core is busy and no burst of copies fills the vector-memory queue.
 // The PV MFMAs of this tile follow, their V^T reads kLook steps ahead.
-// Scheduling fences keep each step's instructions together.
-template <int D>
+// Scheduling fences keep each step's instructions together. The last
+// iteration (kLast) has no next tile: it issues no QK^T MFMAs and no copies.
+template <int D, bool kLast>
 __device__ __forceinline__ void hot_tile(WaveState<D>& w, const floatx16 (&s_cur)[2], floatx16 (&s_next)[2],
                                          const uint16_t* ks_next, const uint16_t* vs_cur, const DmaPlan<D>& pl,
                                          uint32_t dma_tile_bytes, lds_u16* dma_dst, int half, int h, int l32,
@@ -192,13 +193,15 @@ __device__ __forceinline__ void hot_tile(WaveState<D>& w, const floatx16 (&s_cur
   float psum = 0.0f;
   u32x4 pf[2][2];
   u32x4 kf[kS];
+  if constexpr (!kLast) {
 #pragma unroll
-  for (int t = 0; t < kLook && t < kS; ++t) kf[t] = k_frag<D>(ks_next, t, half, h, l32);
+    for (int t = 0; t < kLook && t < kS; ++t) kf[t] = k_frag<D>(ks_next, t, half, h, l32);
+  }
   const floatx16 zero = {};
 #pragma unroll
   for (int t = 0; t < kSteps; ++t) {
-    if (t + kLook < kS) kf[t + kLook] = k_frag<D>(ks_next, t + kLook, half, h, l32);
-    if (t < kS) {
+    if (!kLast && t + kLook < kS) kf[t + kLook] = k_frag<D>(ks_next, t + kLook, half, h, l32);
+    if (!kLast && t < kS) {
       const int kb = t / S::kDC, dc = t % S::kDC;
       s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[t]), as_bf16x8(w.qf[dc]),
                                                            dc == 0 ? zero : s_next[kb], 0, 0, 0);
@@ -210,7 +213,7 @@ __device__ __forceinline__ void hot_tile(WaveState<D>& w, const floatx16 (&s_cur
       psum += p0 + p1;
       pf[kb][v / 8][(v % 8) / 2] = pack_bf16x2(p0, p1);
     }
-    if (t % 2 == 1 && t / 2 < S::kChunksPerWave)
+    if (!kLast && t % 2 == 1 && t / 2 < S::kChunksPerWave)
       dma_copy(pl.base, pl.bytes, pl.off[(t / 2) % 4], dma_tile_bytes + 4096u * (t / 8), dma_dst + (pl.first + t / 2) * 512);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -305,27 +308,39 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
   __syncthreads();  // every wave has read lds[0] before tile 2 lands there
 
   // One pipelined iteration: s_cur holds S of tile i, s_next receives S of
-  // tile i+1 (computed unconditionally; after the last tile it is unused).
-  auto iteration = [&](int i, floatx16 (&s_cur)[2], floatx16 (&s_next)[2]) {
+  // tile i+1 (except in the last iteration, `last` = true_type, which only
+  // finishes tile i).
+  auto iteration = [&](auto last, int i, floatx16 (&s_cur)[2], floatx16 (&s_next)[2]) {
+    constexpr bool kLast = decltype(last)::value;
     const int cur = i & 1;
     softmax_max<D>(w, s_cur, real_key_bits(g, hg, j, half, h), scale_log2);
     // K of tile i+2 into lds[cur] (K of tile i, read in the previous
     // iteration) or V of tile i+1 into lds[2 + (cur ^ 1)] (V of tile i-1).
-    hot_tile<D>(w, s_cur, s_next, lds[cur ^ 1], lds[2 + cur], plan, tile_src(plan.is_k ? jn2 : jn),
-                lbuf + (plan.is_k ? cur : 2 + (cur ^ 1)) * S::kTileElems, half, h, l32, scale_log2);
-    j = jn;
-    jn = jn2;
-    jn2 = sel[min(i + 3, kh - 1)];
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies and the next index have landed
-    __syncthreads();
+    hot_tile<D, kLast>(w, s_cur, s_next, lds[cur ^ 1], lds[2 + cur], plan, tile_src(plan.is_k ? jn2 : jn),
+                       lbuf + (plan.is_k ? cur : 2 + (cur ^ 1)) * S::kTileElems, half, h, l32, scale_log2);
+    if constexpr (!kLast) {
+      j = jn;
+      jn = jn2;
+      jn2 = sel[min(i + 3, kh - 1)];
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies and the next index have landed
+      __syncthreads();
+    }
   };
+  const std::false_type more{};
+  const std::true_type last{};
   floatx16 sn[2];
   int i = 0;
-  for (; i + 1 < kh; i += 2) {
-    iteration(i, sc, sn);
-    iteration(i + 1, sn, sc);
+  for (; i + 2 < kh; i += 2) {
+    iteration(more, i, sc, sn);
+    iteration(more, i + 1, sn, sc);
   }
-  if (i < kh) iteration(i, sc, sn);
+  if (i + 1 < kh) {
+    iteration(more, i, sc, sn);
+    iteration(last, i + 1, sn, sc);
+  } else {
+    iteration(last, i, sc, sn);
+  }
+  __syncthreads();  // every wave is done with the tile buffers
 
   // Merge the two key halves through LDS (the tile buffers are free now):
   // m = max(m0, m1), O = O0 2^(m0-m) + O1 2^(m1-m), l likewise.

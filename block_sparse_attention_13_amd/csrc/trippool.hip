@@ -144,20 +144,20 @@ __global__ __launch_bounds__(kThreads) void trippool_features_kernel(
 }
 
 // Projections alone, from statistics already in HBM (written by the permute
-// that computes them on the fly). Lane i owns tile i of the workgroup's 256
-// and keeps all r sums of that tile in registers, so its r FMA chains run
-// side by side; every lane walks the 3d channels in the same ascending order,
-// reading W row c (the head's W sits in LDS) with uniform addresses, which
-// LDS broadcasts. Each sum still takes one channel at a time in ascending
-// order from +0, exactly as project_tile does.
-constexpr int kProjTiles = kThreads;
-
+// that computes them on the fly). r/8 lanes share a tile; each owns 8 of its
+// r outputs and keeps their sums in registers, so 8 FMA chains run side by
+// side in every lane. All lanes walk the 3d channels in the same ascending
+// order and read their 16 bytes of W row c from LDS (the lanes of a wave
+// read one contiguous row, free of bank conflicts). Each sum still takes one
+// channel at a time in ascending order from +0, exactly as project_tile.
 template <int D, int R>
 __global__ __launch_bounds__(kThreads) void trippool_project_kernel(
     GeoTable g, const uint16_t* __restrict__ stats_q, const uint16_t* __restrict__ stats_k,
     const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wk, uint16_t* __restrict__ feat_q,
     uint16_t* __restrict__ feat_k) {
   constexpr int C = 3 * D;
+  constexpr int kGroups = R / 8;                     // lanes per tile
+  constexpr int kTilesPerBlock = kThreads / kGroups;
   __shared__ __attribute__((aligned(16))) uint16_t w_s[C * R];
 
   const int hd = blockIdx.y;
@@ -174,46 +174,38 @@ __global__ __launch_bounds__(kThreads) void trippool_project_kernel(
   }
   __syncthreads();
 
-  const int32_t tau = blockIdx.x * kProjTiles + threadIdx.x;
+  const int grp = threadIdx.x % kGroups;
+  const int32_t tau = blockIdx.x * kTilesPerBlock + threadIdx.x / kGroups;
   const bool real = tau < hg.nT;
   // Lanes past the head's tiles read tile 0's statistics (in bounds) and
   // store zeros.
-  const int64_t row = (int64_t(b) * g.heads + hd) * g.nT_max + (real ? tau : 0);
-  const uint4* st = reinterpret_cast<const uint4*>(stats + row * C);
-  float acc[R];
+  const int64_t head_row = (int64_t(b) * g.heads + hd) * g.nT_max;
+  const uint4* st = reinterpret_cast<const uint4*>(stats + (head_row + (real ? tau : 0)) * C);
+  const uint16_t* wcol = w_s + 8 * grp;
+  float acc[8];
 #pragma unroll
-  for (int j = 0; j < R; ++j) acc[j] = 0.0f;
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
   for (int c8 = 0; c8 < C / 8; ++c8) {
     const uint4 sv = st[c8];
     const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
       const float x = __uint_as_float((cc & 1) ? (sw[cc / 2] & 0xFFFF0000u) : (sw[cc / 2] << 16));
-      const uint4* wrow = reinterpret_cast<const uint4*>(w_s + (c8 * 8 + cc) * R);
+      const uint4 wv = *reinterpret_cast<const uint4*>(wcol + (c8 * 8 + cc) * R);
+      const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-      for (int j8 = 0; j8 < R / 8; ++j8) {
-        const uint4 wv = wrow[j8];
-        const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float wf = __uint_as_float((e & 1) ? (ww[e / 2] & 0xFFFF0000u) : (ww[e / 2] << 16));
-          acc[8 * j8 + e] = __builtin_fmaf(x, wf, acc[8 * j8 + e]);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float wf = __uint_as_float((e & 1) ? (ww[e / 2] & 0xFFFF0000u) : (ww[e / 2] << 16));
+        acc[e] = __builtin_fmaf(x, wf, acc[e]);
       }
     }
   }
   if (tau >= g.nT_max) return;
-  uint4* out = reinterpret_cast<uint4*>(feat + ((int64_t(b) * g.heads + hd) * g.nT_max + tau) * R);
+  uint32_t o[4];
 #pragma unroll
-  for (int j8 = 0; j8 < R / 8; ++j8) {
-    uint32_t o[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      o[e] = real ? (uint32_t(f32_to_bf16_rne(acc[8 * j8 + 2 * e])) |
-                     (uint32_t(f32_to_bf16_rne(acc[8 * j8 + 2 * e + 1])) << 16))
-                  : 0u;
-    out[j8] = make_uint4(o[0], o[1], o[2], o[3]);
-  }
+  for (int e = 0; e < 4; ++e)
+    o[e] = real ? (uint32_t(f32_to_bf16_rne(acc[2 * e])) | (uint32_t(f32_to_bf16_rne(acc[2 * e + 1])) << 16)) : 0u;
+  *reinterpret_cast<uint4*>(feat + (head_row + tau) * R + 8 * grp) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 constexpr int kScoreTile = 128;   // scores per workgroup: 128 x 128, 8 x 8 per thread
@@ -301,7 +293,8 @@ hipError_t launch_trippool_features(const GeoTable& g, const uint16_t* q_t, cons
 hipError_t launch_trippool_project(const GeoTable& g, const uint16_t* stats_q, const uint16_t* stats_k,
                                    const uint16_t* wq, const uint16_t* wk, int32_t r, uint16_t* feat_q,
                                    uint16_t* feat_k, hipStream_t s) {
-  const dim3 grid((g.nT_max + kProjTiles - 1) / kProjTiles, g.heads, 2 * g.B);
+  const int tiles_per_block = kThreads / (r / 8);
+  const dim3 grid((g.nT_max + tiles_per_block - 1) / tiles_per_block, g.heads, 2 * g.B);
   if (g.d == 128 && r == 64)
     trippool_project_kernel<128, 64><<<grid, kThreads, 0, s>>>(g, stats_q, stats_k, wq, wk, feat_q, feat_k);
   else if (g.d == 128 && r == 32)
