@@ -17,6 +17,21 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Streaming (non-temporal) 16-byte loads and stores: every byte is touched
+// once here and the tensors are far larger than L2 and MALL, so nothing is
+// gained by keeping them there. Measured on the 245,760-token layer they move
+// the gathers 4-10% closer to HBM bandwidth; the channel-major permute keeps
+// ordinary loads (its eight-row reads per thread ran slower streamed).
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  const u32x4_nt x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ void store_stream(void* p, uint4 v) {
+  const u32x4_nt x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x4_nt*>(p));
+}
+
 template <int D>
 struct RowMap {
   static constexpr int kChunks = D / 8;                 // 16-byte chunks per token row
@@ -51,14 +66,14 @@ __global__ __launch_bounds__(kThreads) void tile_permute_kernel(GeoTable g, cons
 #pragma unroll
     for (int p = 0; p < M::kPasses; ++p) {
       const int64_t n = raster_of_slot(g, hg, e, row0 + p * M::kRowsPerPass);
-      val[p] = n >= 0 ? *reinterpret_cast<const uint4*>(src + n * sn) : make_uint4(0, 0, 0, 0);
+      val[p] = n >= 0 ? load_stream(src + n * sn) : make_uint4(0, 0, 0, 0);
     }
   } else {
 #pragma unroll
     for (int p = 0; p < M::kPasses; ++p) val[p] = make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
-  for (int p = 0; p < M::kPasses; ++p) dst[(row0 + p * M::kRowsPerPass) * M::kChunks + chunk] = val[p];
+  for (int p = 0; p < M::kPasses; ++p) store_stream(&dst[(row0 + p * M::kRowsPerPass) * M::kChunks + chunk], val[p]);
 }
 
 // Token-major permute of Q or K fused with the TripPool statistics of each
@@ -96,12 +111,12 @@ __global__ __launch_bounds__(kThreads) void tile_permute_stats_kernel(GeoTable g
 #pragma unroll
   for (int p = 0; p < M::kPasses; ++p) {
     const int64_t n = raster_of_slot(g, hg, e, row0 + p * M::kRowsPerPass);
-    val[p] = n >= 0 ? *reinterpret_cast<const uint4*>(src + n * sn) : make_uint4(0, 0, 0, 0);
+    val[p] = n >= 0 ? load_stream(src + n * sn) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int p = 0; p < M::kPasses; ++p) {
     const int r = row0 + p * M::kRowsPerPass;
-    dst[r * M::kChunks + chunk] = val[p];
+    store_stream(&dst[r * M::kChunks + chunk], val[p]);
     tile_s[r * M::kChunks + chunk] = val[p];
   }
   __syncthreads();
@@ -182,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void tile_permute_cm_kernel(GeoTable g, c
       const uint32_t a = w[(2 * p) * 4 + i / 2], c = w[(2 * p + 1) * 4 + i / 2];
       o[p] = (i & 1) ? ((a >> 16) | (c & 0xFFFF0000u)) : ((a & 0xFFFFu) | (c << 16));
     }
-    *reinterpret_cast<uint4*>(dst + (8 * cg + i) * VEDA_TILE_TOKENS + 8 * sg) = make_uint4(o[0], o[1], o[2], o[3]);
+    store_stream(dst + (8 * cg + i) * VEDA_TILE_TOKENS + 8 * sg, make_uint4(o[0], o[1], o[2], o[3]));
   }
 }
 
@@ -201,12 +216,12 @@ __global__ __launch_bounds__(kThreads) void tile_unpermute_kernel(GeoTable g, co
   const BoxExtent e = box_extent(g, hg, tau);
   uint4 val[M::kPasses];
 #pragma unroll
-  for (int p = 0; p < M::kPasses; ++p) val[p] = src[(row0 + p * M::kRowsPerPass) * M::kChunks + chunk];
+  for (int p = 0; p < M::kPasses; ++p) val[p] = load_stream(&src[(row0 + p * M::kRowsPerPass) * M::kChunks + chunk]);
   uint16_t* dst = x + int64_t(b) * sb + int64_t(hd) * sh + chunk * 8;
 #pragma unroll
   for (int p = 0; p < M::kPasses; ++p) {
     const int64_t n = raster_of_slot(g, hg, e, row0 + p * M::kRowsPerPass);
-    if (n >= 0) *reinterpret_cast<uint4*>(dst + n * sn) = val[p];
+    if (n >= 0) store_stream(dst + n * sn, val[p]);
   }
 }
 
