@@ -5,9 +5,10 @@
 // One wave per row (b, head, query tile). Each score becomes a 32-bit key
 // whose unsigned order is the float order (-0 is first made +0, so signed
 // zeros tie). The row's keys stay in registers (chunk i, lane l holds key
-// tile j = 64*i + l). A bitwise search from the top bit finds the k-th
-// largest key t; then one ascending pass over the chunks keeps every key > t
-// and the lowest-indexed keys == t until k are kept, which is exactly the
+// tile j = 64*i + l). A bitwise search from the top bit finds a threshold t:
+// the k-th largest key, or (stopping early) any t with exactly k keys >= t.
+// One ascending pass over the chunks then keeps every key > t and the
+// lowest-indexed keys == t until k are kept, which is exactly the
 // lower-index tie rule. Ballots give output positions and bitmask words.
 #include "veda_internal.hpp"
 
@@ -70,14 +71,20 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(GeoTable g, const float*
     const int j = i * 64 + lane;
     key[i] = j < n ? order_key(s[j]) : 0u;  // 0 lies below every finite score's key
   }
-  // Largest t with #{key >= t} >= k: the k-th largest key.
+  // Largest t with #{key >= t} >= k: the k-th largest key. The search may
+  // stop early at a t with exactly k keys >= t; those k keys are then the
+  // k largest, and the selection below keeps exactly them.
   uint32_t t = 0u;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = t | (1u << bit);
     int c = 0;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) c += key[i] >= cand;
-    if (wave_sum(c) >= k) t = cand;
+    const int total = wave_sum(c);  // wave-uniform
+    if (total >= k) {
+      t = cand;
+      if (total == k) break;
+    }
   }
   int c_gt = 0;
 #pragma unroll

@@ -223,11 +223,20 @@ __global__ __launch_bounds__(kThreads) void tile_scores_kernel(GeoTable g, const
   const int i0 = blockIdx.x / nb * kScoreTile;
   const int j0 = blockIdx.x % nb * kScoreTile;
   const int64_t head_row = (int64_t(b) * g.heads + hd) * g.nT_max;
-  for (int e = threadIdx.x; e < kScoreTile * R; e += kThreads) {
-    const int r = e / R, c = e % R;
+  // Stage both sides as fp32, transposed to [channel][row]; each thread
+  // reads 8 features (16 bytes) of a row at a time.
+  for (int e = threadIdx.x; e < kScoreTile * R / 8; e += kThreads) {
+    const int r = e / (R / 8), c0 = (e % (R / 8)) * 8;
     const int i = i0 + r, j = j0 + r;
-    fq_s[c][r] = i < hg.nT ? bf16_to_f32(feat_q[(head_row + i) * R + c]) : 0.0f;
-    fk_s[c][r] = j < hg.nT ? bf16_to_f32(feat_k[(head_row + j) * R + c]) : 0.0f;
+    const uint4 zero4 = make_uint4(0, 0, 0, 0);
+    const uint4 qa = i < hg.nT ? *reinterpret_cast<const uint4*>(feat_q + (head_row + i) * R + c0) : zero4;
+    const uint4 ka = j < hg.nT ? *reinterpret_cast<const uint4*>(feat_k + (head_row + j) * R + c0) : zero4;
+    const uint32_t qw[4] = {qa.x, qa.y, qa.z, qa.w}, kw[4] = {ka.x, ka.y, ka.z, ka.w};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      fq_s[c0 + u][r] = __uint_as_float((u & 1) ? (qw[u / 2] & 0xFFFF0000u) : (qw[u / 2] << 16));
+      fk_s[c0 + u][r] = __uint_as_float((u & 1) ? (kw[u / 2] & 0xFFFF0000u) : (kw[u / 2] << 16));
+    }
   }
   __syncthreads();
   const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
