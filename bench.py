@@ -5,8 +5,9 @@ A step is the whole layer on one batch of seeded synthetic input already
 resident in HBM: tile permute of Q, K and V, the Q and K permutes also
 taking each tile's TripPool statistics (stage "permute_x3"); head-specific
 projections and tile scores ("project_score"); head-aware Top-k;
-tile-skipping attention forward; tile unpermute of O. Default workload: 245,760 tokens (64x48x80 latents),
-40 heads, d = 128, tile (4,4,8) -> 1920 tiles, k = 96 (95% sparse).
+tile-skipping attention forward, which writes O back in raster order itself
+(no separate unpermute pass). Default workload: 245,760 tokens (64x48x80
+latents), 40 heads, d = 128, tile (4,4,8) -> 1920 tiles, k = 96 (95% sparse).
 
 Prints one JSON line: ms per layer (the value), the attention kernel's
 effective TFLOP/s against the bf16 MFMA peak (roofline), per-stage times
@@ -80,7 +81,7 @@ def layer_floor(w, stage_ms: dict) -> dict:
     sb = stage_bytes(w)
     sb["sparse_attn"] = attention_bytes(w)
     fl = {"permute_x3": 0.0, "project_score": estimator_flops(w) / PEAK_FP32_VALU_TFLOPS,
-          "topk": 0.0, "sparse_attn": attention_flops(w) / PEAK_BF16_TFLOPS, "unpermute": 0.0}
+          "topk": 0.0, "sparse_attn": attention_flops(w) / PEAK_BF16_TFLOPS}
     floor = {n: max(fl[n] / 1e9, sb[n] / (PEAK_HBM_GBS * 1e6)) for n in fl}   # ms
     total = sum(floor.values())
     return {"floor_ms": {n: round(v, 4) for n, v in floor.items()}, "floor_ms_layer": round(total, 3),
@@ -104,7 +105,6 @@ def stage_bytes(w) -> dict:
         "permute_x3": 3 * (raster + tiled) + 2 * stats,
         "project_score": 2 * stats + 2 * feats + scores + 2 * Hh * 3 * d * w.r * 2,
         "topk": scores + idx,
-        "unpermute": tiled + raster,
     }
 
 
@@ -154,11 +154,12 @@ def attention_mfma_counters(workload: str):
 
 
 def attention_bytes(w) -> int:
-    """Algorithmic HBM bytes of one attention launch: Q, K, V read once, O and
-    LSE written once, the index lists read once."""
+    """Algorithmic HBM bytes of one attention launch: tiled Q, K, V read once,
+    raster O and the LSE written once, the index lists read once."""
     nT = max(w.tiles_per_head())
     tiled = w.B * w.heads * nT * 128 * w.d * 2
-    return 4 * tiled + w.B * w.heads * nT * 128 * 4 + w.B * w.heads * nT * max(w.k_per_head()) * 4
+    raster = w.B * w.tokens * w.heads * w.d * 2
+    return 3 * tiled + raster + w.B * w.heads * nT * 128 * 4 + w.B * w.heads * nT * max(w.k_per_head()) * 4
 
 
 def cpu_baseline(w, data, sample_tiles: int, seconds_hint: float = 20.0):
@@ -243,7 +244,7 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0):
     torch.cuda.synchronize()
     log("[bench] first layer done")
 
-    stages = ["permute_x3", "project_score", "topk", "sparse_attn", "unpermute"]
+    stages = ["permute_x3", "project_score", "topk", "sparse_attn"]
 
     def step(ev=None):
         if ev is not None:
@@ -260,13 +261,10 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0):
         V.topk_mask(bufs["scores"], geom, ks, idx=bufs["idx"], bitmask=bufs["bitmask"])
         if ev is not None:
             ev[3].record(stream)
-        V.sparse_attn_fwd(bufs["q_t"], bufs["k_t"], bufs["v_t"], bufs["idx"], geom, ks,
-                          o_t=bufs["o_t"], lse=bufs["lse"])
+        V.sparse_attn_fwd_raster(bufs["q_t"], bufs["k_t"], bufs["v_t"], bufs["idx"], geom, ks,
+                                 out=bufs["o"], lse=bufs["lse"])
         if ev is not None:
             ev[4].record(stream)
-        V.tile_unpermute(bufs["o_t"], geom, bufs["o"])
-        if ev is not None:
-            ev[5].record(stream)
 
     for _ in range(warmup):
         step()
@@ -274,7 +272,7 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0):
     log(f"[bench] warmup {warmup} done")
 
     def timed(flush=None):
-        events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
         for s in range(steps):
@@ -288,7 +286,7 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0):
         for ev in events:
             for i, name in enumerate(stages):
                 per_stage[name].append(ev[i].elapsed_time(ev[i + 1]))
-            total.append(ev[0].elapsed_time(ev[5]))
+            total.append(ev[0].elapsed_time(ev[len(stages)]))
         res = {"ms_step": float(np.mean(total)), "ms_step_median": float(np.median(total)),
                "ms_step_min": float(np.min(total)),
                "stage_ms": {n: round(float(np.mean(v)), 4) for n, v in per_stage.items()},

@@ -13,8 +13,9 @@ Python: the five steps of the layer are HIP kernels.
   tile_unpermute   tiled -> raster
   tile_permute_stats      raster Q or K -> token-major tiles + TripPool stats, one pass
   trippool_project_score  stats + W_q, W_k -> features, tile scores
+  sparse_attn_fwd_raster  sparse_attn_fwd writing raster O (no unpermute pass)
   layer_forward    the layer: tile_permute_stats of Q and K, tile_permute of V,
-                   trippool_project_score, topk_mask, sparse_attn_fwd, tile_unpermute
+                   trippool_project_score, topk_mask, sparse_attn_fwd_raster
 
 Measuring a mask against the method's own target:
   dense_index      index lists that keep every key tile (dense attention through sparse_attn_fwd)
@@ -48,7 +49,7 @@ from . import _lib
 from ._lib import VedaError
 
 __all__ = ["Geometry", "VedaError", "tile_permute", "tile_permute_stats", "tile_unpermute", "trippool_score",
-           "trippool_project_score", "topk_mask",
+           "trippool_project_score", "topk_mask", "sparse_attn_fwd_raster",
            "sparse_attn_fwd", "layer_forward", "dense_index", "teacher_tile_max", "mask_overlap", "tile_recall",
            "head_sq_error", "candidate_tiles", "tile_search", "distill_kl", "distill_grad", "adam_step",
            "distill_train", "TILE_TOKENS", "TOKEN_MAJOR", "CHANNEL_MAJOR"]
@@ -268,6 +269,44 @@ def topk_mask(scores: torch.Tensor, geom: Geometry, k_per_head: Sequence[int], k
     return idx, bitmask
 
 
+def _attn_args(q_t, k_t, v_t, idx, geom, k_per_head, with_lse, lse):
+    tshape = _tiled_shape(geom, geom.head_dim)
+    for name, t in (("q_tiled", q_t), ("k_tiled", k_t)):
+        _need(t, torch.bfloat16, tshape, name)
+    _need(v_t, torch.bfloat16, _tiled_cm_shape(geom), "v_tiled")
+    if idx.dim() != 4:
+        raise ValueError("idx must be [B, heads, nT_max, k_max]")
+    k_max = idx.shape[3]
+    _need(idx, torch.int32, (geom.B, geom.n_heads, tshape[2], k_max), "idx")
+    ks = list(k_per_head)
+    if len(ks) != geom.n_heads:
+        raise ValueError("need one k per head")
+    if with_lse and lse is None:
+        lse = torch.empty(tshape[:4], dtype=torch.float32, device=q_t.device)
+    if lse is not None:
+        _need(lse, torch.float32, tshape[:4], "lse")
+    return ks, k_max, lse
+
+
+def sparse_attn_fwd_raster(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, idx: torch.Tensor,
+                           geom: Geometry, k_per_head: Sequence[int], scale: Optional[float] = None,
+                           with_lse: bool = True, out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """sparse_attn_fwd writing O straight into raster order [B, N, heads, d]
+    (`out` may be any strided view with unit channel stride): the bytes
+    tile_unpermute of the tiled O would give, without that pass."""
+    ks, k_max, lse = _attn_args(q_t, k_t, v_t, idx, geom, k_per_head, with_lse, lse)
+    if out is None:
+        out = torch.empty((geom.B, geom.tokens, geom.n_heads, geom.head_dim), dtype=torch.bfloat16,
+                          device=q_t.device)
+    s = _raster_strides(out, geom, "out")
+    sc = float(scale) if scale is not None else 0.0
+    _lib.check(_lib.lib.veda_sparse_attn_fwd_raster(
+        geom.c, q_t.data_ptr(), k_t.data_ptr(), v_t.data_ptr(), idx.data_ptr(), _lib.int_array(ks), int(k_max), sc,
+        out.data_ptr(), s, lse.data_ptr() if lse is not None else None, _stream(q_t)), "veda_sparse_attn_fwd_raster")
+    return out, lse
+
+
 def sparse_attn_fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, idx: torch.Tensor, geom: Geometry,
                     k_per_head: Sequence[int], scale: Optional[float] = None, with_lse: bool = True,
                     o_t: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
@@ -307,8 +346,9 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.
                   buffers: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
     """One Veda attention layer: permute Q/K/V (the TripPool statistics of Q
     and K taken in the same pass), projections and tile scores, Top-k mask,
-    tile-skipping attention, unpermute. `buffers` (from a previous call)
-    reuses every output allocation. Returns all intermediates and `o`."""
+    tile-skipping attention writing raster O. `buffers` (from a previous
+    call) reuses every output allocation. Returns all intermediates and `o`
+    (no tiled O: sparse_attn_fwd + tile_unpermute give the same `o`)."""
     b = buffers if buffers is not None else {}
     b["q_t"], b["stats_q"] = tile_permute_stats(q, geom, b.get("q_t"), b.get("stats_q"))
     b["k_t"], b["stats_k"] = tile_permute_stats(k, geom, b.get("k_t"), b.get("stats_k"))
@@ -317,9 +357,8 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.
                                  {n: b[n] for n in ("feat_q", "feat_k", "scores")} if "scores" in b else None)
     b.update(est)
     b["idx"], b["bitmask"] = topk_mask(b["scores"], geom, k_per_head, idx=b.get("idx"), bitmask=b.get("bitmask"))
-    b["o_t"], b["lse"] = sparse_attn_fwd(b["q_t"], b["k_t"], b["v_t"], b["idx"], geom, k_per_head, scale,
-                                         o_t=b.get("o_t"), lse=b.get("lse"))
-    b["o"] = tile_unpermute(b["o_t"], geom, b.get("o"))
+    b["o"], b["lse"] = sparse_attn_fwd_raster(b["q_t"], b["k_t"], b["v_t"], b["idx"], geom, k_per_head, scale,
+                                              out=b.get("o"), lse=b.get("lse"))
     return b
 
 
@@ -430,9 +469,8 @@ def tile_search(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.Te
     k_t = tile_permute(k, g0)
     v_t = tile_permute(v, g0, layout=CHANNEL_MAJOR)
     idx, ks_all = dense_index(g0, q.device)
-    o_t, _ = sparse_attn_fwd(q_t, k_t, v_t, idx, g0, ks_all, scale, with_lse=False)
-    o_dense = tile_unpermute(o_t, g0)
-    del q_t, k_t, v_t, idx, o_t
+    o_dense, _ = sparse_attn_fwd_raster(q_t, k_t, v_t, idx, g0, ks_all, scale, with_lse=False)
+    del q_t, k_t, v_t, idx
     errs = []
     for tile in cands:
         g = Geometry(B, Hh, d, tuple(grid), [tuple(tile)] * Hh)

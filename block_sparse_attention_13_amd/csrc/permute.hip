@@ -39,16 +39,6 @@ struct RowMap {
   static constexpr int kPasses = VEDA_TILE_TOKENS / kRowsPerPass;
 };
 
-// Raster index of slot sigma of a box, or -1 for a pad slot.
-__device__ __forceinline__ int64_t raster_of_slot(const GeoTable& g, const HeadGeo& hg, const BoxExtent& e,
-                                                  int32_t sigma) {
-  if (!slot_is_real(hg, e, sigma)) return -1;
-  const int32_t sx = sigma & ((1 << hg.lpw) - 1);
-  const int32_t sy = (sigma >> hg.lpw) & ((1 << hg.lph) - 1);
-  const int32_t st = sigma >> (hg.lpw + hg.lph);
-  return (int64_t(e.t0 + st) * g.H + (e.y0 + sy)) * g.W + (e.x0 + sx);
-}
-
 template <int D>
 __global__ __launch_bounds__(kThreads) void tile_permute_kernel(GeoTable g, const uint16_t* __restrict__ x,
                                                                int64_t sb, int64_t sn, int64_t sh,

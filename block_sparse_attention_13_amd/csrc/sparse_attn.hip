@@ -235,7 +235,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
     GeoTable g, const uint16_t* __restrict__ q_t, const uint16_t* __restrict__ k_t,
     const uint16_t* __restrict__ v_t, const int32_t* __restrict__ idx, int32_t k_max, float scale_log2,
-    uint16_t* __restrict__ o_t, float* __restrict__ lse) {
+    uint16_t* __restrict__ o_t, float* __restrict__ lse, uint16_t* __restrict__ o_r, int64_t osb, int64_t osn,
+    int64_t osh) {
   using S = AttnShape<D>;
   // K buffers lds[0..1], V buffers lds[2..3]; after the loop the space holds
   // the half merge.
@@ -246,12 +247,15 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
   const int32_t tq = xcd_tile_order(blockIdx.x, g.nT_max);
   const int64_t head_base = (int64_t(b) * g.heads + hd) * g.nT_max;
   const int64_t tile_elems = S::kTileElems;
-  uint16_t* o_tile = o_t + (head_base + tq) * tile_elems;
+  // Tiled output o_t, or (o_r non-null) raster output: then each real query
+  // writes its token's row of o_r and pad query slots write nothing.
+  uint16_t* o_tile = o_r ? nullptr : o_t + (head_base + tq) * tile_elems;
   float* lse_tile = lse ? lse + (head_base + tq) * kTok : nullptr;
 
   if (tq >= hg.nT) {  // no such query tile for this head: defined zeros / -inf
-    for (int e = threadIdx.x; e < kTok * D / 8; e += kThreads)
-      reinterpret_cast<u32x4*>(o_tile)[e] = u32x4{0u, 0u, 0u, 0u};
+    if (o_tile)
+      for (int e = threadIdx.x; e < kTok * D / 8; e += kThreads)
+        reinterpret_cast<u32x4*>(o_tile)[e] = u32x4{0u, 0u, 0u, 0u};
     if (lse_tile)
       for (int e = threadIdx.x; e < kTok; e += kThreads) lse_tile[e] = -__builtin_inff();
     return;
@@ -365,7 +369,13 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
     const float l_tot = l_half * a0 + l1 * a1;
     const float inv = 1.0f / l_tot;
     const float c0 = a0 * inv, c1 = a1 * inv;
-    uint16_t* orow = o_tile + (qg * 32 + l32) * D;
+    uint16_t* orow;
+    if (o_tile) {
+      orow = o_tile + (qg * 32 + l32) * D;
+    } else {
+      const int64_t n = raster_of_slot(g, hg, box_extent(g, hg, tq), qg * 32 + l32);
+      orow = n >= 0 ? o_r + int64_t(b) * osb + n * osn + int64_t(hd) * osh : nullptr;
+    }
 #pragma unroll
     for (int db = 0; db < S::kDB; ++db) {
       float o[16];
@@ -376,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
         u32x2 wd;
         wd[0] = pack_bf16x2(o[4 * g4 + 0], o[4 * g4 + 1]);
         wd[1] = pack_bf16x2(o[4 * g4 + 2], o[4 * g4 + 3]);
-        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g4 + 4 * h) = wd;
+        if (orow) *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g4 + 4 * h) = wd;
       }
     }
     if (lse_tile && h == 0) lse_tile[qg * 32 + l32] = (m + __log2f(l_tot)) * 0.69314718055994530942f;
@@ -387,13 +397,15 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
 
 hipError_t launch_sparse_attn(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t, const uint16_t* v_t,
                               const int32_t* idx, int32_t k_max, float scale, uint16_t* o_t, float* lse,
-                              hipStream_t s) {
+                              uint16_t* o_r, int64_t osb, int64_t osn, int64_t osh, hipStream_t s) {
   const dim3 grid(g.nT_max, g.heads, g.B);
   const float scale_log2 = scale * 1.44269504088896340736f;
   if (g.d == 128)
-    sparse_attn_fwd_kernel<128><<<grid, kThreads, 0, s>>>(g, q_t, k_t, v_t, idx, k_max, scale_log2, o_t, lse);
+    sparse_attn_fwd_kernel<128><<<grid, kThreads, 0, s>>>(g, q_t, k_t, v_t, idx, k_max, scale_log2, o_t, lse, o_r,
+                                                         osb, osn, osh);
   else
-    sparse_attn_fwd_kernel<64><<<grid, kThreads, 0, s>>>(g, q_t, k_t, v_t, idx, k_max, scale_log2, o_t, lse);
+    sparse_attn_fwd_kernel<64><<<grid, kThreads, 0, s>>>(g, q_t, k_t, v_t, idx, k_max, scale_log2, o_t, lse, o_r,
+                                                        osb, osn, osh);
   return hipGetLastError();
 }
 

@@ -243,7 +243,26 @@ int veda_sparse_attn_fwd(const veda_geom* g, const void* q_tiled, const void* k_
   return launched(veda::launch_sparse_attn(
       t, static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_tiled),
       static_cast<const uint16_t*>(v_tiled), idx, k_max, softmax_scale, static_cast<uint16_t*>(o_tiled), lse,
-      static_cast<hipStream_t>(stream)));
+      nullptr, 0, 0, 0, static_cast<hipStream_t>(stream)));
+}
+
+int veda_sparse_attn_fwd_raster(const veda_geom* g, const void* q_tiled, const void* k_tiled, const void* v_tiled,
+                                const int32_t* idx, const int32_t* k_per_head, int32_t k_max, float softmax_scale,
+                                void* o_raster, veda_raster_strides s, float* lse, void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!q_tiled || !k_tiled || !v_tiled || !idx || !o_raster) return VEDA_ERR_NULL;
+  VEDA_TRY(set_k(k_per_head, k_max, &t));
+  for (const void* p : {q_tiled, k_tiled, v_tiled, static_cast<const void*>(idx), static_cast<const void*>(o_raster)})
+    if (!aligned16(p)) return VEDA_ERR_ALIGN;
+  if (lse && !aligned16(lse)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_strides(s));
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) softmax_scale = 1.0f / std::sqrt(float(t.d));
+  VEDA_TRY(check_device());
+  return launched(veda::launch_sparse_attn(
+      t, static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_tiled),
+      static_cast<const uint16_t*>(v_tiled), idx, k_max, softmax_scale, nullptr, lse,
+      static_cast<uint16_t*>(o_raster), s.b, s.n, s.h, static_cast<hipStream_t>(stream)));
 }
 
 int veda_teacher_tile_max(const veda_geom* g, const void* q_tiled, const void* k_tiled, const float* lse_dense,

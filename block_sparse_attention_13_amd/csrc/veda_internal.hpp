@@ -64,6 +64,15 @@ VEDA_HD bool slot_is_real(const HeadGeo& hg, const BoxExtent& e, int32_t sigma) 
   return st < e.vt && sy < e.vh && sx < e.vw;
 }
 
+// Raster index n = (t*H + y)*W + x of slot sigma of a box, or -1 for a pad slot.
+VEDA_HD int64_t raster_of_slot(const GeoTable& g, const HeadGeo& hg, const BoxExtent& e, int32_t sigma) {
+  if (!slot_is_real(hg, e, sigma)) return -1;
+  const int32_t sx = sigma & ((1 << hg.lpw) - 1);
+  const int32_t sy = (sigma >> hg.lpw) & ((1 << hg.lph) - 1);
+  const int32_t st = sigma >> (hg.lpw + hg.lph);
+  return (int64_t(e.t0 + st) * g.H + (e.y0 + sy)) * g.W + (e.x0 + sx);
+}
+
 // 64 bits of a periodic slot pattern: bit b (slot base + b) is set iff
 // (slot mod 2^lg_period) < lim. Slots are numbered 0..127 inside a box.
 VEDA_HD uint64_t periodic_slot_bits(int lg_period, int lim, int base) {
@@ -134,8 +143,10 @@ hipError_t launch_distill_grad(const GeoTable& g, int32_t r, const uint16_t* sta
                                float* d_feat_q, float* d_feat_k, float* d_wq, float* d_wk, hipStream_t s);
 hipError_t launch_adam(int64_t n, float* w, const float* grad, float* m, float* v, float lr, float beta1, float beta2,
                        float eps, float bc1, float bc2, uint16_t* w_bf16, hipStream_t s);
+// O goes to o_t (tiled) when o_r is null, else straight to raster o_r with
+// element strides (osb, osn, osh).
 hipError_t launch_sparse_attn(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t, const uint16_t* v_t,
                               const int32_t* idx, int32_t k_max, float scale, uint16_t* o_t, float* lse,
-                              hipStream_t s);
+                              uint16_t* o_r, int64_t osb, int64_t osn, int64_t osh, hipStream_t s);
 
 }  // namespace veda

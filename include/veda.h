@@ -14,7 +14,8 @@
  * The same layer in fewer passes over HBM, with identical results:
  *   veda_tile_permute_stats    x2  raster Q/K -> tiles and each tile's TripPool stats in one pass
  *   veda_trippool_project_score    stats -> head-specific projections -> tile scores
- *   (then veda_tile_permute of V, veda_topk_mask, veda_sparse_attn_fwd, veda_tile_unpermute)
+ *   veda_sparse_attn_fwd_raster    attention that writes raster O itself (no unpermute pass)
+ *   (with veda_tile_permute of V and veda_topk_mask in between)
  *
  * Two more calls measure the mask against the method's own target:
  *   veda_teacher_tile_max      max-pooled dense attention per (query tile, key tile); its
@@ -226,6 +227,22 @@ int veda_sparse_attn_fwd(const veda_geom* g, const void* q_tiled, const void* k_
                          const void* v_tiled, const int32_t* idx, const int32_t* k_per_head,
                          int32_t k_max, float softmax_scale, void* o_tiled, float* lse,
                          void* stream);
+
+/*
+ * The same attention forward writing O straight into raster order, which
+ * spares the tile unpermute pass (Veda page, same passages; the raster O is
+ * the inverse of the head-conditioned re-tiling, "Architecture", Principle 02).
+ * Arguments as veda_sparse_attn_fwd, except:
+ *   o_raster  out  raster bf16 [B, N, heads, d] with element strides `s` (channel stride 1): the
+ *                  row of every real token of every head is written; nothing else is touched
+ *   s         in   strides of o_raster (elements; multiples of 8, else VEDA_ERR_ALIGN)
+ * For the same inputs, o_raster holds exactly the bytes veda_tile_unpermute of veda_sparse_attn_fwd's
+ * o_tiled would give, and lse is identical.
+ */
+int veda_sparse_attn_fwd_raster(const veda_geom* g, const void* q_tiled, const void* k_tiled,
+                                const void* v_tiled, const int32_t* idx, const int32_t* k_per_head,
+                                int32_t k_max, float softmax_scale, void* o_raster,
+                                veda_raster_strides s, float* lse, void* stream);
 
 /*
  * Inverse re-tiling: raster x[b, n, hd, :] = tiled x at the slot of token n

@@ -21,7 +21,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     from block_sparse_attention_13_amd import _lib
     declared = _declared_functions()
-    assert len(declared) == 16, declared
+    assert len(declared) == 17, declared
     assert sorted(_lib.EXPORTS) == declared
     for name in declared:
         assert hasattr(_lib.lib, name), name
@@ -108,6 +108,12 @@ def test_call_errors_precede_any_device_work():
     assert L.veda_sparse_attn_fwd(g.c, FAKE, FAKE, FAKE, FAKE, _lib.int_array([9]), 8, 0.0, FAKE, None, None) == -4
     assert L.veda_sparse_attn_fwd(g.c, FAKE, None, FAKE, FAKE, ks, 4, 0.0, FAKE, None, None) == -1
     assert L.veda_sparse_attn_fwd(g.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE, FAKE + 4, None) == -5
+    assert L.veda_sparse_attn_fwd_raster(g.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, None, s, None, None) == -1
+    assert L.veda_sparse_attn_fwd_raster(g.c, FAKE, FAKE, FAKE, FAKE, _lib.int_array([9]), 8, 0.0, FAKE, s, None,
+                                         None) == -4
+    assert L.veda_sparse_attn_fwd_raster(g.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE,
+                                         _lib.VedaRasterStrides(1024, 132, 128), None, None) == -5
+    assert L.veda_sparse_attn_fwd_raster(g.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE, s, FAKE + 4, None) == -5
     assert L.veda_teacher_tile_max(g.c, FAKE, FAKE, None, 0.0, FAKE, None) == -1
     assert L.veda_teacher_tile_max(g.c, FAKE, FAKE, FAKE, 0.0, FAKE + 4, None) == -5
     assert L.veda_teacher_tile_max(_geom(tiles=((2, 2, 2),)).c, FAKE, FAKE, FAKE, 0.0, FAKE, None) == -3
@@ -136,6 +142,8 @@ def test_valid_call_without_gpu_reports_device_error():
     assert _lib.lib.veda_tile_permute(g.c, FAKE, s, FAKE, _lib.VEDA_TILED_CHANNEL_MAJOR, None) == -6
     assert _lib.lib.veda_tile_permute_stats(g.c, FAKE, s, FAKE, FAKE, None) == -6
     assert _lib.lib.veda_trippool_project_score(g.c, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, None) == -6
+    assert _lib.lib.veda_sparse_attn_fwd_raster(g.c, FAKE, FAKE, FAKE, FAKE, _lib.int_array([3]), 4, 0.0, FAKE, s,
+                                                None, None) == -6
 
 
 def test_python_wrappers_validate_before_calling():

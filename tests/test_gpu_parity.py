@@ -75,6 +75,16 @@ def check_head(w, data, out, hd, ks, tiles, b=0, check_attention=True):
     assert np.array_equal(bm, want_bm), ("bitmask", hd)
     if not check_attention:
         return r
+    # The layer writes raster O directly; the tiled route (pre-filled with
+    # garbage, so every byte it leaves is checked) must give the same bytes.
+    V = _lib()
+    geom = geometry(w)
+    o_tiled = torch.full(out["q_t"].shape, 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    o_tiled, lse_tiled = V.sparse_attn_fwd(out["q_t"], out["k_t"], out["v_t"], out["idx"], geom, ks, o_t=o_tiled)
+    o_back = V.tile_unpermute(o_tiled, geom)
+    torch.cuda.synchronize()
+    assert torch.equal(o_back[b, :, hd].view(torch.int16), out["o"][b, :, hd].view(torch.int16)), ("raster O", hd)
+    assert torch.equal(lse_tiled[b, hd].view(torch.int32), out["lse"][b, hd].view(torch.int32)), ("lse", hd)
     pos = O.tiled_position(w.grid, tile)
     rows = np.flatnonzero(np.isfinite(r["lse"]))
     o_gpu = f32_of_bf16(out["o"][b, :, hd, :])
@@ -86,7 +96,7 @@ def check_head(w, data, out, hd, ks, tiles, b=0, check_attention=True):
     valid = np.zeros(nT * 128, bool)
     valid[pos] = True
     v_t = O.bf16_bits_to_float(bits_of(out["v_t"][b, hd])).reshape(nT_max, d, 128).swapaxes(1, 2).astype(np.float64)
-    o_t = f32_of_bf16(out["o_t"][b, hd]).reshape(nT_max, 128, d)
+    o_t = f32_of_bf16(o_tiled[b, hd]).reshape(nT_max, 128, d)
     for t in tiles:
         pads = np.flatnonzero(~valid[t * 128:(t + 1) * 128])
         if len(pads):
@@ -95,7 +105,7 @@ def check_head(w, data, out, hd, ks, tiles, b=0, check_attention=True):
             want = keys.mean(axis=0)
             compare_o(o_t[t, pads], np.broadcast_to(want, (len(pads), d)), f"pad queries of tile {t}")
     if nT < nT_max:
-        assert not bits_of(out["o_t"][b, hd])[nT:].any()
+        assert not bits_of(o_tiled[b, hd])[nT:].any()
         assert np.all(np.isneginf(out["lse"][b, hd, nT:].cpu().numpy()))
     return r
 
@@ -172,10 +182,13 @@ def test_unpermute_inverts_permute_with_strided_raster():
     ("tiny", None, 1, None),                                       # d = 64, r = 32
     (None, None, 1, ((3, 9, 17), [(1, 8, 16), (8, 4, 4)], 64, 64)),  # d = 64, r = 64, mostly pad
 ])
-def test_one_pass_estimator_matches_two_pass(wname, heads, B, custom):
+def test_fused_layer_matches_unfused(wname, heads, B, custom):
     """layer_forward takes the statistics while it permutes Q and K
-    (tile_permute_stats + trippool_project_score); the two-pass route
-    (tile_permute + trippool_score) must give the same bytes."""
+    (tile_permute_stats + trippool_project_score) and writes raster O from
+    the attention kernel (sparse_attn_fwd_raster); the unfused route
+    (tile_permute, trippool_score, topk_mask, sparse_attn_fwd,
+    tile_unpermute) must give the same bytes. The raster O also goes into
+    a strided view whose neighbouring bytes must stay untouched."""
     V = _lib()
     if custom is None:
         w = W[wname] if heads is None else W[wname].with_heads(heads)
@@ -194,6 +207,21 @@ def test_one_pass_estimator_matches_two_pass(wname, heads, B, custom):
     for name in ("stats_q", "stats_k", "feat_q", "feat_k"):
         assert torch.equal(out[name].view(torch.int16), two[name].view(torch.int16)), name
     assert torch.equal(out["scores"].view(torch.int32), two["scores"].view(torch.int32))
+    ks = w.k_per_head()
+    idx, _ = V.topk_mask(two["scores"], geom, ks)
+    v_t = V.tile_permute(v, geom, layout=V.CHANNEL_MAJOR)
+    o_t, lse = V.sparse_attn_fwd(q_t, k_t, v_t, idx, geom, ks)
+    o = V.tile_unpermute(o_t, geom)
+    torch.cuda.synchronize()
+    assert torch.equal(out["idx"], idx)
+    assert torch.equal(out["o"].view(torch.int16), o.view(torch.int16))
+    assert torch.equal(out["lse"].view(torch.int32), lse.view(torch.int32))
+    packed = torch.full((w.B, w.tokens, 2, w.heads, w.d), 0x7FC0, dtype=torch.int16, device="cuda")
+    view = packed.view(torch.bfloat16)[:, :, 1]
+    V.sparse_attn_fwd_raster(q_t, k_t, v_t, idx, geom, ks, out=view, with_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(packed[:, :, 1], o.view(torch.int16))
+    assert torch.all(packed[:, :, 0] == 0x7FC0)
 
 
 def _random_workload(grid, tiles, d, r, heads, seed, keep=None, k=None):
@@ -319,7 +347,7 @@ def test_every_output_byte_is_written():
     g = lambda shape, dt: torch.full(shape, 0x7FC0 if dt == torch.bfloat16 else -1, dtype=torch.int16 if dt == torch.bfloat16 else torch.int32, device="cuda").view(dt)
     bufs = {
         "q_t": g((B, Hh, nT, 128, d), torch.bfloat16), "k_t": g((B, Hh, nT, 128, d), torch.bfloat16),
-        "v_t": g((B, Hh, nT, d, 128), torch.bfloat16), "o_t": g((B, Hh, nT, 128, d), torch.bfloat16),
+        "v_t": g((B, Hh, nT, d, 128), torch.bfloat16),
         "stats_q": g((B, Hh, nT, 3 * d), torch.bfloat16), "stats_k": g((B, Hh, nT, 3 * d), torch.bfloat16),
         "feat_q": g((B, Hh, nT, w.r), torch.bfloat16), "feat_k": g((B, Hh, nT, w.r), torch.bfloat16),
         "scores": g((B, Hh, nT, nT), torch.float32), "idx": g((B, Hh, nT, max(w.k_per_head())), torch.int32),
