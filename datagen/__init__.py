@@ -30,6 +30,9 @@ A_hd is 1, or U(0.5, 2) for the 720p and hc workloads.
 Projection weights W_q, W_k [heads, 3d, r] are N(0, 1) / sqrt(3d), rounded to
 bfloat16.
 
+The field is summed in a fixed order without BLAS, so the same workload
+gives the same bytes on every call, whatever the thread count.
+
 Random streams: numpy PCG64 seeded by SeedSequence([seed, tensor_id, b, hd])
 for tensor_id 0/1/2 = Q/K/V; [seed, 99, hd] for A_hd; [seed, 100, hd] and
 [seed, 101, hd] for W_q and W_k.
@@ -147,7 +150,12 @@ def _fill_head(out: np.ndarray, w: Workload, tensor_id: int, b: int, hd: int,
     phi = rng.uniform(0.0, 2.0 * math.pi, size=8)
     a = rng.standard_normal((8, w.d))
     a /= np.linalg.norm(a, axis=0, keepdims=True)
-    field = (amp * np.cos(2.0 * math.pi * (pos @ kf.T) + phi)) @ a          # [N, d] float64
+    # Sums in a fixed order without BLAS (whose summation order can change
+    # with its threading), so the bytes are the same on every call: the
+    # 3-term phase elementwise, the 8-term field with numpy's own einsum loop.
+    arg = pos[:, 0:1] * kf[:, 0] + pos[:, 1:2] * kf[:, 1] + pos[:, 2:3] * kf[:, 2]   # [N, 8]
+    c = amp * np.cos(2.0 * math.pi * arg + phi)
+    field = np.einsum("nf,fd->nd", c, a, optimize=False)                         # [N, d] float64
     noise = rng.standard_normal((pos.shape[0], w.d), dtype=np.float32)
     out[b, :, hd, :] = to_bf16_bits(field.astype(np.float32) + noise)
 

@@ -63,3 +63,18 @@ def test_products_stay_normal_on_generated_data():
     wq = O.bf16_bits_to_float(data["wq"][0]).astype(np.float64)
     prods = np.abs(st[:, :, None] * wq[None, :, :])
     assert prods[prods > 0].min() > 2.0 ** -126
+
+
+def test_input_generator_bytes_are_pinned():
+    """The seeded inputs are the bytes recorded in tests/golden/datagen_sha256.json."""
+    import json
+    import os
+    import importlib.util
+    here = os.path.dirname(os.path.abspath(__file__))
+    spec = importlib.util.spec_from_file_location("make_datagen_hashes",
+                                                  os.path.join(here, "golden", "make_datagen_hashes.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    with open(os.path.join(here, "golden", "datagen_sha256.json")) as f:
+        want = json.load(f)["hashes"]
+    assert mod.hashes() == want
