@@ -371,3 +371,80 @@ def test_invalid_call_raises_and_writes_nothing():
         V.topk_mask(s, geom, [9, 4], k_max=4, idx=idx, with_bitmask=False)
     torch.cuda.synchronize()
     assert torch.all(idx == 7)
+
+
+def test_layer_is_deterministic():
+    """Three runs of the whole layer give the same bytes in every output."""
+    V = _lib()
+    w = W["480p"]
+    data = datagen.generate(w)
+    geom, first, (q, k, v, wq, wk) = run_layer(w, data)
+    for _ in range(2):
+        again = V.layer_forward(q, k, v, wq, wk, geom, w.k_per_head())
+        torch.cuda.synchronize()
+        for name, t in first.items():
+            a, b = t.contiguous().view(torch.uint8), again[name].contiguous().view(torch.uint8)
+            assert torch.equal(a, b), name
+
+
+_GUARD_BYTES = 4096
+
+
+def _guarded(shape, dtype):
+    """A tensor of `shape` inside a larger buffer whose first and last 4 KiB
+    hold a known pattern; returns (tensor, buffer)."""
+    n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+    buf = torch.full((n + 2 * _GUARD_BYTES,), 0xA5, dtype=torch.uint8, device="cuda")
+    return buf[_GUARD_BYTES:_GUARD_BYTES + n].view(dtype).view(shape), buf
+
+
+def _guards_intact(buf):
+    return bool(torch.all(buf[:_GUARD_BYTES] == 0xA5)) and bool(torch.all(buf[-_GUARD_BYTES:] == 0xA5))
+
+
+def test_outputs_stay_in_their_buffers():
+    """Every call writes inside its outputs: 4 KiB before and after each one
+    stay untouched (ragged boxes, three tile shapes, B = 2)."""
+    V = _lib()
+    w = dataclasses.replace(W["hc"].with_heads(6), B=2)
+    data = datagen.generate(w)
+    geom = geometry(w)
+    nT, B, Hh, d, r = geom.max_tiles(), w.B, w.heads, w.d, w.r
+    kmax = max(w.k_per_head())
+    shapes = {
+        "q_t": ((B, Hh, nT, 128, d), torch.bfloat16), "k_t": ((B, Hh, nT, 128, d), torch.bfloat16),
+        "v_t": ((B, Hh, nT, d, 128), torch.bfloat16),
+        "stats_q": ((B, Hh, nT, 3 * d), torch.bfloat16), "stats_k": ((B, Hh, nT, 3 * d), torch.bfloat16),
+        "feat_q": ((B, Hh, nT, r), torch.bfloat16), "feat_k": ((B, Hh, nT, r), torch.bfloat16),
+        "scores": ((B, Hh, nT, nT), torch.float32), "idx": ((B, Hh, nT, kmax), torch.int32),
+        "bitmask": ((B, Hh, nT, (nT + 31) // 32), torch.int32), "lse": ((B, Hh, nT, 128), torch.float32),
+        "o": ((B, w.tokens, Hh, d), torch.bfloat16),
+    }
+    bufs, raw = {}, {}
+    for name, (shape, dt) in shapes.items():
+        bufs[name], raw[name] = _guarded(shape, dt)
+    bufs["bitmask"] = bufs["bitmask"].view(torch.uint32)
+    geom, out, (q, k, v, wq, wk) = run_layer(w, data, buffers=bufs)
+    for name, buf in raw.items():
+        assert _guards_intact(buf), ("fused layer", name)
+    # the unfused route and the measurement calls, into guarded outputs too
+    checks = []
+    xt, b1 = _guarded(shapes["q_t"][0], torch.bfloat16)
+    V.tile_permute(q, geom, xt); checks.append(("tile_permute", b1))
+    xc, b2 = _guarded(shapes["v_t"][0], torch.bfloat16)
+    V.tile_permute(v, geom, xc, layout=V.CHANNEL_MAJOR); checks.append(("tile_permute channel-major", b2))
+    est = {}
+    for name in ("stats_q", "stats_k", "feat_q", "feat_k", "scores"):
+        est[name], b3 = _guarded(*shapes[name]); checks.append(("trippool_score " + name, b3))
+    V.trippool_score(out["q_t"], out["k_t"], wq, wk, geom, est)
+    o_t, b4 = _guarded(shapes["q_t"][0], torch.bfloat16)
+    V.sparse_attn_fwd(out["q_t"], out["k_t"], out["v_t"], out["idx"], geom, w.k_per_head(), o_t=o_t)
+    checks.append(("sparse_attn_fwd", b4))
+    o, b5 = _guarded(shapes["o"][0], torch.bfloat16)
+    V.tile_unpermute(o_t, geom, o); checks.append(("tile_unpermute", b5))
+    teacher, b6 = _guarded(shapes["scores"][0], torch.float32)
+    V.teacher_tile_max(out["q_t"], out["k_t"], out["lse"], geom, out=teacher); checks.append(("teacher", b6))
+    torch.cuda.synchronize()
+    for name, buf in checks:
+        assert _guards_intact(buf), name
+    assert torch.equal(o.view(torch.int16), out["o"].view(torch.int16))
