@@ -195,10 +195,24 @@ def cpu_baseline(w, data, sample_tiles: int, seconds_hint: float = 20.0):
     o, lse = O.sparse_attention(q, kk, v, w.grid, tile, idx, 1.0 / math.sqrt(w.d), query_tiles=tiles)
     t_attn = time.perf_counter() - t0
     ms_layer = (t_prep + t_attn / len(tiles) * nT) * w.heads * w.B * 1e3
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
+    blas = None
+    try:
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in threadpoolctl.threadpool_info()
+                         if i.get("user_api") == "blas") or None
+    except Exception:
+        pass
     return {
         "value": round(ms_layer, 1), "unit": "ms/layer", "cores": int(threads), "kind": "oracle",
         "sample": (f"head 0 of {w.heads}: full mask preparation ({t_prep:.1f} s) + attention of "
                    f"{len(tiles)} of {nT} query tiles ({t_attn:.1f} s), scaled to {nT} tiles x {w.heads} heads"),
+        "stage_s": {"mask_preparation_head0": round(t_prep, 2), "attention_sampled_tiles": round(t_attn, 2)},
+        "cpu_model": cpu_model, "numpy": np.__version__, "blas": blas,
     }
 
 
@@ -455,7 +469,7 @@ def distill_report(V, datagen, name="480p", steps=300, lr=3e-3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long")
     ap.add_argument("--heads", type=int, default=0, help="run only the first N heads (0 = all)")
