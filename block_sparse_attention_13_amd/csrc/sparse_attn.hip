@@ -119,12 +119,11 @@ __device__ __forceinline__ void s_tile(floatx16 (&sacc)[2], const WaveState<D>& 
   }
 }
 
-// Mask and the running-max update of the online softmax (base 2, max moved
-// lazily: only when a row's max grows by more than 2^kRescaleSlack).
+// Pad keys of a border tile get -inf through a branch-free bias (wm: this
+// wave's 64 real-key bits; ~0 for a full tile, which is left untouched).
 template <int D>
-__device__ __forceinline__ void softmax_max(WaveState<D>& w, floatx16 (&sacc)[2], uint64_t wm, float scale_log2) {
-  using S = AttnShape<D>;
-  if (wm != ~0ull) {  // pad keys get -inf through a branch-free bias
+__device__ __forceinline__ void mask_tile(floatx16 (&sacc)[2], uint64_t wm) {
+  if (wm != ~0ull) {
     const uint32_t wlo = uint32_t(wm), whi = uint32_t(wm >> 32);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -135,15 +134,30 @@ __device__ __forceinline__ void softmax_max(WaveState<D>& w, floatx16 (&sacc)[2]
         sacc[kb][v] += __uint_as_float((real - 1u) & 0xFF800000u);
       }
   }
+}
+
+// Row max of a lane's 32 scores combined with the other half-wave's (lanes
+// l and l + 32 hold the two halves of one query's keys), in base-2 units.
+__device__ __forceinline__ float row_max_base2(float mx, float scale_log2) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+}
+
+template <int D>
+__device__ __forceinline__ float tile_max(const floatx16 (&sacc)[2], float scale_log2) {
   float mx = sacc[0][0];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-  {  // lanes l and l + 32 hold the two halves of one query's keys
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
-  }
+  return row_max_base2(mx, scale_log2);
+}
+
+// Running-max update of the online softmax (base 2), moved lazily: only when
+// a row's max grows by more than 2^kRescaleSlack are m, l and O rescaled.
+template <int D>
+__device__ __forceinline__ void update_max(WaveState<D>& w, float mx) {
+  using S = AttnShape<D>;
   if (__builtin_amdgcn_ballot_w64(mx > w.m_run + kRescaleSlack) != 0) {
     const float m_new = fmaxf(w.m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_new);
@@ -172,19 +186,23 @@ __device__ __forceinline__ u32x4 v_frag(const uint16_t* vs, int t, int half, int
 // step, one LDS-DMA chunk, so the VALU work and the copies run while the
 // matrix core is busy and no burst of copies fills the vector-memory queue.
 // The PV MFMAs of this tile follow, their V^T reads kLook steps ahead.
-// Scheduling fences keep each step's instructions together. The last
-// iteration (kLast) has no next tile: it issues no QK^T MFMAs and no copies.
-template <int D, bool kLast>
+// Scheduling fences keep each step's instructions together. The next
+// tile's pad-key bias and row max (VALU work) run under the PV MFMAs, two
+// scores per step. The last iteration (kLast) has no next tile: it issues no
+// QK^T MFMAs, no copies and no max.
+template <int D, bool kLast, typename NextMask>
 __device__ __forceinline__ void hot_tile(WaveState<D>& w, const floatx16 (&s_cur)[2], floatx16 (&s_next)[2],
                                          const uint16_t* ks_next, const uint16_t* vs_cur, const DmaPlan<D>& pl,
                                          uint32_t dma_tile_bytes, lds_u16* dma_dst, int half, int h, int l32,
-                                         float scale_log2) {
+                                         float scale_log2, const NextMask& next_mask, float& mx_next) {
   using S = AttnShape<D>;
   constexpr int kLook = 4;                 // LDS operand reads in flight ahead of the S MFMAs
   constexpr int kLookV = 4;                // ... and ahead of the PV MFMAs
   constexpr int kS = 2 * S::kDC;           // QK^T MFMAs per tile
   constexpr int kE = 16;                   // exponential pairs per tile
   constexpr int kPV = 4 * S::kDB;          // PV MFMAs per tile
+  constexpr int kPer = 32 / kPV;           // next-tile scores whose max each PV step takes
+  static_assert(kPer * kPV == 32, "the PV steps cover the 32 scores of a lane");
   constexpr int kSteps = kS > kE ? kS : kE;
 
   // A half that has seen only pad keys so far keeps m = -inf; its exponents
@@ -218,17 +236,24 @@ __device__ __forceinline__ void hot_tile(WaveState<D>& w, const floatx16 (&s_cur
     __builtin_amdgcn_sched_barrier(0);
   }
   w.l_run += psum;
+  if constexpr (!kLast) mask_tile<D>(s_next, next_mask());  // real-key bits of the next tile
 
   u32x4 vf[kPV];
 #pragma unroll
   for (int t = 0; t < kLookV; ++t) vf[t] = v_frag<D>(vs_cur, t, half, h, l32);
+  float mx = -__builtin_inff();
 #pragma unroll
   for (int t = 0; t < kPV; ++t) {
     if (t + kLookV < kPV) vf[t + kLookV] = v_frag<D>(vs_cur, t + kLookV, half, h, l32);
     const int db = t / 4, kb = (t / 2) % 2, c2 = t % 2;
     w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[t]), as_bf16x8(pf[kb][c2]), w.oacc[db], 0, 0, 0);
+    if (!kLast) {  // scores kPer*t .. kPer*t + kPer - 1 of the next tile's 32
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) mx = fmaxf(mx, s_next[(kPer * t + e) / 16][(kPer * t + e) % 16]);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (!kLast) mx_next = row_max_base2(mx, scale_log2);
 }
 
 template <int D>
@@ -309,6 +334,8 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
   __syncthreads();
   floatx16 sc[2];
   s_tile<D>(sc, w, lds[0], half, h, l32);
+  mask_tile<D>(sc, real_key_bits(g, hg, j, half, h));
+  float mx_cur = tile_max<D>(sc, scale_log2);  // row max of the tile the next iteration finishes
   __syncthreads();  // every wave has read lds[0] before tile 2 lands there
 
   // One pipelined iteration: s_cur holds S of tile i, s_next receives S of
@@ -317,12 +344,16 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
   auto iteration = [&](auto last, int i, floatx16 (&s_cur)[2], floatx16 (&s_next)[2]) {
     constexpr bool kLast = decltype(last)::value;
     const int cur = i & 1;
-    softmax_max<D>(w, s_cur, real_key_bits(g, hg, j, half, h), scale_log2);
+    update_max<D>(w, mx_cur);
     // K of tile i+2 into lds[cur] (K of tile i, read in the previous
     // iteration) or V of tile i+1 into lds[2 + (cur ^ 1)] (V of tile i-1).
+    // Tile i+1's scores are masked and their row max taken under the PV MFMAs.
+    float mx_next = 0.0f;
     hot_tile<D, kLast>(w, s_cur, s_next, lds[cur ^ 1], lds[2 + cur], plan, tile_src(plan.is_k ? jn2 : jn),
-                       lbuf + (plan.is_k ? cur : 2 + (cur ^ 1)) * S::kTileElems, half, h, l32, scale_log2);
+                       lbuf + (plan.is_k ? cur : 2 + (cur ^ 1)) * S::kTileElems, half, h, l32, scale_log2,
+                       [&] { return real_key_bits(g, hg, jn, half, h); }, mx_next);
     if constexpr (!kLast) {
+      mx_cur = mx_next;
       j = jn;
       jn = jn2;
       jn2 = sel[min(i + 3, kh - 1)];
