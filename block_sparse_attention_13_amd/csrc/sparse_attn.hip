@@ -180,13 +180,16 @@ __device__ __forceinline__ u32x4 v_frag(const uint16_t* vs, int t, int half, int
   return *reinterpret_cast<const u32x4*>(vs + d * kTok + (((8 * half + 4 * kb + 2 * c2 + h) ^ (d & 15)) * 8));
 }
 
-// The hot part of one pipelined iteration, in the order the instructions
-// are to issue. Step t issues one QK^T MFMA of the next tile (operand read
-// kLook steps ahead), one pair of exponentials of this tile and, every other
-// step, one LDS-DMA chunk, so the VALU work and the copies run while the
-// matrix core is busy and no burst of copies fills the vector-memory queue.
-// The PV MFMAs of this tile follow, their V^T reads kLook steps ahead.
-// Scheduling fences keep each step's instructions together. The next
+// The hot part of one pipelined iteration. Step t issues one QK^T MFMA of
+// the next tile (operand read kLook steps ahead) and, every other step, one
+// LDS-DMA chunk, so no burst of copies fills the vector-memory queue; the PV
+// MFMAs of this tile follow, their V^T reads kLook steps ahead. Scheduling
+// fences keep each step's instructions together. The exponentials of this
+// tile are written beside the QK^T steps, but the compiler sinks them below
+// the next tile's mask code, toward their first use: the emitted order is a
+// QK^T block, the exponentials, then PV. That order measured faster than
+// exponentials kept inside the QK^T steps, and than the same order written
+// out by hand. The next
 // tile's pad-key bias and row max (VALU work) run under the PV MFMAs, two
 // scores per step. The last iteration (kLast) has no next tile: it issues no
 // QK^T MFMAs, no copies and no max.
