@@ -611,6 +611,12 @@ def main():
                      "kernel": "sparse_attn_fwd_kernel<128>", "flops_per_launch": f_attn,
                      "counters": attention_mfma_counters(args.workload)},
         "cpu_baseline": cpu,
+        "pages_context": {
+            "note": "the Veda pages' own figures, context only: their layer includes the MLP, and they state "
+                    "neither the GPU nor the precision, so vs_baseline stays null",
+            "ms_per_layer_245k_dense_fa3": 1576, "ms_per_layer_245k_veda": 309,
+            "attention_speedup_vs_fa3": 10.5, "end_to_end_speedup": 5.1, "hardware": "unstated",
+        },
         "per_config": per_config,
         "head_shard": shard,
         "dense_reference": dense,
