@@ -108,6 +108,18 @@ def stage_bytes(w) -> dict:
     }
 
 
+def kernel_code_hash(path: str) -> str:
+    """First 16 hex digits of the SHA-256 of a source file's code with its
+    comments and whitespace removed, so that edits to comments alone do not
+    mark counter summaries taken from the same code as stale."""
+    import hashlib
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
+
+
 ATTN_COUNTERS = os.path.join(ROOT, "profiles", "sparse_attn_long245k_hbm_counters.md")
 ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_13_amd", "csrc", "sparse_attn.hip")
 
@@ -116,19 +128,15 @@ def attention_traffic(workload: str):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads
     for a plain copy of known size), or None when that summary is missing,
-    covers another workload, or was taken from a different kernel source."""
-    import hashlib
+    covers another workload, or was taken from different kernel code."""
     if workload != "long" or not os.path.exists(ATTN_COUNTERS):
         return None
     with open(ATTN_COUNTERS) as f:
         text = f.read()
     m_b = re.search(r"^traffic_bytes_per_launch = (\d+)$", text, re.M)
-    m_h = re.search(r"^kernel_source_sha256_16 = ([0-9a-f]{16})$", text, re.M)
-    if not (m_b and m_h):
+    m_h = re.search(r"^kernel_code_sha256_16 = ([0-9a-f]{16})$", text, re.M)
+    if not (m_b and m_h) or kernel_code_hash(ATTN_SOURCE) != m_h.group(1):
         return None
-    with open(ATTN_SOURCE, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest()[:16] != m_h.group(1):
-            return None
     return int(m_b.group(1))
 
 
@@ -139,17 +147,13 @@ def attention_mfma_counters(workload: str):
     """MFMA-busy fraction of SIMD cycles and the effective shader clock of the
     attention kernel from the committed rocprofv3 counter summary, or None
     when it is missing, covers another workload or another kernel source."""
-    import hashlib
     if workload != "long" or not os.path.exists(ATTN_MFMA_COUNTERS):
         return None
     with open(ATTN_MFMA_COUNTERS) as f:
         text = f.read()
-    vals = dict(re.findall(r"^(mfma_busy_frac|effective_clock_ghz|kernel_source_sha256_16) = (\S+)$", text, re.M))
-    if len(vals) != 3:
+    vals = dict(re.findall(r"^(mfma_busy_frac|effective_clock_ghz|kernel_code_sha256_16) = (\S+)$", text, re.M))
+    if len(vals) != 3 or kernel_code_hash(ATTN_SOURCE) != vals["kernel_code_sha256_16"]:
         return None
-    with open(ATTN_SOURCE, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest()[:16] != vals["kernel_source_sha256_16"]:
-            return None
     return {"mfma_busy_frac": float(vals["mfma_busy_frac"]), "effective_clock_ghz": float(vals["effective_clock_ghz"])}
 
 

@@ -33,6 +33,9 @@
 // under the compute of tile i. Query tiles of a head are dealt out so each XCD
 // works on a contiguous run of neighbouring query tiles, whose key selections
 // overlap, while all XCDs share the same head's K/V in the MALL.
+// The finished O rows go to the tiled output, or straight to each real
+// token's row of a raster output (pad query slots are then not written), which
+// spares the layer a separate unpermute pass.
 #include "attn_tiles.hpp"
 
 namespace veda {
