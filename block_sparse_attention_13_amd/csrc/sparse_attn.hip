@@ -294,8 +294,11 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
 
   // Wave (qg, half): queries 32qg..32qg+31 against keys 64half..64half+63 of
   // every selected tile; the two halves are merged at the end.
+  // The two waves of a query group sit on different SIMDs (waves are dealt
+  // to SIMDs round robin), so a tile whose only real queries form one group
+  // keeps two SIMDs busy.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
-  const int qg = wave & 3, half = wave >> 2;
+  const int qg = (wave >> 1) & 3, half = wave & 1;
   const int l32 = lane % 32, h = lane / 32;
   const int32_t* sel = idx + (head_base + tq) * k_max;
   const unsigned nT = unsigned(hg.nT);
@@ -369,17 +372,36 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
   };
   const std::false_type more{};
   const std::true_type last{};
-  floatx16 sn[2];
-  int i = 0;
-  for (; i + 2 < kh; i += 2) {
-    iteration(more, i, sc, sn);
-    iteration(more, i + 1, sn, sc);
+  // With raster output, a query group made only of pad slots (border tiles)
+  // computes nothing: its waves only make their copies and keep the barriers
+  // (one per iteration but the last, as below), and nothing of it is written.
+  bool pad_group = false;
+  if (o_r && !hg.all_full) {
+    const BoxExtent e = box_extent(g, hg, tq);
+    if (!box_is_full(hg, e)) pad_group = uint32_t(box_slot_mask64(hg, e, 64 * (qg >> 1)) >> (32 * (qg & 1))) == 0u;
   }
-  if (i + 1 < kh) {
-    iteration(more, i, sc, sn);
-    iteration(last, i + 1, sn, sc);
+  if (pad_group) {
+    for (int i = 0; i + 1 < kh; ++i) {
+      const int cur = i & 1;
+      dma_issue<D>(plan, tile_src(plan.is_k ? jn2 : jn), lbuf + (plan.is_k ? cur : 2 + (cur ^ 1)) * S::kTileElems);
+      jn = jn2;
+      jn2 = sel[min(i + 3, kh - 1)];
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   } else {
-    iteration(last, i, sc, sn);
+    floatx16 sn[2];
+    int i = 0;
+    for (; i + 2 < kh; i += 2) {
+      iteration(more, i, sc, sn);
+      iteration(more, i + 1, sn, sc);
+    }
+    if (i + 1 < kh) {
+      iteration(more, i, sc, sn);
+      iteration(last, i + 1, sn, sc);
+    } else {
+      iteration(last, i, sc, sn);
+    }
   }
   __syncthreads();  // every wave is done with the tile buffers
 
@@ -426,7 +448,10 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
         if (orow) *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g4 + 4 * h) = wd;
       }
     }
-    if (lse_tile && h == 0) lse_tile[qg * 32 + l32] = (m + __log2f(l_tot)) * 0.69314718055994530942f;
+    // A pad query slot has no token in a raster output: its LSE is -inf there.
+    const bool pad_slot = o_r && !slot_is_real(hg, box_extent(g, hg, tq), qg * 32 + l32);
+    if (lse_tile && h == 0)
+      lse_tile[qg * 32 + l32] = pad_slot ? -__builtin_inff() : (m + __log2f(l_tot)) * 0.69314718055994530942f;
   }
 }
 

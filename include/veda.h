@@ -236,8 +236,10 @@ int veda_sparse_attn_fwd(const veda_geom* g, const void* q_tiled, const void* k_
  *   o_raster  out  raster bf16 [B, N, heads, d] with element strides `s` (channel stride 1): the
  *                  row of every real token of every head is written; nothing else is touched
  *   s         in   strides of o_raster (elements; multiples of 8, else VEDA_ERR_ALIGN)
+ *   lse       out  as veda_sparse_attn_fwd for real query slots; -inf for pad query slots, which
+ *                  have no raster row (a group of 32 pad slots is not computed at all)
  * For the same inputs, o_raster holds exactly the bytes veda_tile_unpermute of veda_sparse_attn_fwd's
- * o_tiled would give, and lse is identical.
+ * o_tiled would give, and lse matches veda_sparse_attn_fwd's on every real query slot.
  */
 int veda_sparse_attn_fwd_raster(const veda_geom* g, const void* q_tiled, const void* k_tiled,
                                 const void* v_tiled, const int32_t* idx, const int32_t* k_per_head,

@@ -84,8 +84,12 @@ def check_head(w, data, out, hd, ks, tiles, b=0, check_attention=True):
     o_back = V.tile_unpermute(o_tiled, geom)
     torch.cuda.synchronize()
     assert torch.equal(o_back[b, :, hd].view(torch.int16), out["o"][b, :, hd].view(torch.int16)), ("raster O", hd)
-    assert torch.equal(lse_tiled[b, hd].view(torch.int32), out["lse"][b, hd].view(torch.int32)), ("lse", hd)
     pos = O.tiled_position(w.grid, tile)
+    real = np.zeros(nT_max * 128, bool)
+    real[pos] = True
+    lse_r, lse_tl = out["lse"][b, hd].cpu().numpy().reshape(-1), lse_tiled[b, hd].cpu().numpy().reshape(-1)
+    assert np.array_equal(lse_r[real].view(np.int32), lse_tl[real].view(np.int32)), ("lse", hd)
+    assert np.all(np.isneginf(lse_r[~real])), ("raster lse of pad slots", hd)
     rows = np.flatnonzero(np.isfinite(r["lse"]))
     o_gpu = f32_of_bf16(out["o"][b, :, hd, :])
     compare_o(o_gpu[rows], r["o"][rows], f"{w.name} head {hd} O")
@@ -215,7 +219,12 @@ def test_fused_layer_matches_unfused(wname, heads, B, custom):
     torch.cuda.synchronize()
     assert torch.equal(out["idx"], idx)
     assert torch.equal(out["o"].view(torch.int16), o.view(torch.int16))
-    assert torch.equal(out["lse"].view(torch.int32), lse.view(torch.int32))
+    real = torch.zeros(lse.shape, dtype=torch.bool, device=lse.device)
+    for hd, tile in enumerate(w.head_tiles()):
+        pos = torch.from_numpy(O.tiled_position(w.grid, tile)).to(lse.device)
+        real[:, hd].view(w.B, -1)[:, pos] = True
+    assert torch.equal(out["lse"][real].view(torch.int32), lse[real].view(torch.int32))
+    assert torch.all(torch.isneginf(out["lse"][~real]))
     packed = torch.full((w.B, w.tokens, 2, w.heads, w.d), 0x7FC0, dtype=torch.int16, device="cuda")
     view = packed.view(torch.bfloat16)[:, :, 1]
     V.sparse_attn_fwd_raster(q_t, k_t, v_t, idx, geom, ks, out=view, with_lse=False)
