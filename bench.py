@@ -211,12 +211,37 @@ def cpu_baseline(w, data, sample_tiles: int, seconds_hint: float = 20.0):
                          if i.get("user_api") == "blas") or None
     except Exception:
         pass
-    return {
+    ref = {"idx": idx, "o": o, "lse": lse}
+    return ref, {
         "value": round(ms_layer, 1), "unit": "ms/layer", "cores": int(threads), "kind": "oracle",
         "sample": (f"head 0 of {w.heads}: full mask preparation ({t_prep:.1f} s) + attention of "
                    f"{len(tiles)} of {nT} query tiles ({t_attn:.1f} s), scaled to {nT} tiles x {w.heads} heads"),
         "stage_s": {"mask_preparation_head0": round(t_prep, 2), "attention_sampled_tiles": round(t_attn, 2)},
         "cpu_model": cpu_model, "numpy": np.__version__, "blas": blas,
+    }
+
+
+def parity_head0(w, gpu: dict, ref: dict) -> dict:
+    """The timed layer's head 0 against the oracle's run of the same head in
+    the CPU baseline: Top-k lists bit for bit; O as the parity tests measure
+    it (max-abs error beyond the bf16 rounding of the oracle value, and
+    relative L2); LSE max-abs, on every query the oracle computed."""
+    import numpy as np
+    import oracle as O
+    nT, k = w.tiles_per_head()[0], w.k_per_head()[0]
+    rows = np.flatnonzero(np.isfinite(ref["lse"]))
+    want = ref["o"][rows]
+    err = gpu["o"][rows].astype(np.float64) - want
+    half_ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(want), 2.0 ** -126))) - 8)
+    pos = O.tiled_position(w.grid, w.head_tiles()[0])
+    lse_err = np.abs(gpu["lse"].reshape(-1)[pos[rows]].astype(np.float64) - ref["lse"][rows])
+    return {
+        "head": 0, "queries_checked": int(len(rows)),
+        "topk_lists_bit_exact": bool(np.array_equal(gpu["idx"][:nT, :k], ref["idx"])),
+        "o_max_abs": float(np.abs(err).max()), "o_max_abs_beyond_bf16_rounding": float((np.abs(err) - half_ulp).max()),
+        "o_rel_l2": float(np.linalg.norm(err) / max(np.linalg.norm(want), 1e-30)),
+        "lse_max_abs": float(lse_err.max()),
+        "criteria": "bit-exact lists; O within 1e-2 beyond bf16 rounding and 5e-3 relative L2",
     }
 
 
@@ -322,6 +347,9 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0):
         del flush
     out.update({"data": data if keep_data else None, "valid_flops": valid_pair_flops(w, bufs["idx"].cpu().numpy()),
                 "bitmask": bufs["bitmask"] if keep_data else None})
+    if keep_data:  # head 0 of batch 0, for the parity check against the oracle
+        out["gpu_head0"] = {"idx": bufs["idx"][0, 0].cpu().numpy(), "o": bufs["o"][0, :, 0, :].float().cpu().numpy(),
+                            "lse": bufs["lse"][0, 0].cpu().numpy()}
     del bufs, q, k, v, wq, wk
     torch.cuda.empty_cache()
     return out
@@ -578,11 +606,13 @@ def main():
         dense["sparse_speedup"] = round(dense["attn_ms"] / stage_ms["sparse_attn"], 2)
         log(f"[bench] dense: {dense}")
 
-    cpu = None
+    cpu, parity = None, None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(w, data, args.cpu_sample_tiles)
+        ref, cpu = cpu_baseline(w, data, args.cpu_sample_tiles)
         log(f"[bench] cpu baseline: {cpu}")
+        parity = parity_head0(w, r["gpu_head0"], ref)
+        log(f"[bench] parity of head 0 against the oracle: {parity}")
 
     line = {
         "metric": "ms/layer + effective sparse-attn TFLOP/s (% bf16 MFMA peak) at 245K tok, 95% sparse",
@@ -615,6 +645,7 @@ def main():
                      "kernel": "sparse_attn_fwd_kernel<128>", "flops_per_launch": f_attn,
                      "counters": attention_mfma_counters(args.workload)},
         "cpu_baseline": cpu,
+        "parity_head0": parity,
         "pages_context": {
             "note": "the Veda pages' own figures, context only: their layer includes the MLP, and they state "
                     "neither the GPU nor the precision, so vs_baseline stays null",
