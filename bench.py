@@ -305,7 +305,7 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0):
         if ev is not None:
             ev[3].record(stream)
         V.sparse_attn_fwd_raster(bufs["q_t"], bufs["k_t"], bufs["v_t"], bufs["idx"], geom, ks,
-                                 out=bufs["o"], lse=bufs["lse"])
+                                 out=bufs["o"], lse=bufs["lse"], work_queue=bufs["queue"])
         if ev is not None:
             ev[4].record(stream)
 
@@ -374,14 +374,15 @@ def dense_reference(V, w, data, trip_bitmask=None, steps=2, warmup=1):
     idx = torch.arange(nT, dtype=torch.int32, device=dev).expand(w.B, w.heads, nT, nT).contiguous()
     o_t = torch.empty_like(q_t)
     lse = torch.empty((w.B, w.heads, nT, 128), dtype=torch.float32, device=dev)
+    queue = V.attn_queue(dev)
     stream = torch.cuda.current_stream(dev)
     for _ in range(warmup):
-        V.sparse_attn_fwd(q_t, k_t, v_t, idx, geom, nts, o_t=o_t, lse=lse)
+        V.sparse_attn_fwd(q_t, k_t, v_t, idx, geom, nts, o_t=o_t, lse=lse, work_queue=queue)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     ev[0].record(stream)
     for i in range(steps):
-        V.sparse_attn_fwd(q_t, k_t, v_t, idx, geom, nts, o_t=o_t, lse=lse)
+        V.sparse_attn_fwd(q_t, k_t, v_t, idx, geom, nts, o_t=o_t, lse=lse, work_queue=queue)
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))

@@ -14,6 +14,7 @@ Python: the five steps of the layer are HIP kernels.
   tile_permute_stats      raster Q or K -> token-major tiles + TripPool stats, one pass
   trippool_project_score  stats + W_q, W_k -> features, tile scores
   sparse_attn_fwd_raster  sparse_attn_fwd writing raster O (no unpermute pass)
+  attn_queue       workspace of the attention calls' work queue (query tiles handed out at run time)
   layer_forward    the layer: tile_permute_stats of Q and K, tile_permute of V,
                    trippool_project_score, topk_mask, sparse_attn_fwd_raster
 
@@ -50,7 +51,8 @@ from ._lib import VedaError
 
 __all__ = ["Geometry", "VedaError", "tile_permute", "tile_permute_stats", "tile_unpermute", "trippool_score",
            "trippool_project_score", "topk_mask", "sparse_attn_fwd_raster",
-           "sparse_attn_fwd", "layer_forward", "dense_index", "teacher_tile_max", "mask_overlap", "tile_recall",
+           "sparse_attn_fwd", "attn_queue", "layer_forward",
+           "dense_index", "teacher_tile_max", "mask_overlap", "tile_recall",
            "head_sq_error", "candidate_tiles", "tile_search", "distill_kl", "distill_grad", "adam_step",
            "distill_train", "TILE_TOKENS", "TOKEN_MAJOR", "CHANNEL_MAJOR"]
 
@@ -269,6 +271,29 @@ def topk_mask(scores: torch.Tensor, geom: Geometry, k_per_head: Sequence[int], k
     return idx, bitmask
 
 
+ATTN_QUEUE_BYTES = 64
+
+
+def attn_queue(device) -> torch.Tensor:
+    """Workspace of the attention work queue (each attention call clears it
+    on its stream first; calls that may overlap need separate ones)."""
+    return torch.empty(ATTN_QUEUE_BYTES // 4, dtype=torch.int32, device=device)
+
+
+def _queue_ptr(work_queue, dynamic, device):
+    """Device pointer of the work-queue workspace: None (fixed per-XCD shares)
+    unless `dynamic`; a fresh workspace when none is given."""
+    if not dynamic:
+        return None
+    if work_queue is None:
+        work_queue = attn_queue(device)
+    if (work_queue.dtype != torch.int32 or work_queue.device != device or not work_queue.is_contiguous()
+            or work_queue.numel() * 4 < ATTN_QUEUE_BYTES):
+        raise ValueError(f"work_queue must be a contiguous int32 tensor of {ATTN_QUEUE_BYTES // 4} elements "
+                         f"on {device}")
+    return work_queue.data_ptr()
+
+
 def _attn_args(q_t, k_t, v_t, idx, geom, k_per_head, with_lse, lse):
     tshape = _tiled_shape(geom, geom.head_dim)
     for name, t in (("q_tiled", q_t), ("k_tiled", k_t)):
@@ -291,10 +316,12 @@ def _attn_args(q_t, k_t, v_t, idx, geom, k_per_head, with_lse, lse):
 def sparse_attn_fwd_raster(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, idx: torch.Tensor,
                            geom: Geometry, k_per_head: Sequence[int], scale: Optional[float] = None,
                            with_lse: bool = True, out: Optional[torch.Tensor] = None,
-                           lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                           lse: Optional[torch.Tensor] = None, work_queue: Optional[torch.Tensor] = None,
+                           dynamic: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """sparse_attn_fwd writing O straight into raster order [B, N, heads, d]
     (`out` may be any strided view with unit channel stride): the bytes
-    tile_unpermute of the tiled O would give, without that pass."""
+    tile_unpermute of the tiled O would give, without that pass. `work_queue`
+    and `dynamic` as in sparse_attn_fwd."""
     ks, k_max, lse = _attn_args(q_t, k_t, v_t, idx, geom, k_per_head, with_lse, lse)
     if out is None:
         out = torch.empty((geom.B, geom.tokens, geom.n_heads, geom.head_dim), dtype=torch.bfloat16,
@@ -303,18 +330,23 @@ def sparse_attn_fwd_raster(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tens
     sc = float(scale) if scale is not None else 0.0
     _lib.check(_lib.lib.veda_sparse_attn_fwd_raster(
         geom.c, q_t.data_ptr(), k_t.data_ptr(), v_t.data_ptr(), idx.data_ptr(), _lib.int_array(ks), int(k_max), sc,
-        out.data_ptr(), s, lse.data_ptr() if lse is not None else None, _stream(q_t)), "veda_sparse_attn_fwd_raster")
+        out.data_ptr(), s, lse.data_ptr() if lse is not None else None, _queue_ptr(work_queue, dynamic, q_t.device),
+        _stream(q_t)), "veda_sparse_attn_fwd_raster")
     return out, lse
 
 
 def sparse_attn_fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, idx: torch.Tensor, geom: Geometry,
                     k_per_head: Sequence[int], scale: Optional[float] = None, with_lse: bool = True,
-                    o_t: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+                    o_t: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    work_queue: Optional[torch.Tensor] = None, dynamic: bool = True
                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Tile-skipping attention over the selected key tiles. Q and K are
     token-major tiles, V channel-major ([B, heads, nT_max, d, 128]); returns
     tiled O (bf16, token-major) and LSE [B, heads, nT_max, 128] (fp32,
-    natural log)."""
+    natural log). With `dynamic` the query tiles are handed out through a
+    work queue (`work_queue`, from attn_queue, or a fresh one), which keeps
+    XCDs at different clocks busy to the end; the outputs are the same bytes
+    either way."""
     tshape = _tiled_shape(geom, geom.head_dim)
     for name, t in (("q_tiled", q_t), ("k_tiled", k_t)):
         _need(t, torch.bfloat16, tshape, name)
@@ -336,7 +368,8 @@ def sparse_attn_fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, idx
     sc = float(scale) if scale is not None else 0.0
     _lib.check(_lib.lib.veda_sparse_attn_fwd(geom.c, q_t.data_ptr(), k_t.data_ptr(), v_t.data_ptr(), idx.data_ptr(),
                                              _lib.int_array(ks), int(k_max), sc, o_t.data_ptr(),
-                                             lse.data_ptr() if lse is not None else None, _stream(q_t)),
+                                             lse.data_ptr() if lse is not None else None,
+                                             _queue_ptr(work_queue, dynamic, q_t.device), _stream(q_t)),
                "veda_sparse_attn_fwd")
     return o_t, lse
 
@@ -347,8 +380,9 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.
     """One Veda attention layer: permute Q/K/V (the TripPool statistics of Q
     and K taken in the same pass), projections and tile scores, Top-k mask,
     tile-skipping attention writing raster O. `buffers` (from a previous
-    call) reuses every output allocation. Returns all intermediates and `o`
-    (no tiled O: sparse_attn_fwd + tile_unpermute give the same `o`)."""
+    call) reuses every output allocation. Returns all intermediates, `o`
+    (no tiled O: sparse_attn_fwd + tile_unpermute give the same `o`) and the
+    attention's work-queue workspace `queue`."""
     b = buffers if buffers is not None else {}
     b["q_t"], b["stats_q"] = tile_permute_stats(q, geom, b.get("q_t"), b.get("stats_q"))
     b["k_t"], b["stats_k"] = tile_permute_stats(k, geom, b.get("k_t"), b.get("stats_k"))
@@ -357,8 +391,10 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.
                                  {n: b[n] for n in ("feat_q", "feat_k", "scores")} if "scores" in b else None)
     b.update(est)
     b["idx"], b["bitmask"] = topk_mask(b["scores"], geom, k_per_head, idx=b.get("idx"), bitmask=b.get("bitmask"))
+    if b.get("queue") is None:
+        b["queue"] = attn_queue(q.device)
     b["o"], b["lse"] = sparse_attn_fwd_raster(b["q_t"], b["k_t"], b["v_t"], b["idx"], geom, k_per_head, scale,
-                                              out=b.get("o"), lse=b.get("lse"))
+                                              out=b.get("o"), lse=b.get("lse"), work_queue=b["queue"])
     return b
 
 

@@ -80,11 +80,12 @@ def _load():
                                    c_void_p]
     lib.veda_topk_mask.restype = ctypes.c_int
     lib.veda_sparse_attn_fwd.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_void_p,
-                                         POINTER(c_int32), c_int32, c_float, c_void_p, c_void_p, c_void_p]
+                                         POINTER(c_int32), c_int32, c_float, c_void_p, c_void_p, c_void_p,
+                                         c_void_p]
     lib.veda_sparse_attn_fwd.restype = ctypes.c_int
     lib.veda_sparse_attn_fwd_raster.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_void_p,
                                                 POINTER(c_int32), c_int32, c_float, c_void_p, VedaRasterStrides,
-                                                c_void_p, c_void_p]
+                                                c_void_p, c_void_p, c_void_p]
     lib.veda_sparse_attn_fwd_raster.restype = ctypes.c_int
     lib.veda_teacher_tile_max.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p]
     lib.veda_teacher_tile_max.restype = ctypes.c_int

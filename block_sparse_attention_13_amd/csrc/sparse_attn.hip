@@ -33,6 +33,11 @@
 // under the compute of tile i. Query tiles of a head are dealt out so each XCD
 // works on a contiguous run of neighbouring query tiles, whose key selections
 // overlap, while all XCDs share the same head's K/V in the MALL.
+// Under the socket power limit the XCDs run at different clocks, so a fixed
+// deal leaves the fastest XCDs idle while the slowest finishes. With a work
+// queue the grid is one-dimensional and each XCD first works through the
+// query tiles the fixed deal would have given it, then the last ones of
+// every XCD are handed out through atomic counters to whichever XCD is free.
 // The finished O rows go to the tiled output, or straight to each real
 // token's row of a raster output (pad query slots are then not written), which
 // spares the layer a separate unpermute pass.
@@ -262,20 +267,73 @@ __device__ __forceinline__ void hot_tile(WaveState<D>& w, const floatx16 (&s_cur
   if constexpr (!kLast) mx_next = row_max_base2(mx, scale_log2);
 }
 
+// Work items are the linear indices bx + nT_max (hd + heads b) of a
+// (nT_max, heads, B) grid. Queue x (x < 8) holds items x, x + 8, x + 16, ...:
+// those a grid of that shape deals to XCD x, since workgroups go to the XCDs
+// round robin. In the one-dimensional grid workgroup i is taken to sit on XCD
+// i % 8 (only locality rests on this) and, for i / 8 < n_static, simply does
+// item 8 (i / 8) + i % 8. Any other workgroup draws a ticket from counter 8;
+// a ticket below the number of remaining items guarantees that an item is
+// left somewhere, so it takes the next item of its own queue (counter x
+// counts the draws past n_static from queue x) or else of the next queues in
+// turn, and one pass finds it: a queue once exhausted stays exhausted.
+// Returns -1 for a workgroup without an item. `word` is LDS scratch for the
+// broadcast (inside the tile buffers: a second LDS object would make the
+// compiler wait for every LDS-DMA before each LDS read).
+__device__ __forceinline__ int32_t take_item(const GeoTable& g, int32_t* queue, int32_t n_static, int32_t* word) {
+  const int32_t total = g.nT_max * g.heads * g.B;
+  const int home = blockIdx.x % 8;
+  const int32_t n = blockIdx.x / 8;
+  if (n < n_static) return 8 * n + home;
+  if (threadIdx.x == 0) {
+    int32_t item = -1;
+    if (atomicAdd(&queue[8], 1) < total - 8 * n_static) {
+      for (int t = 0; t < 8; ++t) {
+        const int x = (home + t) % 8;
+        const int32_t m = n_static + atomicAdd(&queue[x], 1);
+        if (m < (total - x + 7) / 8) {
+          item = 8 * m + x;
+          break;
+        }
+      }
+    }
+    *word = item;
+  }
+  __syncthreads();
+  const int32_t item = __builtin_amdgcn_readfirstlane(*word);
+  __syncthreads();  // every wave has read the word before the tile copies overwrite it
+  return item;
+}
+
+__global__ void queue_reset_kernel(int32_t* queue) {
+  if (threadIdx.x < kAttnQueueInts) queue[threadIdx.x] = 0;
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
     GeoTable g, const uint16_t* __restrict__ q_t, const uint16_t* __restrict__ k_t,
     const uint16_t* __restrict__ v_t, const int32_t* __restrict__ idx, int32_t k_max, float scale_log2,
     uint16_t* __restrict__ o_t, float* __restrict__ lse, uint16_t* __restrict__ o_r, int64_t osb, int64_t osn,
-    int64_t osh) {
+    int64_t osh, int32_t* __restrict__ queue, int32_t n_static) {
   using S = AttnShape<D>;
   // K buffers lds[0..1], V buffers lds[2..3]; after the loop the space holds
   // the half merge.
   __shared__ __attribute__((aligned(16))) uint16_t lds[4][S::kTileElems];
 
-  const int hd = blockIdx.y, b = blockIdx.z;
+  int32_t bx, hd, b;
+  if (queue) {
+    const int32_t item = take_item(g, queue, n_static, reinterpret_cast<int32_t*>(&lds[0][0]));
+    if (item < 0) return;
+    bx = item % g.nT_max;
+    hd = (item / g.nT_max) % g.heads;
+    b = item / (g.nT_max * g.heads);
+  } else {
+    bx = blockIdx.x;
+    hd = blockIdx.y;
+    b = blockIdx.z;
+  }
   const HeadGeo hg = g.h[hd];
-  const int32_t tq = xcd_tile_order(blockIdx.x, g.nT_max);
+  const int32_t tq = xcd_tile_order(bx, g.nT_max);
   const int64_t head_base = (int64_t(b) * g.heads + hd) * g.nT_max;
   const int64_t tile_elems = S::kTileElems;
   // Tiled output o_t, or (o_r non-null) raster output: then each real query
@@ -459,15 +517,28 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
 
 hipError_t launch_sparse_attn(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t, const uint16_t* v_t,
                               const int32_t* idx, int32_t k_max, float scale, uint16_t* o_t, float* lse,
-                              uint16_t* o_r, int64_t osb, int64_t osn, int64_t osh, hipStream_t s) {
-  const dim3 grid(g.nT_max, g.heads, g.B);
+                              uint16_t* o_r, int64_t osb, int64_t osn, int64_t osh, int32_t* queue, hipStream_t s) {
+  dim3 grid(g.nT_max, g.heads, g.B);
+  int32_t n_static = 0;
+  if (queue) {
+    // The last sixteenth of each XCD's share is handed out at run time, and
+    // each XCD has workgroups for up to a further sixteenth taken from the
+    // others (enough for per-XCD speeds that differ by about 12%).
+    const int32_t total = g.nT_max * g.heads * g.B;
+    const int32_t per = total / 8, per_max = (total + 7) / 8;
+    n_static = per - per / 16;
+    grid = dim3(8 * (per_max + per / 16 + 1), 1, 1);
+    queue_reset_kernel<<<1, 64, 0, s>>>(queue);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const float scale_log2 = scale * 1.44269504088896340736f;
   if (g.d == 128)
     sparse_attn_fwd_kernel<128><<<grid, kThreads, 0, s>>>(g, q_t, k_t, v_t, idx, k_max, scale_log2, o_t, lse, o_r,
-                                                         osb, osn, osh);
+                                                         osb, osn, osh, queue, n_static);
   else
     sparse_attn_fwd_kernel<64><<<grid, kThreads, 0, s>>>(g, q_t, k_t, v_t, idx, k_max, scale_log2, o_t, lse, o_r,
-                                                        osb, osn, osh);
+                                                        osb, osn, osh, queue, n_static);
   return hipGetLastError();
 }
 

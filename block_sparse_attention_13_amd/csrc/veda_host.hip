@@ -104,6 +104,15 @@ int launched(hipError_t e) { return e == hipSuccess ? VEDA_OK : VEDA_ERR_LAUNCH;
     if (rc_ != VEDA_OK) return rc_; \
   } while (0)
 
+// The attention work queue: 16-byte aligned, and every item index (up to
+// B * heads * nT_max) and the launch size stay far inside int32.
+int check_queue(const GeoTable& t, const int32_t* queue) {
+  if (!queue) return VEDA_OK;
+  if (!aligned16(queue)) return VEDA_ERR_ALIGN;
+  if (int64_t(t.B) * t.heads * t.nT_max > (int64_t(1) << 28)) return VEDA_ERR_SHAPE;
+  return VEDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -230,7 +239,7 @@ int veda_topk_mask(const veda_geom* g, const float* scores, const int32_t* k_per
 
 int veda_sparse_attn_fwd(const veda_geom* g, const void* q_tiled, const void* k_tiled, const void* v_tiled,
                          const int32_t* idx, const int32_t* k_per_head, int32_t k_max, float softmax_scale,
-                         void* o_tiled, float* lse, void* stream) {
+                         void* o_tiled, float* lse, int32_t* work_queue, void* stream) {
   GeoTable t;
   VEDA_TRY(build_table(g, &t));
   if (!q_tiled || !k_tiled || !v_tiled || !idx || !o_tiled) return VEDA_ERR_NULL;
@@ -238,17 +247,19 @@ int veda_sparse_attn_fwd(const veda_geom* g, const void* q_tiled, const void* k_
   for (const void* p : {q_tiled, k_tiled, v_tiled, static_cast<const void*>(idx), static_cast<const void*>(o_tiled)})
     if (!aligned16(p)) return VEDA_ERR_ALIGN;
   if (lse && !aligned16(lse)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_queue(t, work_queue));
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) softmax_scale = 1.0f / std::sqrt(float(t.d));
   VEDA_TRY(check_device());
   return launched(veda::launch_sparse_attn(
       t, static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_tiled),
       static_cast<const uint16_t*>(v_tiled), idx, k_max, softmax_scale, static_cast<uint16_t*>(o_tiled), lse,
-      nullptr, 0, 0, 0, static_cast<hipStream_t>(stream)));
+      nullptr, 0, 0, 0, work_queue, static_cast<hipStream_t>(stream)));
 }
 
 int veda_sparse_attn_fwd_raster(const veda_geom* g, const void* q_tiled, const void* k_tiled, const void* v_tiled,
                                 const int32_t* idx, const int32_t* k_per_head, int32_t k_max, float softmax_scale,
-                                void* o_raster, veda_raster_strides s, float* lse, void* stream) {
+                                void* o_raster, veda_raster_strides s, float* lse, int32_t* work_queue,
+                                void* stream) {
   GeoTable t;
   VEDA_TRY(build_table(g, &t));
   if (!q_tiled || !k_tiled || !v_tiled || !idx || !o_raster) return VEDA_ERR_NULL;
@@ -256,13 +267,14 @@ int veda_sparse_attn_fwd_raster(const veda_geom* g, const void* q_tiled, const v
   for (const void* p : {q_tiled, k_tiled, v_tiled, static_cast<const void*>(idx), static_cast<const void*>(o_raster)})
     if (!aligned16(p)) return VEDA_ERR_ALIGN;
   if (lse && !aligned16(lse)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_queue(t, work_queue));
   VEDA_TRY(check_strides(s));
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) softmax_scale = 1.0f / std::sqrt(float(t.d));
   VEDA_TRY(check_device());
   return launched(veda::launch_sparse_attn(
       t, static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_tiled),
       static_cast<const uint16_t*>(v_tiled), idx, k_max, softmax_scale, nullptr, lse,
-      static_cast<uint16_t*>(o_raster), s.b, s.n, s.h, static_cast<hipStream_t>(stream)));
+      static_cast<uint16_t*>(o_raster), s.b, s.n, s.h, work_queue, static_cast<hipStream_t>(stream)));
 }
 
 int veda_teacher_tile_max(const veda_geom* g, const void* q_tiled, const void* k_tiled, const float* lse_dense,

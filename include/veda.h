@@ -84,6 +84,8 @@ extern "C" {
 #define VEDA_TILE_TOKENS 128
 #define VEDA_MAX_HEADS 128
 #define VEDA_MAX_TILES 8192
+/* Size of the work-queue workspace the attention calls may take. */
+#define VEDA_ATTN_QUEUE_BYTES 64
 
 /* Layout of a tiled tensor: token-major [.., 128, d] or channel-major [.., d, 128]. */
 enum { VEDA_TILED_TOKEN_MAJOR = 0, VEDA_TILED_CHANNEL_MAJOR = 1 };
@@ -222,11 +224,19 @@ int veda_topk_mask(const veda_geom* g, const float* scores, const int32_t* k_per
  *                                   output of a zero query
  *   lse                        out  fp32 [B, heads, nT_max, 128], natural log of the softmax
  *                                   denominator of the scaled logits; -inf for tiles >= nT_hd; may be NULL
+ *   work_queue                 tmp  device workspace of VEDA_ATTN_QUEUE_BYTES (16-byte aligned), or
+ *                                   NULL. With it, query tiles are handed out at run time so that
+ *                                   XCDs running at different clocks finish together; the call
+ *                                   first clears it with a kernel on `stream` (no memset). Calls
+ *                                   that may run at the same time need separate workspaces. With
+ *                                   NULL every XCD gets a fixed share. The outputs are the same
+ *                                   bytes either way. With a workspace, B * heads * nT_max must
+ *                                   not exceed 2^28 (else VEDA_ERR_SHAPE).
  */
 int veda_sparse_attn_fwd(const veda_geom* g, const void* q_tiled, const void* k_tiled,
                          const void* v_tiled, const int32_t* idx, const int32_t* k_per_head,
                          int32_t k_max, float softmax_scale, void* o_tiled, float* lse,
-                         void* stream);
+                         int32_t* work_queue, void* stream);
 
 /*
  * The same attention forward writing O straight into raster order, which
@@ -244,7 +254,7 @@ int veda_sparse_attn_fwd(const veda_geom* g, const void* q_tiled, const void* k_
 int veda_sparse_attn_fwd_raster(const veda_geom* g, const void* q_tiled, const void* k_tiled,
                                 const void* v_tiled, const int32_t* idx, const int32_t* k_per_head,
                                 int32_t k_max, float softmax_scale, void* o_raster,
-                                veda_raster_strides s, float* lse, void* stream);
+                                veda_raster_strides s, float* lse, int32_t* work_queue, void* stream);
 
 /*
  * Inverse re-tiling: raster x[b, n, hd, :] = tiled x at the slot of token n

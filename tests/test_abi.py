@@ -105,15 +105,22 @@ def test_call_errors_precede_any_device_work():
     assert L.veda_topk_mask(g.c, FAKE, _lib.int_array([5]), 4, FAKE, None, None) == -4
     assert L.veda_topk_mask(g.c, FAKE, None, 4, FAKE, None, None) == -1
     assert L.veda_topk_mask(g.c, FAKE, ks, 4, FAKE, FAKE + 4, None) == -5
-    assert L.veda_sparse_attn_fwd(g.c, FAKE, FAKE, FAKE, FAKE, _lib.int_array([9]), 8, 0.0, FAKE, None, None) == -4
-    assert L.veda_sparse_attn_fwd(g.c, FAKE, None, FAKE, FAKE, ks, 4, 0.0, FAKE, None, None) == -1
-    assert L.veda_sparse_attn_fwd(g.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE, FAKE + 4, None) == -5
-    assert L.veda_sparse_attn_fwd_raster(g.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, None, s, None, None) == -1
+    assert L.veda_sparse_attn_fwd(g.c, FAKE, FAKE, FAKE, FAKE, _lib.int_array([9]), 8, 0.0, FAKE, None, None,
+                                  None) == -4
+    assert L.veda_sparse_attn_fwd(g.c, FAKE, None, FAKE, FAKE, ks, 4, 0.0, FAKE, None, None, None) == -1
+    assert L.veda_sparse_attn_fwd(g.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE, FAKE + 4, None, None) == -5
+    assert L.veda_sparse_attn_fwd(g.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE, None, FAKE + 4, None) == -5
+    assert L.veda_sparse_attn_fwd_raster(g.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, None, s, None, None, None) == -1
     assert L.veda_sparse_attn_fwd_raster(g.c, FAKE, FAKE, FAKE, FAKE, _lib.int_array([9]), 8, 0.0, FAKE, s, None,
-                                         None) == -4
+                                         None, None) == -4
     assert L.veda_sparse_attn_fwd_raster(g.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE,
-                                         _lib.VedaRasterStrides(1024, 132, 128), None, None) == -5
-    assert L.veda_sparse_attn_fwd_raster(g.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE, s, FAKE + 4, None) == -5
+                                         _lib.VedaRasterStrides(1024, 132, 128), None, None, None) == -5
+    assert L.veda_sparse_attn_fwd_raster(g.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE, s, FAKE + 4, None, None) == -5
+    assert L.veda_sparse_attn_fwd_raster(g.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE, s, None, FAKE + 8,
+                                         None) == -5
+    # a work queue needs B * heads * nT_max <= 2^28 (here 65535 * 8192 tiles)
+    big = _geom(B=65535, grid=(1, 128, 8192), tiles=((1, 8, 16),))
+    assert L.veda_sparse_attn_fwd(big.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE, None, FAKE, None) == -2
     assert L.veda_teacher_tile_max(g.c, FAKE, FAKE, None, 0.0, FAKE, None) == -1
     assert L.veda_teacher_tile_max(g.c, FAKE, FAKE, FAKE, 0.0, FAKE + 4, None) == -5
     assert L.veda_teacher_tile_max(_geom(tiles=((2, 2, 2),)).c, FAKE, FAKE, FAKE, 0.0, FAKE, None) == -3
@@ -143,7 +150,7 @@ def test_valid_call_without_gpu_reports_device_error():
     assert _lib.lib.veda_tile_permute_stats(g.c, FAKE, s, FAKE, FAKE, None) == -6
     assert _lib.lib.veda_trippool_project_score(g.c, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, None) == -6
     assert _lib.lib.veda_sparse_attn_fwd_raster(g.c, FAKE, FAKE, FAKE, FAKE, _lib.int_array([3]), 4, 0.0, FAKE, s,
-                                                None, None) == -6
+                                                None, FAKE, None) == -6
 
 
 def test_python_wrappers_validate_before_calling():

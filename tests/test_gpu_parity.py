@@ -237,6 +237,36 @@ def _random_workload(grid, tiles, d, r, heads, seed, keep=None, k=None):
     return datagen.Workload("custom", 1, heads, d, r, grid, tuple(tiles), keep, k, False, seed, "custom")
 
 
+def test_work_queue_matches_fixed_deal():
+    """Handing query tiles out through the work queue changes only which
+    workgroup computes a tile: tiled O, raster O and LSE are the same bytes
+    as with fixed per-XCD shares. One workspace, filled with garbage first,
+    serves every call, the later workloads smaller (d 128 then 64, item
+    counts that are not multiples of 8): each call clears it itself."""
+    V = _lib()
+    queue = torch.full((V.ATTN_QUEUE_BYTES // 4,), 123456, dtype=torch.int32, device="cuda")
+    cases = [dataclasses.replace(W["480p"].with_heads(4), B=2),
+             _random_workload((3, 9, 17), [(1, 8, 16), (8, 4, 4)], 128, 32, heads=2, seed=3, k=2),
+             _random_workload((5, 6, 20), [(2, 4, 16)], 64, 64, heads=3, seed=4, k=3)]
+    for w in cases:
+        say(f"[queue] {w.description} B {w.B} items {max(w.tiles_per_head()) * w.heads * w.B}")
+        data = datagen.generate(w)
+        geom, out, _ = run_layer(w, data)
+        ks = w.k_per_head()
+        args = (out["q_t"], out["k_t"], out["v_t"], out["idx"], geom, ks)
+        o_f, lse_f = V.sparse_attn_fwd(*args, dynamic=False)
+        r_f, rl_f = V.sparse_attn_fwd_raster(*args, dynamic=False)
+        for _ in range(2):
+            o_d, lse_d = V.sparse_attn_fwd(*args, work_queue=queue)
+            r_d, rl_d = V.sparse_attn_fwd_raster(*args, work_queue=queue)
+            torch.cuda.synchronize()
+            assert torch.equal(o_d.view(torch.int16), o_f.view(torch.int16))
+            assert torch.equal(lse_d.view(torch.int32), lse_f.view(torch.int32))
+            assert torch.equal(r_d.view(torch.int16), r_f.view(torch.int16))
+            assert torch.equal(rl_d.view(torch.int32), rl_f.view(torch.int32))
+        assert torch.equal(out["o"].view(torch.int16), r_f.view(torch.int16))
+
+
 @pytest.mark.parametrize("grid,tiles,d,r", [
     ((5, 6, 20), [(2, 4, 16)], 64, 64),
     ((3, 9, 17), [(1, 8, 16), (8, 4, 4)], 128, 32),
@@ -383,7 +413,8 @@ def test_invalid_call_raises_and_writes_nothing():
 
 
 def test_layer_is_deterministic():
-    """Three runs of the whole layer give the same bytes in every output."""
+    """Three runs of the whole layer give the same bytes in every output
+    (the work-queue workspace is scratch: its counts vary with timing)."""
     V = _lib()
     w = W["480p"]
     data = datagen.generate(w)
@@ -392,6 +423,8 @@ def test_layer_is_deterministic():
         again = V.layer_forward(q, k, v, wq, wk, geom, w.k_per_head())
         torch.cuda.synchronize()
         for name, t in first.items():
+            if name == "queue":
+                continue
             a, b = t.contiguous().view(torch.uint8), again[name].contiguous().view(torch.uint8)
             assert torch.equal(a, b), name
 
@@ -412,8 +445,9 @@ def _guards_intact(buf):
 
 
 def test_outputs_stay_in_their_buffers():
-    """Every call writes inside its outputs: 4 KiB before and after each one
-    stay untouched (ragged boxes, three tile shapes, B = 2)."""
+    """Every call writes inside its outputs and the attention's work-queue
+    workspace: 4 KiB before and after each one stay untouched (ragged boxes,
+    three tile shapes, B = 2)."""
     V = _lib()
     w = dataclasses.replace(W["hc"].with_heads(6), B=2)
     data = datagen.generate(w)
@@ -427,7 +461,7 @@ def test_outputs_stay_in_their_buffers():
         "feat_q": ((B, Hh, nT, r), torch.bfloat16), "feat_k": ((B, Hh, nT, r), torch.bfloat16),
         "scores": ((B, Hh, nT, nT), torch.float32), "idx": ((B, Hh, nT, kmax), torch.int32),
         "bitmask": ((B, Hh, nT, (nT + 31) // 32), torch.int32), "lse": ((B, Hh, nT, 128), torch.float32),
-        "o": ((B, w.tokens, Hh, d), torch.bfloat16),
+        "o": ((B, w.tokens, Hh, d), torch.bfloat16), "queue": ((V.ATTN_QUEUE_BYTES // 4,), torch.int32),
     }
     bufs, raw = {}, {}
     for name, (shape, dt) in shapes.items():
