@@ -305,6 +305,8 @@ __device__ __forceinline__ int32_t take_item(const GeoTable& g, int32_t* queue, 
   return item;
 }
 
+constexpr int32_t kQueueMinItems = 1024;  // 4 query tiles per CU
+
 __global__ void queue_reset_kernel(int32_t* queue) {
   if (threadIdx.x < kAttnQueueInts) queue[threadIdx.x] = 0;
 }
@@ -520,12 +522,15 @@ hipError_t launch_sparse_attn(const GeoTable& g, const uint16_t* q_t, const uint
                               uint16_t* o_r, int64_t osb, int64_t osn, int64_t osh, int32_t* queue, hipStream_t s) {
   dim3 grid(g.nT_max, g.heads, g.B);
   int32_t n_static = 0;
+  const int64_t total = int64_t(g.nT_max) * g.heads * g.B;
+  // A grid of a few workgroups per CU has no tail worth balancing: there the
+  // queue is not used (nor cleared), which saves the extra launch.
+  if (total < kQueueMinItems) queue = nullptr;
   if (queue) {
     // The last sixteenth of each XCD's share is handed out at run time, and
     // each XCD has workgroups for up to a further sixteenth taken from the
     // others (enough for per-XCD speeds that differ by about 12%).
-    const int32_t total = g.nT_max * g.heads * g.B;
-    const int32_t per = total / 8, per_max = (total + 7) / 8;
+    const int32_t per = int32_t(total / 8), per_max = int32_t((total + 7) / 8);
     n_static = per - per / 16;
     grid = dim3(8 * (per_max + per / 16 + 1), 1, 1);
     queue_reset_kernel<<<1, 64, 0, s>>>(queue);

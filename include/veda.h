@@ -229,9 +229,10 @@ int veda_topk_mask(const veda_geom* g, const float* scores, const int32_t* k_per
  *                                   XCDs running at different clocks finish together; the call
  *                                   first clears it with a kernel on `stream` (no memset). Calls
  *                                   that may run at the same time need separate workspaces. With
- *                                   NULL every XCD gets a fixed share. The outputs are the same
- *                                   bytes either way. With a workspace, B * heads * nT_max must
- *                                   not exceed 2^28 (else VEDA_ERR_SHAPE).
+ *                                   NULL, or when B * heads * nT_max < 1024 (nothing to balance),
+ *                                   every XCD gets a fixed share and the workspace is not touched.
+ *                                   The outputs are the same bytes either way. With a workspace,
+ *                                   B * heads * nT_max must not exceed 2^28 (else VEDA_ERR_SHAPE).
  */
 int veda_sparse_attn_fwd(const veda_geom* g, const void* q_tiled, const void* k_tiled,
                          const void* v_tiled, const int32_t* idx, const int32_t* k_per_head,

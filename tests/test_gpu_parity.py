@@ -242,11 +242,15 @@ def test_work_queue_matches_fixed_deal():
     workgroup computes a tile: tiled O, raster O and LSE are the same bytes
     as with fixed per-XCD shares. One workspace, filled with garbage first,
     serves every call, the later workloads smaller (d 128 then 64, item
-    counts that are not multiples of 8): each call clears it itself."""
+    counts B * heads * nT_max of 2688, 1700 and 1260, the last two not
+    multiples of 8): each call clears it itself. Below 1024 items the
+    fixed deal is used and the workspace is not touched."""
     V = _lib()
     queue = torch.full((V.ATTN_QUEUE_BYTES // 4,), 123456, dtype=torch.int32, device="cuda")
     cases = [dataclasses.replace(W["480p"].with_heads(4), B=2),
-             _random_workload((3, 9, 17), [(1, 8, 16), (8, 4, 4)], 128, 32, heads=2, seed=3, k=2),
+             dataclasses.replace(_random_workload((5, 37, 66), [(1, 8, 16), (8, 4, 4)], 128, 32, heads=2, seed=3,
+                                                  k=2), B=5),
+             dataclasses.replace(_random_workload((9, 27, 33), [(2, 4, 16)], 64, 64, heads=3, seed=4, k=3), B=4),
              _random_workload((5, 6, 20), [(2, 4, 16)], 64, 64, heads=3, seed=4, k=3)]
     for w in cases:
         say(f"[queue] {w.description} B {w.B} items {max(w.tiles_per_head()) * w.heads * w.B}")
@@ -265,6 +269,11 @@ def test_work_queue_matches_fixed_deal():
             assert torch.equal(r_d.view(torch.int16), r_f.view(torch.int16))
             assert torch.equal(rl_d.view(torch.int32), rl_f.view(torch.int32))
         assert torch.equal(out["o"].view(torch.int16), r_f.view(torch.int16))
+        if max(w.tiles_per_head()) * w.heads * w.B < 1024:
+            queue_bytes = queue.clone()
+            V.sparse_attn_fwd(*args, work_queue=queue)
+            torch.cuda.synchronize()
+            assert torch.equal(queue, queue_bytes)
 
 
 @pytest.mark.parametrize("grid,tiles,d,r", [
