@@ -394,7 +394,7 @@ def dense_reference(V, w, data, trip_bitmask=None, steps=2, warmup=1):
     if trip_bitmask is not None:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        teacher = V.teacher_tile_max(q_t, k_t, lse, geom)
+        teacher = V.teacher_tile_max(q_t, k_t, lse, geom, work_queue=queue)
         e1.record(stream)
         ks = w.k_per_head()
         _, oracle_bm = V.topk_mask(teacher, geom, ks)

@@ -408,11 +408,12 @@ def dense_index(geom: Geometry, device) -> Tuple[torch.Tensor, List[int]]:
 
 
 def teacher_tile_max(q_t: torch.Tensor, k_t: torch.Tensor, lse_dense: torch.Tensor, geom: Geometry,
-                     scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                     work_queue: Optional[torch.Tensor] = None, dynamic: bool = True) -> torch.Tensor:
     """Max-pooled dense attention: [B, heads, nT_max, nT_max] fp32, the
     largest dense softmax probability between each query tile and key tile
     (-inf outside the head's block). lse_dense is the LSE of sparse_attn_fwd
-    run with dense_index."""
+    run with dense_index. `work_queue` and `dynamic` as in sparse_attn_fwd."""
     tshape = _tiled_shape(geom, geom.head_dim)
     _need(q_t, torch.bfloat16, tshape, "q_tiled")
     _need(k_t, torch.bfloat16, tshape, "k_tiled")
@@ -423,7 +424,8 @@ def teacher_tile_max(q_t: torch.Tensor, k_t: torch.Tensor, lse_dense: torch.Tens
     _need(out, torch.float32, (geom.B, geom.n_heads, nT, nT), "teacher")
     sc = float(scale) if scale is not None else 0.0
     _lib.check(_lib.lib.veda_teacher_tile_max(geom.c, q_t.data_ptr(), k_t.data_ptr(), lse_dense.data_ptr(), sc,
-                                              out.data_ptr(), _stream(q_t)), "veda_teacher_tile_max")
+                                              out.data_ptr(), _queue_ptr(work_queue, dynamic, q_t.device),
+                                              _stream(q_t)), "veda_teacher_tile_max")
     return out
 
 

@@ -87,7 +87,8 @@ def _load():
                                                 POINTER(c_int32), c_int32, c_float, c_void_p, VedaRasterStrides,
                                                 c_void_p, c_void_p, c_void_p]
     lib.veda_sparse_attn_fwd_raster.restype = ctypes.c_int
-    lib.veda_teacher_tile_max.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p]
+    lib.veda_teacher_tile_max.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p,
+                                          c_void_p]
     lib.veda_teacher_tile_max.restype = ctypes.c_int
     lib.veda_mask_overlap.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_void_p]
     lib.veda_mask_overlap.restype = ctypes.c_int

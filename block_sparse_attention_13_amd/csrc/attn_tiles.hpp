@@ -57,6 +57,92 @@ __device__ __forceinline__ int32_t xcd_tile_order(int32_t x, int32_t n) {
   return xcd < r ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
 }
 
+// Work queue. Under the power limit the XCDs run at different clocks, so a
+// fixed deal of query tiles leaves the fastest XCDs idle while the slowest
+// finishes. Work items are the linear indices bx + nT_max (hd + heads b) of
+// a (nT_max, heads, B) grid. Queue x (x < 8) holds items x, x + 8, x + 16,
+// ...: those a grid of that shape deals to XCD x, since workgroups go to the
+// XCDs round robin. In the one-dimensional queue grid workgroup i is taken to
+// sit on XCD i % 8 (only locality rests on this) and, for i / 8 < n_static,
+// simply does item 8 (i / 8) + i % 8. Any other workgroup draws a ticket from
+// counter 8; a ticket below the number of remaining items guarantees that an
+// item is left somewhere, so it takes the next item of its own queue
+// (counter x counts the draws past n_static from queue x) or else of the
+// next queues in turn, and one pass finds it: a queue once exhausted stays
+// exhausted. Workgroups with a ticket past the end have no item.
+//
+// Sets (bx, hd, b) and returns true, or returns false for no item. Without a
+// queue the item is the workgroup's own grid position. `word` is LDS scratch
+// for the broadcast; it must lie inside the kernel's tile buffers (a second
+// LDS object makes the compiler wait for every LDS-DMA before each LDS read)
+// and is free again when this returns.
+__device__ __forceinline__ bool work_item(const GeoTable& g, int32_t* queue, int32_t n_static, int32_t* word,
+                                          int32_t* bx, int32_t* hd, int32_t* b) {
+  if (!queue) {
+    *bx = blockIdx.x;
+    *hd = blockIdx.y;
+    *b = blockIdx.z;
+    return true;
+  }
+  const int32_t total = g.nT_max * g.heads * g.B;
+  const int home = blockIdx.x % 8;
+  const int32_t n = blockIdx.x / 8;
+  int32_t item = 8 * n + home;
+  if (n >= n_static) {
+    if (threadIdx.x == 0) {
+      int32_t got = -1;
+      if (atomicAdd(&queue[8], 1) < total - 8 * n_static) {
+        for (int t = 0; t < 8; ++t) {
+          const int x = (home + t) % 8;
+          const int32_t m = n_static + atomicAdd(&queue[x], 1);
+          if (m < (total - x + 7) / 8) {
+            got = 8 * m + x;
+            break;
+          }
+        }
+      }
+      *word = got;
+    }
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(*word);
+    __syncthreads();  // every wave has read the word before the tile copies overwrite it
+    if (item < 0) return false;
+  }
+  *bx = item % g.nT_max;
+  *hd = (item / g.nT_max) % g.heads;
+  *b = item / (g.nT_max * g.heads);
+  return true;
+}
+
+namespace {
+
+__global__ void queue_reset_kernel(int32_t* queue) {
+  if (threadIdx.x < kAttnQueueInts) queue[threadIdx.x] = 0;
+}
+
+// Launch shape of a kernel over (nT_max, heads, B) query tiles: that grid
+// without a queue, or the one-dimensional queue grid, after a one-workgroup
+// kernel has cleared the counters on the stream (a kernel, not a memset, so
+// the call can be captured in a graph). The last sixteenth of each XCD's
+// share is handed out at run time, and each XCD has workgroups for a further
+// sixteenth taken from the others (enough for clocks about 12% apart). A
+// grid of fewer than 1024 tiles (4 per CU) has no tail worth balancing and
+// does not use (or clear) the queue.
+hipError_t queue_launch(const GeoTable& g, int32_t*& queue, dim3* grid, int32_t* n_static, hipStream_t s) {
+  const int64_t total = int64_t(g.nT_max) * g.heads * g.B;
+  *grid = dim3(g.nT_max, g.heads, g.B);
+  *n_static = 0;
+  if (total < 1024) queue = nullptr;
+  if (!queue) return hipSuccess;
+  const int32_t per = int32_t(total / 8), per_max = int32_t((total + 7) / 8);
+  *n_static = per - per / 16;
+  *grid = dim3(8 * (per_max + per / 16 + 1), 1, 1);
+  queue_reset_kernel<<<1, 64, 0, s>>>(queue);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 // One 1-KiB LDS-DMA copy: lane l loads 16 bytes at byte tile_bytes + voff

@@ -33,11 +33,9 @@
 // under the compute of tile i. Query tiles of a head are dealt out so each XCD
 // works on a contiguous run of neighbouring query tiles, whose key selections
 // overlap, while all XCDs share the same head's K/V in the MALL.
-// Under the socket power limit the XCDs run at different clocks, so a fixed
-// deal leaves the fastest XCDs idle while the slowest finishes. With a work
-// queue the grid is one-dimensional and each XCD first works through the
-// query tiles the fixed deal would have given it, then the last ones of
-// every XCD are handed out through atomic counters to whichever XCD is free.
+// With a work queue (work_item) each XCD first works through the query tiles
+// the fixed deal would have given it, then the last ones of every XCD are
+// handed out through atomic counters to whichever XCD is free.
 // The finished O rows go to the tiled output, or straight to each real
 // token's row of a raster output (pad query slots are then not written), which
 // spares the layer a separate unpermute pass.
@@ -267,50 +265,6 @@ __device__ __forceinline__ void hot_tile(WaveState<D>& w, const floatx16 (&s_cur
   if constexpr (!kLast) mx_next = row_max_base2(mx, scale_log2);
 }
 
-// Work items are the linear indices bx + nT_max (hd + heads b) of a
-// (nT_max, heads, B) grid. Queue x (x < 8) holds items x, x + 8, x + 16, ...:
-// those a grid of that shape deals to XCD x, since workgroups go to the XCDs
-// round robin. In the one-dimensional grid workgroup i is taken to sit on XCD
-// i % 8 (only locality rests on this) and, for i / 8 < n_static, simply does
-// item 8 (i / 8) + i % 8. Any other workgroup draws a ticket from counter 8;
-// a ticket below the number of remaining items guarantees that an item is
-// left somewhere, so it takes the next item of its own queue (counter x
-// counts the draws past n_static from queue x) or else of the next queues in
-// turn, and one pass finds it: a queue once exhausted stays exhausted.
-// Returns -1 for a workgroup without an item. `word` is LDS scratch for the
-// broadcast (inside the tile buffers: a second LDS object would make the
-// compiler wait for every LDS-DMA before each LDS read).
-__device__ __forceinline__ int32_t take_item(const GeoTable& g, int32_t* queue, int32_t n_static, int32_t* word) {
-  const int32_t total = g.nT_max * g.heads * g.B;
-  const int home = blockIdx.x % 8;
-  const int32_t n = blockIdx.x / 8;
-  if (n < n_static) return 8 * n + home;
-  if (threadIdx.x == 0) {
-    int32_t item = -1;
-    if (atomicAdd(&queue[8], 1) < total - 8 * n_static) {
-      for (int t = 0; t < 8; ++t) {
-        const int x = (home + t) % 8;
-        const int32_t m = n_static + atomicAdd(&queue[x], 1);
-        if (m < (total - x + 7) / 8) {
-          item = 8 * m + x;
-          break;
-        }
-      }
-    }
-    *word = item;
-  }
-  __syncthreads();
-  const int32_t item = __builtin_amdgcn_readfirstlane(*word);
-  __syncthreads();  // every wave has read the word before the tile copies overwrite it
-  return item;
-}
-
-constexpr int32_t kQueueMinItems = 1024;  // 4 query tiles per CU
-
-__global__ void queue_reset_kernel(int32_t* queue) {
-  if (threadIdx.x < kAttnQueueInts) queue[threadIdx.x] = 0;
-}
-
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
     GeoTable g, const uint16_t* __restrict__ q_t, const uint16_t* __restrict__ k_t,
@@ -323,17 +277,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t lds[4][S::kTileElems];
 
   int32_t bx, hd, b;
-  if (queue) {
-    const int32_t item = take_item(g, queue, n_static, reinterpret_cast<int32_t*>(&lds[0][0]));
-    if (item < 0) return;
-    bx = item % g.nT_max;
-    hd = (item / g.nT_max) % g.heads;
-    b = item / (g.nT_max * g.heads);
-  } else {
-    bx = blockIdx.x;
-    hd = blockIdx.y;
-    b = blockIdx.z;
-  }
+  if (!work_item(g, queue, n_static, reinterpret_cast<int32_t*>(&lds[0][0]), &bx, &hd, &b)) return;
   const HeadGeo hg = g.h[hd];
   const int32_t tq = xcd_tile_order(bx, g.nT_max);
   const int64_t head_base = (int64_t(b) * g.heads + hd) * g.nT_max;
@@ -520,23 +464,10 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
 hipError_t launch_sparse_attn(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t, const uint16_t* v_t,
                               const int32_t* idx, int32_t k_max, float scale, uint16_t* o_t, float* lse,
                               uint16_t* o_r, int64_t osb, int64_t osn, int64_t osh, int32_t* queue, hipStream_t s) {
-  dim3 grid(g.nT_max, g.heads, g.B);
+  dim3 grid;
   int32_t n_static = 0;
-  const int64_t total = int64_t(g.nT_max) * g.heads * g.B;
-  // A grid of a few workgroups per CU has no tail worth balancing: there the
-  // queue is not used (nor cleared), which saves the extra launch.
-  if (total < kQueueMinItems) queue = nullptr;
-  if (queue) {
-    // The last sixteenth of each XCD's share is handed out at run time, and
-    // each XCD has workgroups for up to a further sixteenth taken from the
-    // others (enough for per-XCD speeds that differ by about 12%).
-    const int32_t per = int32_t(total / 8), per_max = int32_t((total + 7) / 8);
-    n_static = per - per / 16;
-    grid = dim3(8 * (per_max + per / 16 + 1), 1, 1);
-    queue_reset_kernel<<<1, 64, 0, s>>>(queue);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  const hipError_t e = queue_launch(g, queue, &grid, &n_static, s);
+  if (e != hipSuccess) return e;
   const float scale_log2 = scale * 1.44269504088896340736f;
   if (g.d == 128)
     sparse_attn_fwd_kernel<128><<<grid, kThreads, 0, s>>>(g, q_t, k_t, v_t, idx, k_max, scale_log2, o_t, lse, o_r,

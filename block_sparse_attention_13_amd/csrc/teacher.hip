@@ -13,6 +13,8 @@
 //
 // One workgroup (8 waves) handles one query tile and streams every key tile
 // of its head through three LDS buffers (LDS-DMA copies two tiles ahead).
+// Query tiles are dealt to the XCDs as in the attention forward, through the
+// same optional work queue.
 // Wave (qg, half) computes S^T for queries 32qg..32qg+31 and keys
 // 64half..64half+63 with 32x32x16 bf16 MFMAs (fp32 accumulation), takes the
 // maximum of scale*log2(e)*s - log2(e)*lse per lane, reduces it over the wave,
@@ -53,15 +55,17 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void teacher_kernel(GeoTable g, const uint16_t* __restrict__ q_t,
                                                              const uint16_t* __restrict__ k_t,
                                                              const float* __restrict__ lse, float scale_log2,
-                                                             float* __restrict__ teacher) {
+                                                             float* __restrict__ teacher, int32_t* __restrict__ queue,
+                                                             int32_t n_static) {
   using S = AttnShape<D>;
   using TS = TeacherShape<D>;
   __shared__ __attribute__((aligned(16))) uint16_t kbuf[3][S::kTileElems];
   __shared__ float red[2][kWaves];
 
-  const int hd = blockIdx.y, b = blockIdx.z;
+  int32_t bx, hd, b;
+  if (!work_item(g, queue, n_static, reinterpret_cast<int32_t*>(&kbuf[0][0]), &bx, &hd, &b)) return;
   const HeadGeo hg = g.h[hd];
-  const int32_t tq = xcd_tile_order(blockIdx.x, g.nT_max);
+  const int32_t tq = xcd_tile_order(bx, g.nT_max);
   const int64_t head_base = (int64_t(b) * g.heads + hd) * g.nT_max;
   const int64_t tile_elems = S::kTileElems;
   float* trow = teacher + (head_base + tq) * g.nT_max;
@@ -192,13 +196,16 @@ __global__ __launch_bounds__(256) void mask_overlap_kernel(GeoTable g, const uin
 }  // namespace
 
 hipError_t launch_teacher(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t, const float* lse, float scale,
-                          float* teacher, hipStream_t s) {
-  const dim3 grid(g.nT_max, g.heads, g.B);
+                          float* teacher, int32_t* queue, hipStream_t s) {
+  dim3 grid;
+  int32_t n_static = 0;
+  const hipError_t e = queue_launch(g, queue, &grid, &n_static, s);
+  if (e != hipSuccess) return e;
   const float scale_log2 = scale * 1.44269504088896340736f;
   if (g.d == 128)
-    teacher_kernel<128><<<grid, kThreads, 0, s>>>(g, q_t, k_t, lse, scale_log2, teacher);
+    teacher_kernel<128><<<grid, kThreads, 0, s>>>(g, q_t, k_t, lse, scale_log2, teacher, queue, n_static);
   else
-    teacher_kernel<64><<<grid, kThreads, 0, s>>>(g, q_t, k_t, lse, scale_log2, teacher);
+    teacher_kernel<64><<<grid, kThreads, 0, s>>>(g, q_t, k_t, lse, scale_log2, teacher, queue, n_static);
   return hipGetLastError();
 }
 

@@ -278,16 +278,18 @@ int veda_sparse_attn_fwd_raster(const veda_geom* g, const void* q_tiled, const v
 }
 
 int veda_teacher_tile_max(const veda_geom* g, const void* q_tiled, const void* k_tiled, const float* lse_dense,
-                          float softmax_scale, float* teacher, void* stream) {
+                          float softmax_scale, float* teacher, int32_t* work_queue, void* stream) {
   GeoTable t;
   VEDA_TRY(build_table(g, &t));
   if (!q_tiled || !k_tiled || !lse_dense || !teacher) return VEDA_ERR_NULL;
   for (const void* p : {q_tiled, k_tiled, static_cast<const void*>(lse_dense), static_cast<const void*>(teacher)})
     if (!aligned16(p)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_queue(t, work_queue));
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) softmax_scale = 1.0f / std::sqrt(float(t.d));
   VEDA_TRY(check_device());
   return launched(veda::launch_teacher(t, static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_tiled),
-                                       lse_dense, softmax_scale, teacher, static_cast<hipStream_t>(stream)));
+                                       lse_dense, softmax_scale, teacher, work_queue,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 int veda_mask_overlap(const veda_geom* g, const uint32_t* bitmask_a, const uint32_t* bitmask_b, uint64_t* counts,

@@ -133,7 +133,7 @@ hipError_t launch_tile_scores(const GeoTable& g, const uint16_t* feat_q, const u
 hipError_t launch_topk(const GeoTable& g, const float* scores, int32_t k_max, int32_t* idx, uint32_t* bitmask,
                        hipStream_t s);
 hipError_t launch_teacher(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t, const float* lse, float scale,
-                          float* teacher, hipStream_t s);
+                          float* teacher, int32_t* queue, hipStream_t s);
 hipError_t launch_mask_overlap(const GeoTable& g, const uint32_t* a, const uint32_t* b, unsigned long long* counts,
                                hipStream_t s);
 hipError_t launch_head_sq_error(const GeoTable& g, const uint16_t* a, int64_t sab, int64_t san, int64_t sah,

@@ -279,9 +279,10 @@ int veda_tile_unpermute(const veda_geom* g, const void* x_tiled, void* x_raster,
  *   softmax_scale     in   <= 0 selects 1/sqrt(d)
  *   teacher           out  fp32 [B, heads, nT_max, nT_max], values in (0, 1]; -inf outside the head's
  *                          nT_hd x nT_hd block. veda_topk_mask(teacher) gives the oracle tile mask.
+ *   work_queue        tmp  as veda_sparse_attn_fwd (query tiles handed out at run time, or NULL)
  */
 int veda_teacher_tile_max(const veda_geom* g, const void* q_tiled, const void* k_tiled, const float* lse_dense,
-                          float softmax_scale, float* teacher, void* stream);
+                          float softmax_scale, float* teacher, int32_t* work_queue, void* stream);
 
 /*
  * Overlap of two tile masks (tile recall of a mask against an oracle mask is

@@ -121,9 +121,10 @@ def test_call_errors_precede_any_device_work():
     # a work queue needs B * heads * nT_max <= 2^28 (here 65535 * 8192 tiles)
     big = _geom(B=65535, grid=(1, 128, 8192), tiles=((1, 8, 16),))
     assert L.veda_sparse_attn_fwd(big.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE, None, FAKE, None) == -2
-    assert L.veda_teacher_tile_max(g.c, FAKE, FAKE, None, 0.0, FAKE, None) == -1
-    assert L.veda_teacher_tile_max(g.c, FAKE, FAKE, FAKE, 0.0, FAKE + 4, None) == -5
-    assert L.veda_teacher_tile_max(_geom(tiles=((2, 2, 2),)).c, FAKE, FAKE, FAKE, 0.0, FAKE, None) == -3
+    assert L.veda_teacher_tile_max(g.c, FAKE, FAKE, None, 0.0, FAKE, None, None) == -1
+    assert L.veda_teacher_tile_max(g.c, FAKE, FAKE, FAKE, 0.0, FAKE + 4, None, None) == -5
+    assert L.veda_teacher_tile_max(g.c, FAKE, FAKE, FAKE, 0.0, FAKE, FAKE + 12, None) == -5
+    assert L.veda_teacher_tile_max(_geom(tiles=((2, 2, 2),)).c, FAKE, FAKE, FAKE, 0.0, FAKE, None, None) == -3
     assert L.veda_mask_overlap(g.c, FAKE, None, FAKE, None) == -1
     assert L.veda_mask_overlap(g.c, FAKE, FAKE, FAKE + 8, None) == -5
     assert L.veda_head_sq_error(g.c, FAKE, s, None, s, FAKE, None) == -1

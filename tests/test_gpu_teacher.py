@@ -53,9 +53,12 @@ def test_teacher_oracle_mask_and_recall(wname, heads, qtiles):
     idx_d, ks_d = V.dense_index(geom, q.device)
     _, lse_d = V.sparse_attn_fwd(out["q_t"], out["k_t"], out["v_t"], idx_d, geom, ks_d)
     T = V.teacher_tile_max(out["q_t"], out["k_t"], lse_d, geom)
+    T_fixed = V.teacher_tile_max(out["q_t"], out["k_t"], lse_d, geom, dynamic=False)
     o_idx, o_bm = V.topk_mask(T, geom, ks)
     counts = V.mask_overlap(out["bitmask"], o_bm, geom)
     torch.cuda.synchronize()
+    # the work queue (used from 1024 query tiles on) only changes which workgroup computes a row
+    assert torch.equal(T.view(torch.int32), T_fixed.view(torch.int32))
     nT_max = geom.max_tiles()
     scale = 1.0 / math.sqrt(w.d)
     Tc = T.cpu().numpy()
