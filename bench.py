@@ -108,20 +108,24 @@ def stage_bytes(w) -> dict:
     }
 
 
-def kernel_code_hash(path: str) -> str:
-    """First 16 hex digits of the SHA-256 of a source file's code with its
-    comments and whitespace removed, so that edits to comments alone do not
-    mark counter summaries taken from the same code as stale."""
+def kernel_code_hash(paths) -> str:
+    """First 16 hex digits of the SHA-256 of source files' code (in the order
+    given) with comments and whitespace removed, so that edits to comments
+    alone do not mark counter summaries taken from the same code as stale."""
     import hashlib
-    with open(path) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
+    code = []
+    for path in ([paths] if isinstance(paths, str) else paths):
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        code.append(" ".join(text.split()))
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 ATTN_COUNTERS = os.path.join(ROOT, "profiles", "sparse_attn_long245k_hbm_counters.md")
-ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_13_amd", "csrc", "sparse_attn.hip")
+# The attention kernel's code: its source and the tile header it includes.
+ATTN_SOURCE = [os.path.join(ROOT, "block_sparse_attention_13_amd", "csrc", n) for n in ("sparse_attn.hip", "attn_tiles.hpp")]
 
 
 def attention_traffic(workload: str):

@@ -242,15 +242,16 @@ def test_work_queue_matches_fixed_deal():
     workgroup computes a tile: tiled O, raster O and LSE are the same bytes
     as with fixed per-XCD shares. One workspace, filled with garbage first,
     serves every call, the later workloads smaller (d 128 then 64, item
-    counts B * heads * nT_max of 2688, 1700 and 1260, the last two not
-    multiples of 8): each call clears it itself. Below 1024 items the
-    fixed deal is used and the workspace is not touched."""
+    counts B * heads * nT_max of 2688, 1700, 1260 and exactly 1024, two not
+    multiples of 8): each call clears it itself. Below 1024 items (1008
+    and 36 here) the fixed deal is used and the workspace is not touched."""
     V = _lib()
     queue = torch.full((V.ATTN_QUEUE_BYTES // 4,), 123456, dtype=torch.int32, device="cuda")
     cases = [dataclasses.replace(W["480p"].with_heads(4), B=2),
              dataclasses.replace(_random_workload((5, 37, 66), [(1, 8, 16), (8, 4, 4)], 128, 32, heads=2, seed=3,
                                                   k=2), B=5),
              dataclasses.replace(_random_workload((9, 27, 33), [(2, 4, 16)], 64, 64, heads=3, seed=4, k=3), B=4),
+             dataclasses.replace(W["tiny"], B=64), dataclasses.replace(W["tiny"], B=63),
              _random_workload((5, 6, 20), [(2, 4, 16)], 64, 64, heads=3, seed=4, k=3)]
     for w in cases:
         say(f"[queue] {w.description} B {w.B} items {max(w.tiles_per_head()) * w.heads * w.B}")
