@@ -15,10 +15,11 @@
 // of its head through three LDS buffers (LDS-DMA copies two tiles ahead).
 // Query tiles are dealt to the XCDs as in the attention forward, through the
 // same optional work queue.
-// Wave (qg, half) computes S^T for queries 32qg..32qg+31 and keys
-// 64half..64half+63 with 32x32x16 bf16 MFMAs (fp32 accumulation), takes the
-// maximum of scale*log2(e)*s - log2(e)*lse per lane, reduces it over the wave,
-// and the eight wave maxima of a key tile are combined through LDS.
+// Wave (qp, kq) computes S^T for queries 64qp..64qp+63 and keys
+// 32kq..32kq+31 with 32x32x16 bf16 MFMAs (fp32 accumulation), each K
+// fragment feeding two of them, takes the maximum of
+// scale*log2(e)*s - log2(e)*lse per lane, reduces it over the wave, and the
+// eight wave maxima of a key tile are combined through LDS.
 #include "attn_tiles.hpp"
 
 namespace veda {
@@ -77,20 +78,27 @@ __global__ __launch_bounds__(kThreads, 2) void teacher_kernel(GeoTable g, const 
   if (tq >= nT) return;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
-  const int qg = wave & 3, half = wave >> 2;
+  // Wave (qp, kq): queries 64qp..64qp+63 (two 32-query MFMA blocks) against
+  // keys 32kq..32kq+31 of every key tile, i.e. block kq & 1 of key half
+  // kq >> 1. Each K fragment read from LDS feeds two MFMAs (one per query
+  // block), which halves the LDS reads of four 32-query groups.
+  const int qp = wave & 1, kq = wave >> 1;
+  const int khalf = kq >> 1, kblk = kq & 1;
   const int l32 = lane % 32, h = lane / 32;
 
-  // Q^T operand of this lane's query, and its base-2 LSE; a pad query gets
-  // +inf so that it never raises a maximum.
-  u32x4 qf[S::kDC];
-  {
-    const uint16_t* qrow = q_t + (head_base + tq) * tile_elems + (qg * 32 + l32) * D + 8 * h;
+  // Q^T operands of this lane's two queries, and their base-2 LSEs; a pad
+  // query gets +inf so that it never raises a maximum.
+  u32x4 qf[2][S::kDC];
+  float lse2[2];
 #pragma unroll
-    for (int dc = 0; dc < S::kDC; ++dc) qf[dc] = *reinterpret_cast<const u32x4*>(qrow + 16 * dc);
+  for (int qb = 0; qb < 2; ++qb) {
+    const int slot = qp * 64 + qb * 32 + l32;
+    const uint16_t* qrow = q_t + (head_base + tq) * tile_elems + slot * D + 8 * h;
+#pragma unroll
+    for (int dc = 0; dc < S::kDC; ++dc) qf[qb][dc] = *reinterpret_cast<const u32x4*>(qrow + 16 * dc);
+    const bool q_real = hg.all_full || slot_is_real(hg, box_extent(g, hg, tq), slot);
+    lse2[qb] = q_real ? lse[(head_base + tq) * kTok + slot] * 1.44269504088896340736f : __builtin_inff();
   }
-  const int slot = qg * 32 + l32;
-  const bool q_real = hg.all_full || slot_is_real(hg, box_extent(g, hg, tq), slot);
-  const float lse2 = q_real ? lse[(head_base + tq) * kTok + slot] * 1.44269504088896340736f : __builtin_inff();
 
   // K-only LDS-DMA plan: wave w copies chunks w*cpw .. w*cpw + cpw - 1.
   uint32_t off[TS::kChunksPerWave];
@@ -120,45 +128,48 @@ __global__ __launch_bounds__(kThreads, 2) void teacher_kernel(GeoTable g, const 
   // K fragments of the current tile; those of tile j+1 are read right after
   // tile j's MFMAs are issued (tile j+1 has been resident since the previous
   // iteration's barrier), so the LDS latency hides under the MFMAs.
-  u32x4 kf[2 * S::kDC];
+  u32x4 kf[S::kDC];
 #pragma unroll
-  for (int t = 0; t < 2 * S::kDC; ++t) kf[t] = k_frag<D>(&kbuf[0][0], t, half, h, l32);
+  for (int dc = 0; dc < S::kDC; ++dc) kf[dc] = k_frag<D>(&kbuf[0][0], kblk * S::kDC + dc, khalf, h, l32);
   for (int32_t j = 0; j < nT; ++j) {
     const int next = buf == 2 ? 0 : buf + 1;
     // K of tile j+2 into the buffer of tile j-1 (read in the previous iteration).
     if (j + 2 < nT) copy_tile(j + 2, next == 2 ? 0 : next + 1);
     floatx16 sacc[2];
 #pragma unroll
-    for (int t = 0; t < 2 * S::kDC; ++t) {
-      const int kb = t % 2, dc = t / 2;  // alternate the two accumulators
-      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[kb * S::kDC + dc]), as_bf16x8(qf[dc]),
-                                                         dc == 0 ? zero : sacc[kb], 0, 0, 0);
-    }
+    for (int dc = 0; dc < S::kDC; ++dc)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)  // alternate the two accumulators
+        sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[dc]), as_bf16x8(qf[qb][dc]),
+                                                           dc == 0 ? zero : sacc[qb], 0, 0, 0);
     if (j + 1 < nT) {
 #pragma unroll
-      for (int t = 0; t < 2 * S::kDC; ++t) kf[t] = k_frag<D>(&kbuf[next][0], t, half, h, l32);
+      for (int dc = 0; dc < S::kDC; ++dc) kf[dc] = k_frag<D>(&kbuf[next][0], kblk * S::kDC + dc, khalf, h, l32);
     }
-    // Pad keys of a border tile never raise the maximum.
-    const uint64_t wm = real_key_bits(g, hg, j, half, h);
+    // Pad keys of a border tile never raise the maximum: this wave's 32 keys
+    // are one word of its key half's real-key bits.
+    const uint64_t wm = real_key_bits(g, hg, j, khalf, h);
     if (wm != ~0ull) {
-      const uint32_t wlo = uint32_t(wm), whi = uint32_t(wm >> 32);
+      const uint32_t w32 = kblk ? uint32_t(wm >> 32) : uint32_t(wm);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int bit = 16 * (v / 8) + 4 * ((v / 4) % 2) + (v % 4);
-          const uint32_t real = ((kb ? whi : wlo) >> bit) & 1u;
-          sacc[kb][v] += __uint_as_float((real - 1u) & 0xFF800000u);
+          sacc[qb][v] += __uint_as_float((((w32 >> bit) & 1u) - 1u) & 0xFF800000u);
         }
     }
-    float mx = sacc[0][0];
+    // scale*log2(e)*s - log2(e)*lse is increasing in s, so each query's
+    // maximum logit gives its maximum probability.
+    float x = -__builtin_inff();
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = sacc[qb][0];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-    // scale*log2(e)*s - log2(e)*lse is increasing in s, so the lane's maximum
-    // logit gives its maximum probability.
-    const float x = wave_max(__builtin_fmaf(mx, scale_log2, -lse2));
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sacc[qb][v]);
+      x = fmaxf(x, __builtin_fmaf(mx, scale_log2, -lse2[qb]));
+    }
+    x = wave_max(x);
     if (lane == 0) red[j & 1][wave] = x;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copy of tile j+2 has landed
     __syncthreads();
