@@ -523,7 +523,8 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the layer shards by head with no communication, "
-              "and multi-GPU runs are not part of this build", file=sys.stderr)
+              "so one GPU's throughput times the GPU count is the multi-GPU figure; no multi-GPU run "
+              "is implemented", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
