@@ -2,11 +2,11 @@
 """Benchmark of one Veda tile-sparse attention layer on one MI355X.
 
 A step is the whole layer on one batch of seeded synthetic input already
-resident in HBM: tile permute of Q, K and V, the Q and K permutes also
-taking each tile's TripPool statistics (stage "permute_x3"); head-specific
-projections and tile scores ("project_score"); head-aware Top-k;
-tile-skipping attention forward, which writes O back in raster order itself
-(no separate unpermute pass). Default workload: 245,760 tokens (64x48x80
+resident in HBM: each tile's TripPool statistics of Q (a read-only pass),
+the tile permute of K with its statistics and of V (stage "prep_qkv");
+head-specific projections and tile scores ("project_score"); head-aware
+Top-k; tile-skipping attention forward, which gathers Q from raster order
+and writes O back in raster order itself (no tiled Q, no unpermute pass). Default workload: 245,760 tokens (64x48x80
 latents), 40 heads, d = 128, tile (4,4,8) -> 1920 tiles, k = 96 (95% sparse).
 
 Prints one JSON line: ms per layer (the value), the attention kernel's
@@ -80,7 +80,7 @@ def layer_floor(w, stage_ms: dict) -> dict:
     roofline fraction: the sum of the floors over the measured time."""
     sb = stage_bytes(w)
     sb["sparse_attn"] = attention_bytes(w)
-    fl = {"permute_x3": 0.0, "project_score": estimator_flops(w) / PEAK_FP32_VALU_TFLOPS,
+    fl = {"prep_qkv": 0.0, "project_score": estimator_flops(w) / PEAK_FP32_VALU_TFLOPS,
           "topk": 0.0, "sparse_attn": attention_flops(w) / PEAK_BF16_TFLOPS}
     floor = {n: max(fl[n] / 1e9, sb[n] / (PEAK_HBM_GBS * 1e6)) for n in fl}   # ms
     total = sum(floor.values())
@@ -102,7 +102,7 @@ def stage_bytes(w) -> dict:
     kmax = max(w.k_per_head())
     idx = B * Hh * nT * kmax * 4 + B * Hh * nT * ((nT + 31) // 32) * 4
     return {
-        "permute_x3": 3 * (raster + tiled) + 2 * stats,
+        "prep_qkv": raster + 2 * (raster + tiled) + 2 * stats,
         "project_score": 2 * stats + 2 * feats + scores + 2 * Hh * 3 * d * w.r * 2,
         "topk": scores + idx,
     }
@@ -162,12 +162,12 @@ def attention_mfma_counters(workload: str):
 
 
 def attention_bytes(w) -> int:
-    """Algorithmic HBM bytes of one attention launch: tiled Q, K, V read once,
-    raster O and the LSE written once, the index lists read once."""
+    """Algorithmic HBM bytes of one attention launch: raster Q and tiled K, V
+    read once, raster O and the LSE written once, the index lists read once."""
     nT = max(w.tiles_per_head())
     tiled = w.B * w.heads * nT * 128 * w.d * 2
     raster = w.B * w.tokens * w.heads * w.d * 2
-    return 3 * tiled + raster + w.B * w.heads * nT * 128 * 4 + w.B * w.heads * nT * max(w.k_per_head()) * 4
+    return 2 * tiled + 2 * raster + w.B * w.heads * nT * 128 * 4 + w.B * w.heads * nT * max(w.k_per_head()) * 4
 
 
 def cpu_baseline(w, data, sample_tiles: int, seconds_hint: float = 20.0):
@@ -291,12 +291,12 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0):
     torch.cuda.synchronize()
     log("[bench] first layer done")
 
-    stages = ["permute_x3", "project_score", "topk", "sparse_attn"]
+    stages = ["prep_qkv", "project_score", "topk", "sparse_attn"]
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        V.tile_permute_stats(q, geom, bufs["q_t"], bufs["stats_q"])
+        V.tile_stats(q, geom, bufs["stats_q"])
         V.tile_permute_stats(k, geom, bufs["k_t"], bufs["stats_k"])
         V.tile_permute(v, geom, bufs["v_t"], layout=V.CHANNEL_MAJOR)
         if ev is not None:
@@ -308,8 +308,8 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0):
         V.topk_mask(bufs["scores"], geom, ks, idx=bufs["idx"], bitmask=bufs["bitmask"])
         if ev is not None:
             ev[3].record(stream)
-        V.sparse_attn_fwd_raster(bufs["q_t"], bufs["k_t"], bufs["v_t"], bufs["idx"], geom, ks,
-                                 out=bufs["o"], lse=bufs["lse"], work_queue=bufs["queue"])
+        V.sparse_attn_fwd_raster_io(q, bufs["k_t"], bufs["v_t"], bufs["idx"], geom, ks,
+                                    out=bufs["o"], lse=bufs["lse"], work_queue=bufs["queue"])
         if ev is not None:
             ev[4].record(stream)
 
@@ -470,7 +470,7 @@ def distill_report(V, datagen, name="480p", steps=300, lr=3e-3):
         data = datagen.generate(w)
         g = V.Geometry(w.B, w.heads, w.d, w.grid, w.head_tiles())
         q, k, v, wq, wk = (to(data[n]) for n in ("q", "k", "v", "wq", "wk"))
-        out = V.layer_forward(q, k, v, wq, wk, g, w.k_per_head())
+        out = V.layer_forward(q, k, v, wq, wk, g, w.k_per_head(), tiled_q=True)
         idx_d, ks_d = V.dense_index(g, dev)
         _, lse = V.sparse_attn_fwd(out["q_t"], out["k_t"], out["v_t"], idx_d, g, ks_d)
         teacher = V.teacher_tile_max(out["q_t"], out["k_t"], lse, g)

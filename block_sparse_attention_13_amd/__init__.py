@@ -14,9 +14,11 @@ Python: the five steps of the layer are HIP kernels.
   tile_permute_stats      raster Q or K -> token-major tiles + TripPool stats, one pass
   trippool_project_score  stats + W_q, W_k -> features, tile scores
   sparse_attn_fwd_raster  sparse_attn_fwd writing raster O (no unpermute pass)
+  tile_stats       the TripPool statistics of raster Q or K alone (no tiled copy)
+  sparse_attn_fwd_raster_io  sparse_attn_fwd_raster reading raster Q (no tiled Q)
   attn_queue       workspace of the attention calls' work queue (query tiles handed out at run time)
-  layer_forward    the layer: tile_permute_stats of Q and K, tile_permute of V,
-                   trippool_project_score, topk_mask, sparse_attn_fwd_raster
+  layer_forward    the layer: tile_stats of Q, tile_permute_stats of K, tile_permute
+                   of V, trippool_project_score, topk_mask, sparse_attn_fwd_raster_io
 
 Measuring a mask against the method's own target:
   dense_index      index lists that keep every key tile (dense attention through sparse_attn_fwd)
@@ -50,7 +52,8 @@ from . import _lib
 from ._lib import VedaError
 
 __all__ = ["Geometry", "VedaError", "tile_permute", "tile_permute_stats", "tile_unpermute", "trippool_score",
-           "trippool_project_score", "topk_mask", "sparse_attn_fwd_raster",
+           "trippool_project_score", "topk_mask", "sparse_attn_fwd_raster", "tile_stats",
+           "sparse_attn_fwd_raster_io",
            "sparse_attn_fwd", "attn_queue", "layer_forward",
            "dense_index", "teacher_tile_max", "mask_overlap", "tile_recall",
            "head_sq_error", "candidate_tiles", "tile_search", "distill_kl", "distill_grad", "adam_step",
@@ -166,6 +169,20 @@ def tile_permute_stats(x: torch.Tensor, geom: Geometry, out: Optional[torch.Tens
     _lib.check(_lib.lib.veda_tile_permute_stats(geom.c, x.data_ptr(), s, out.data_ptr(), stats.data_ptr(),
                                                 _stream(x)), "veda_tile_permute_stats")
     return out, stats
+
+
+def tile_stats(x: torch.Tensor, geom: Geometry, stats: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The TripPool statistics of each tile of Q or K ([B, heads, nT_max, 3d]
+    bf16, the same bytes as tile_permute_stats gives) in a pass that only
+    reads the raster tensor: no tiled copy is written."""
+    s = _raster_strides(x, geom, "x")
+    sshape = (geom.B, geom.n_heads, geom.max_tiles(), 3 * geom.head_dim)
+    if stats is None:
+        stats = torch.empty(sshape, dtype=torch.bfloat16, device=x.device)
+    _need(stats, torch.bfloat16, sshape, "stats")
+    _lib.check(_lib.lib.veda_tile_permute_stats(geom.c, x.data_ptr(), s, None, stats.data_ptr(), _stream(x)),
+               "veda_tile_permute_stats")
+    return stats
 
 
 def tile_unpermute(xt: torch.Tensor, geom: Geometry, out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -335,6 +352,41 @@ def sparse_attn_fwd_raster(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tens
     return out, lse
 
 
+def sparse_attn_fwd_raster_io(q: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, idx: torch.Tensor,
+                              geom: Geometry, k_per_head: Sequence[int], scale: Optional[float] = None,
+                              with_lse: bool = True, out: Optional[torch.Tensor] = None,
+                              lse: Optional[torch.Tensor] = None, work_queue: Optional[torch.Tensor] = None,
+                              dynamic: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """sparse_attn_fwd_raster reading Q in raster order too ([B, N, heads, d],
+    any strided view with unit channel stride): the bytes it gives with the
+    tiled Q of tile_permute(q), with no tiled copy of Q."""
+    tshape = _tiled_shape(geom, geom.head_dim)
+    sq = _raster_strides(q, geom, "q")
+    _need(k_t, torch.bfloat16, tshape, "k_tiled")
+    _need(v_t, torch.bfloat16, _tiled_cm_shape(geom), "v_tiled")
+    if idx.dim() != 4:
+        raise ValueError("idx must be [B, heads, nT_max, k_max]")
+    k_max = idx.shape[3]
+    _need(idx, torch.int32, (geom.B, geom.n_heads, tshape[2], k_max), "idx")
+    ks = list(k_per_head)
+    if len(ks) != geom.n_heads:
+        raise ValueError("need one k per head")
+    if with_lse and lse is None:
+        lse = torch.empty(tshape[:4], dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, torch.float32, tshape[:4], "lse")
+    if out is None:
+        out = torch.empty((geom.B, geom.tokens, geom.n_heads, geom.head_dim), dtype=torch.bfloat16,
+                          device=q.device)
+    so = _raster_strides(out, geom, "out")
+    sc = float(scale) if scale is not None else 0.0
+    _lib.check(_lib.lib.veda_sparse_attn_fwd_raster_io(
+        geom.c, q.data_ptr(), sq, k_t.data_ptr(), v_t.data_ptr(), idx.data_ptr(), _lib.int_array(ks), int(k_max), sc,
+        out.data_ptr(), so, lse.data_ptr() if lse is not None else None, _queue_ptr(work_queue, dynamic, q.device),
+        _stream(q)), "veda_sparse_attn_fwd_raster_io")
+    return out, lse
+
+
 def sparse_attn_fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, idx: torch.Tensor, geom: Geometry,
                     k_per_head: Sequence[int], scale: Optional[float] = None, with_lse: bool = True,
                     o_t: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
@@ -376,15 +428,21 @@ def sparse_attn_fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, idx
 
 def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
                   geom: Geometry, k_per_head: Sequence[int], scale: Optional[float] = None,
-                  buffers: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
-    """One Veda attention layer: permute Q/K/V (the TripPool statistics of Q
-    and K taken in the same pass), projections and tile scores, Top-k mask,
-    tile-skipping attention writing raster O. `buffers` (from a previous
-    call) reuses every output allocation. Returns all intermediates, `o`
-    (no tiled O: sparse_attn_fwd + tile_unpermute give the same `o`) and the
-    attention's work-queue workspace `queue`."""
+                  buffers: Optional[Dict[str, torch.Tensor]] = None, tiled_q: bool = False) -> Dict[str, torch.Tensor]:
+    """One Veda attention layer: the TripPool statistics of Q (a read-only
+    pass), K permuted with its statistics in the same pass, V permuted,
+    projections and tile scores, Top-k mask, and tile-skipping attention
+    that reads Q and writes O in raster order. `buffers` (from a previous
+    call) reuses every output allocation. Returns all intermediates, `o` and
+    the attention's work-queue workspace `queue`; there is no tiled Q or O
+    (tile_permute, sparse_attn_fwd and tile_unpermute give the same `o`).
+    With `tiled_q` the layer tiles Q as well (output `q_t`) and the attention
+    reads that: the same bytes in every other output."""
     b = buffers if buffers is not None else {}
-    b["q_t"], b["stats_q"] = tile_permute_stats(q, geom, b.get("q_t"), b.get("stats_q"))
+    if tiled_q:
+        b["q_t"], b["stats_q"] = tile_permute_stats(q, geom, b.get("q_t"), b.get("stats_q"))
+    else:
+        b["stats_q"] = tile_stats(q, geom, b.get("stats_q"))
     b["k_t"], b["stats_k"] = tile_permute_stats(k, geom, b.get("k_t"), b.get("stats_k"))
     b["v_t"] = tile_permute(v, geom, b.get("v_t"), layout=CHANNEL_MAJOR)
     est = trippool_project_score(b["stats_q"], b["stats_k"], w_q, w_k, geom,
@@ -393,8 +451,12 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.
     b["idx"], b["bitmask"] = topk_mask(b["scores"], geom, k_per_head, idx=b.get("idx"), bitmask=b.get("bitmask"))
     if b.get("queue") is None:
         b["queue"] = attn_queue(q.device)
-    b["o"], b["lse"] = sparse_attn_fwd_raster(b["q_t"], b["k_t"], b["v_t"], b["idx"], geom, k_per_head, scale,
-                                              out=b.get("o"), lse=b.get("lse"), work_queue=b["queue"])
+    if tiled_q:
+        b["o"], b["lse"] = sparse_attn_fwd_raster(b["q_t"], b["k_t"], b["v_t"], b["idx"], geom, k_per_head, scale,
+                                                  out=b.get("o"), lse=b.get("lse"), work_queue=b["queue"])
+    else:
+        b["o"], b["lse"] = sparse_attn_fwd_raster_io(q, b["k_t"], b["v_t"], b["idx"], geom, k_per_head, scale,
+                                                     out=b.get("o"), lse=b.get("lse"), work_queue=b["queue"])
     return b
 
 

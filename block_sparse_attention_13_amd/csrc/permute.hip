@@ -87,11 +87,12 @@ __global__ __launch_bounds__(kThreads) void tile_permute_stats_kernel(GeoTable g
   const int chunk = threadIdx.x % M::kChunks;
   const int row0 = threadIdx.x / M::kChunks;
   const int64_t tile_row = (int64_t(b) * g.heads + hd) * g.nT_max + tau;
-  uint4* dst = reinterpret_cast<uint4*>(xt + tile_row * VEDA_TILE_TOKENS * D);
+  uint4* dst = xt ? reinterpret_cast<uint4*>(xt + tile_row * VEDA_TILE_TOKENS * D) : nullptr;
   uint16_t* st_out = stats + tile_row * 3 * D;
   if (tau >= hg.nT) {  // tile beyond this head's grid: defined zeros
+    if (dst)
 #pragma unroll
-    for (int p = 0; p < M::kPasses; ++p) dst[(row0 + p * M::kRowsPerPass) * M::kChunks + chunk] = make_uint4(0, 0, 0, 0);
+      for (int p = 0; p < M::kPasses; ++p) dst[(row0 + p * M::kRowsPerPass) * M::kChunks + chunk] = make_uint4(0, 0, 0, 0);
     for (int c = threadIdx.x; c < 3 * D; c += kThreads) st_out[c] = 0;
     return;
   }
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void tile_permute_stats_kernel(GeoTable g
 #pragma unroll
   for (int p = 0; p < M::kPasses; ++p) {
     const int r = row0 + p * M::kRowsPerPass;
-    store_stream(&dst[r * M::kChunks + chunk], val[p]);
+    if (dst) store_stream(&dst[r * M::kChunks + chunk], val[p]);
     tile_s[r * M::kChunks + chunk] = val[p];
   }
   __syncthreads();

@@ -38,7 +38,9 @@
 // handed out through atomic counters to whichever XCD is free.
 // The finished O rows go to the tiled output, or straight to each real
 // token's row of a raster output (pad query slots are then not written), which
-// spares the layer a separate unpermute pass.
+// spares the layer a separate unpermute pass. Q likewise comes from tiled Q,
+// or straight from each real token's raster row (a pad slot gets a zero
+// query, as tiled Q holds there), which spares the layer a tiled copy of Q.
 #include "attn_tiles.hpp"
 
 namespace veda {
@@ -270,7 +272,8 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
     GeoTable g, const uint16_t* __restrict__ q_t, const uint16_t* __restrict__ k_t,
     const uint16_t* __restrict__ v_t, const int32_t* __restrict__ idx, int32_t k_max, float scale_log2,
     uint16_t* __restrict__ o_t, float* __restrict__ lse, uint16_t* __restrict__ o_r, int64_t osb, int64_t osn,
-    int64_t osh, int32_t* __restrict__ queue, int32_t n_static) {
+    int64_t osh, const uint16_t* __restrict__ q_r, int64_t qsb, int64_t qsn, int64_t qsh, int32_t* __restrict__ queue,
+    int32_t n_static) {
   using S = AttnShape<D>;
   // K buffers lds[0..1], V buffers lds[2..3]; after the loop the space holds
   // the half merge.
@@ -314,7 +317,17 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
   lds_u16* const lbuf = (lds_u16*)&lds[0][0];   // lds[b] is lbuf + b * kTileElems
 
   WaveState<D> w;
-  {
+  if (q_r) {  // raster Q: this lane's query row, or a zero query for a pad slot (as in tiled Q)
+    const int64_t n = raster_of_slot(g, hg, box_extent(g, hg, tq), qg * 32 + l32);
+    if (n >= 0) {
+      const uint16_t* qrow = q_r + int64_t(b) * qsb + n * qsn + int64_t(hd) * qsh + 8 * h;
+#pragma unroll
+      for (int dc = 0; dc < S::kDC; ++dc) w.qf[dc] = *reinterpret_cast<const u32x4*>(qrow + 16 * dc);
+    } else {
+#pragma unroll
+      for (int dc = 0; dc < S::kDC; ++dc) w.qf[dc] = u32x4{0u, 0u, 0u, 0u};
+    }
+  } else {
     const uint16_t* qrow = q_t + (head_base + tq) * tile_elems + (qg * 32 + l32) * D + 8 * h;
 #pragma unroll
     for (int dc = 0; dc < S::kDC; ++dc) w.qf[dc] = *reinterpret_cast<const u32x4*>(qrow + 16 * dc);
@@ -463,7 +476,8 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
 
 hipError_t launch_sparse_attn(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t, const uint16_t* v_t,
                               const int32_t* idx, int32_t k_max, float scale, uint16_t* o_t, float* lse,
-                              uint16_t* o_r, int64_t osb, int64_t osn, int64_t osh, int32_t* queue, hipStream_t s) {
+                              uint16_t* o_r, int64_t osb, int64_t osn, int64_t osh, const uint16_t* q_r, int64_t qsb,
+                              int64_t qsn, int64_t qsh, int32_t* queue, hipStream_t s) {
   dim3 grid;
   int32_t n_static = 0;
   const hipError_t e = queue_launch(g, queue, &grid, &n_static, s);
@@ -471,10 +485,10 @@ hipError_t launch_sparse_attn(const GeoTable& g, const uint16_t* q_t, const uint
   const float scale_log2 = scale * 1.44269504088896340736f;
   if (g.d == 128)
     sparse_attn_fwd_kernel<128><<<grid, kThreads, 0, s>>>(g, q_t, k_t, v_t, idx, k_max, scale_log2, o_t, lse, o_r,
-                                                         osb, osn, osh, queue, n_static);
+                                                         osb, osn, osh, q_r, qsb, qsn, qsh, queue, n_static);
   else
     sparse_attn_fwd_kernel<64><<<grid, kThreads, 0, s>>>(g, q_t, k_t, v_t, idx, k_max, scale_log2, o_t, lse, o_r,
-                                                        osb, osn, osh, queue, n_static);
+                                                        osb, osn, osh, q_r, qsb, qsn, qsh, queue, n_static);
   return hipGetLastError();
 }
 

@@ -162,8 +162,8 @@ int veda_tile_permute_stats(const veda_geom* g, const void* x_raster, veda_raste
                             void* stats, void* stream) {
   GeoTable t;
   VEDA_TRY(build_table(g, &t));
-  if (!x_raster || !x_tiled || !stats) return VEDA_ERR_NULL;
-  if (!aligned16(x_raster) || !aligned16(x_tiled) || !aligned16(stats)) return VEDA_ERR_ALIGN;
+  if (!x_raster || !stats) return VEDA_ERR_NULL;
+  if (!aligned16(x_raster) || (x_tiled && !aligned16(x_tiled)) || !aligned16(stats)) return VEDA_ERR_ALIGN;
   VEDA_TRY(check_strides(s));
   VEDA_TRY(check_device());
   return launched(veda::launch_tile_permute_stats(t, static_cast<const uint16_t*>(x_raster), s.b, s.n, s.h,
@@ -253,7 +253,7 @@ int veda_sparse_attn_fwd(const veda_geom* g, const void* q_tiled, const void* k_
   return launched(veda::launch_sparse_attn(
       t, static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_tiled),
       static_cast<const uint16_t*>(v_tiled), idx, k_max, softmax_scale, static_cast<uint16_t*>(o_tiled), lse,
-      nullptr, 0, 0, 0, work_queue, static_cast<hipStream_t>(stream)));
+      nullptr, 0, 0, 0, nullptr, 0, 0, 0, work_queue, static_cast<hipStream_t>(stream)));
 }
 
 int veda_sparse_attn_fwd_raster(const veda_geom* g, const void* q_tiled, const void* k_tiled, const void* v_tiled,
@@ -274,7 +274,29 @@ int veda_sparse_attn_fwd_raster(const veda_geom* g, const void* q_tiled, const v
   return launched(veda::launch_sparse_attn(
       t, static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_tiled),
       static_cast<const uint16_t*>(v_tiled), idx, k_max, softmax_scale, nullptr, lse,
-      static_cast<uint16_t*>(o_raster), s.b, s.n, s.h, work_queue, static_cast<hipStream_t>(stream)));
+      static_cast<uint16_t*>(o_raster), s.b, s.n, s.h, nullptr, 0, 0, 0, work_queue, static_cast<hipStream_t>(stream)));
+}
+
+int veda_sparse_attn_fwd_raster_io(const veda_geom* g, const void* q_raster, veda_raster_strides sq,
+                                   const void* k_tiled, const void* v_tiled, const int32_t* idx,
+                                   const int32_t* k_per_head, int32_t k_max, float softmax_scale, void* o_raster,
+                                   veda_raster_strides so, float* lse, int32_t* work_queue, void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!q_raster || !k_tiled || !v_tiled || !idx || !o_raster) return VEDA_ERR_NULL;
+  VEDA_TRY(set_k(k_per_head, k_max, &t));
+  for (const void* p : {q_raster, k_tiled, v_tiled, static_cast<const void*>(idx), static_cast<const void*>(o_raster)})
+    if (!aligned16(p)) return VEDA_ERR_ALIGN;
+  if (lse && !aligned16(lse)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_queue(t, work_queue));
+  VEDA_TRY(check_strides(sq));
+  VEDA_TRY(check_strides(so));
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) softmax_scale = 1.0f / std::sqrt(float(t.d));
+  VEDA_TRY(check_device());
+  return launched(veda::launch_sparse_attn(
+      t, nullptr, static_cast<const uint16_t*>(k_tiled), static_cast<const uint16_t*>(v_tiled), idx, k_max,
+      softmax_scale, nullptr, lse, static_cast<uint16_t*>(o_raster), so.b, so.n, so.h,
+      static_cast<const uint16_t*>(q_raster), sq.b, sq.n, sq.h, work_queue, static_cast<hipStream_t>(stream)));
 }
 
 int veda_teacher_tile_max(const veda_geom* g, const void* q_tiled, const void* k_tiled, const float* lse_dense,

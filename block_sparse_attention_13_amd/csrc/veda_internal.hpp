@@ -150,7 +150,7 @@ hipError_t launch_adam(int64_t n, float* w, const float* grad, float* m, float* 
 // element strides (osb, osn, osh).
 hipError_t launch_sparse_attn(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t, const uint16_t* v_t,
                               const int32_t* idx, int32_t k_max, float scale, uint16_t* o_t, float* lse,
-                              uint16_t* o_r, int64_t osb, int64_t osn, int64_t osh, int32_t* queue,
-                              hipStream_t s);
+                              uint16_t* o_r, int64_t osb, int64_t osn, int64_t osh, const uint16_t* q_r,
+                              int64_t qsb, int64_t qsn, int64_t qsh, int32_t* queue, hipStream_t s);
 
 }  // namespace veda

@@ -16,6 +16,8 @@
  *   veda_trippool_project_score    stats -> head-specific projections -> tile scores
  *   veda_sparse_attn_fwd_raster    attention that writes raster O itself (no unpermute pass)
  *   (with veda_tile_permute of V and veda_topk_mask in between)
+ * and with Q never tiled: veda_tile_permute_stats of Q with no tiled output (statistics
+ * only), then veda_sparse_attn_fwd_raster_io, which also reads Q in raster order.
  *
  * Two more calls measure the mask against the method's own target:
  *   veda_teacher_tile_max      max-pooled dense attention per (query tile, key tile); its
@@ -144,11 +146,13 @@ int veda_tile_permute(const veda_geom* g, const void* x_raster, veda_raster_stri
  * and minimum per tile). One pass over the raster tensor writes both outputs:
  *   x_raster  in   raster bf16 tensor, strides `s` (elements)
  *   x_tiled   out  bf16 [B, heads, nT_max, 128, d], exactly as veda_tile_permute with
- *                  VEDA_TILED_TOKEN_MAJOR writes it
+ *                  VEDA_TILED_TOKEN_MAJOR writes it; may be NULL: then only the statistics are
+ *                  computed, in a pass that only reads x_raster (the layer does this for Q,
+ *                  which veda_sparse_attn_fwd_raster_io reads in raster order)
  *   stats     out  bf16 [B, heads, nT_max, 3d], exactly the stats_q (or stats_k) that
  *                  veda_trippool_score computes from x_tiled (0 for tiles >= nT_hd)
- * Errors: a null pointer (VEDA_ERR_NULL), a pointer not 16-byte aligned or a stride not a
- * multiple of 8 (VEDA_ERR_ALIGN), and the geometry checks of every call.
+ * Errors: a null x_raster or stats (VEDA_ERR_NULL), a pointer not 16-byte aligned or a stride
+ * not a multiple of 8 (VEDA_ERR_ALIGN), and the geometry checks of every call.
  */
 int veda_tile_permute_stats(const veda_geom* g, const void* x_raster, veda_raster_strides s,
                             void* x_tiled, void* stats, void* stream);
@@ -256,6 +260,23 @@ int veda_sparse_attn_fwd_raster(const veda_geom* g, const void* q_tiled, const v
                                 const void* v_tiled, const int32_t* idx, const int32_t* k_per_head,
                                 int32_t k_max, float softmax_scale, void* o_raster,
                                 veda_raster_strides s, float* lse, int32_t* work_queue, void* stream);
+
+/*
+ * The same attention reading Q in raster order as well, so no tiled copy of Q
+ * is needed (the re-tiling of Q, "Architecture", Principle 02, happens in the
+ * kernel's own loads). Arguments as veda_sparse_attn_fwd_raster, except:
+ *   q_raster  in   raster bf16 Q [B, N, heads, d] with element strides `sq` (channel stride 1,
+ *                  multiples of 8); each query slot reads its token's row, and a pad slot a zero
+ *                  query, exactly what tiled Q holds
+ *   o_raster  out  as o_raster of veda_sparse_attn_fwd_raster, with strides `so`
+ * For the same inputs the outputs are the bytes veda_sparse_attn_fwd_raster gives with the
+ * tiled Q that veda_tile_permute makes of q_raster.
+ */
+int veda_sparse_attn_fwd_raster_io(const veda_geom* g, const void* q_raster, veda_raster_strides sq,
+                                   const void* k_tiled, const void* v_tiled, const int32_t* idx,
+                                   const int32_t* k_per_head, int32_t k_max, float softmax_scale,
+                                   void* o_raster, veda_raster_strides so, float* lse,
+                                   int32_t* work_queue, void* stream);
 
 /*
  * Inverse re-tiling: raster x[b, n, hd, :] = tiled x at the slot of token n

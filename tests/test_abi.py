@@ -21,7 +21,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     from block_sparse_attention_13_amd import _lib
     declared = _declared_functions()
-    assert len(declared) == 17, declared
+    assert len(declared) == 18, declared
     assert sorted(_lib.EXPORTS) == declared
     for name in declared:
         assert hasattr(_lib.lib, name), name
@@ -116,6 +116,16 @@ def test_call_errors_precede_any_device_work():
     assert L.veda_sparse_attn_fwd_raster(g.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE,
                                          _lib.VedaRasterStrides(1024, 132, 128), None, None, None) == -5
     assert L.veda_sparse_attn_fwd_raster(g.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE, s, FAKE + 4, None, None) == -5
+    io = L.veda_sparse_attn_fwd_raster_io
+    assert io(g.c, None, s, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE, s, None, None, None) == -1
+    assert io(g.c, FAKE, s, FAKE, FAKE, FAKE, _lib.int_array([9]), 8, 0.0, FAKE, s, None, None, None) == -4
+    assert io(g.c, FAKE + 8, s, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE, s, None, None, None) == -5
+    assert io(g.c, FAKE, _lib.VedaRasterStrides(1024, 132, 128), FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE, s, None, None,
+              None) == -5
+    assert io(g.c, FAKE, s, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE, _lib.VedaRasterStrides(1024, 128, 4), None, None,
+              None) == -5
+    # statistics alone: no tiled output is a valid call; a misaligned stats buffer is not
+    assert L.veda_tile_permute_stats(g.c, FAKE, s, None, FAKE + 8, None) == -5
     assert L.veda_sparse_attn_fwd_raster(g.c, FAKE, FAKE, FAKE, FAKE, ks, 4, 0.0, FAKE, s, None, FAKE + 8,
                                          None) == -5
     # a work queue needs B * heads * nT_max <= 2^28 (here 65535 * 8192 tiles)

@@ -26,15 +26,21 @@ def _lib():
     return V
 
 
-def run_layer(w, data, k_per_head=None, buffers=None):
+def run_layer(w, data, k_per_head=None, buffers=None, tiled_q=False):
     V = _lib()
     geom = geometry(w)
     ks = k_per_head or w.k_per_head()
     q, k, v = (to_dev_bf16(data[n]) for n in ("q", "k", "v"))
     wq, wk = to_dev_bf16(data["wq"]), to_dev_bf16(data["wk"])
-    out = V.layer_forward(q, k, v, wq, wk, geom, ks, buffers=buffers)
+    out = V.layer_forward(q, k, v, wq, wk, geom, ks, buffers=buffers, tiled_q=tiled_q)
     torch.cuda.synchronize()
     return geom, out, (q, k, v, wq, wk)
+
+
+def _tiled_q(out, data, geom):
+    """The layer's tiled Q, or (the layer reads Q in raster order) a tiled
+    copy made by tile_permute."""
+    return out["q_t"] if "q_t" in out else _lib().tile_permute(to_dev_bf16(data["q"]), geom)
 
 
 def _sample_tiles(nT, count, seed):
@@ -51,8 +57,9 @@ def check_head(w, data, out, hd, ks, tiles, b=0, check_attention=True):
     nT_max = max(w.tiles_per_head())
     tile = w.head_tiles()[hd]
     r = oracle_head(data, w, b, hd, ks[hd], query_tiles=tiles if check_attention else [])
+    q_t = _tiled_q(out, data, geometry(w))
     for name in ("q_t", "k_t", "v_t"):
-        got = bits_of(out[name][b, hd])
+        got = bits_of((q_t if name == "q_t" else out[name])[b, hd])
         if name == "v_t":  # channel-major tiles [nT_max, d, 128]
             got = np.ascontiguousarray(got.swapaxes(1, 2))
         assert np.array_equal(got[:nT].reshape(-1, d), O.float_to_bf16_bits(r[name[0] + "t"])), (name, hd)
@@ -79,8 +86,8 @@ def check_head(w, data, out, hd, ks, tiles, b=0, check_attention=True):
     # garbage, so every byte it leaves is checked) must give the same bytes.
     V = _lib()
     geom = geometry(w)
-    o_tiled = torch.full(out["q_t"].shape, 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
-    o_tiled, lse_tiled = V.sparse_attn_fwd(out["q_t"], out["k_t"], out["v_t"], out["idx"], geom, ks, o_t=o_tiled)
+    o_tiled = torch.full(q_t.shape, 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    o_tiled, lse_tiled = V.sparse_attn_fwd(q_t, out["k_t"], out["v_t"], out["idx"], geom, ks, o_t=o_tiled)
     o_back = V.tile_unpermute(o_tiled, geom)
     torch.cuda.synchronize()
     assert torch.equal(o_back[b, :, hd].view(torch.int16), out["o"][b, :, hd].view(torch.int16)), ("raster O", hd)
@@ -145,8 +152,9 @@ def test_estimator_is_deterministic():
     data = datagen.generate(w)
     geom, out, (q, k, v, wq, wk) = run_layer(w, data)
     first = out["scores"].clone()
+    q_t = V.tile_permute(q, geom)
     for _ in range(2):
-        again = V.trippool_score(out["q_t"], out["k_t"], wq, wk, geom)
+        again = V.trippool_score(q_t, out["k_t"], wq, wk, geom)
         torch.cuda.synchronize()
         assert torch.equal(again["scores"].view(torch.int32), first.view(torch.int32))
 
@@ -187,12 +195,14 @@ def test_unpermute_inverts_permute_with_strided_raster():
     (None, None, 1, ((3, 9, 17), [(1, 8, 16), (8, 4, 4)], 64, 64)),  # d = 64, r = 64, mostly pad
 ])
 def test_fused_layer_matches_unfused(wname, heads, B, custom):
-    """layer_forward takes the statistics while it permutes Q and K
-    (tile_permute_stats + trippool_project_score) and writes raster O from
-    the attention kernel (sparse_attn_fwd_raster); the unfused route
-    (tile_permute, trippool_score, topk_mask, sparse_attn_fwd,
-    tile_unpermute) must give the same bytes. The raster O also goes into
-    a strided view whose neighbouring bytes must stay untouched."""
+    """layer_forward takes the statistics of Q alone and of K while it
+    permutes K (tile_stats, tile_permute_stats + trippool_project_score),
+    and its attention reads raster Q and writes raster O
+    (sparse_attn_fwd_raster_io); with tiled_q it tiles Q too and reads that
+    (sparse_attn_fwd_raster). Both, and the unfused route (tile_permute,
+    trippool_score, topk_mask, sparse_attn_fwd, tile_unpermute), must give
+    the same bytes. Raster O also goes into strided views (and raster Q
+    comes from one) whose neighbouring bytes must stay untouched."""
     V = _lib()
     if custom is None:
         w = W[wname] if heads is None else W[wname].with_heads(heads)
@@ -203,10 +213,14 @@ def test_fused_layer_matches_unfused(wname, heads, B, custom):
     say(f"[one-pass] {w.description} B {w.B}")
     data = datagen.generate(w)
     geom, out, (q, k, v, wq, wk) = run_layer(w, data)
+    _, out_t, _ = run_layer(w, data, tiled_q=True)
+    assert "q_t" not in out
+    for name in ("k_t", "v_t", "stats_q", "stats_k", "feat_q", "feat_k", "scores", "idx", "bitmask", "lse", "o"):
+        assert torch.equal(out[name].contiguous().view(torch.uint8), out_t[name].contiguous().view(torch.uint8)), name
     q_t, k_t = V.tile_permute(q, geom), V.tile_permute(k, geom)
     two = V.trippool_score(q_t, k_t, wq, wk, geom)
     torch.cuda.synchronize()
-    assert torch.equal(out["q_t"].view(torch.int16), q_t.view(torch.int16))
+    assert torch.equal(out_t["q_t"].view(torch.int16), q_t.view(torch.int16))
     assert torch.equal(out["k_t"].view(torch.int16), k_t.view(torch.int16))
     for name in ("stats_q", "stats_k", "feat_q", "feat_k"):
         assert torch.equal(out[name].view(torch.int16), two[name].view(torch.int16)), name
@@ -228,6 +242,13 @@ def test_fused_layer_matches_unfused(wname, heads, B, custom):
     packed = torch.full((w.B, w.tokens, 2, w.heads, w.d), 0x7FC0, dtype=torch.int16, device="cuda")
     view = packed.view(torch.bfloat16)[:, :, 1]
     V.sparse_attn_fwd_raster(q_t, k_t, v_t, idx, geom, ks, out=view, with_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(packed[:, :, 1], o.view(torch.int16))
+    assert torch.all(packed[:, :, 0] == 0x7FC0)
+    # raster Q from a strided view (Q in slot 0 of a packed [B, N, 3, heads, d] tensor)
+    qkv = torch.stack([q, k, v], dim=2)
+    packed.fill_(0x7FC0)
+    V.sparse_attn_fwd_raster_io(qkv[:, :, 0], k_t, v_t, idx, geom, ks, out=view, with_lse=False)
     torch.cuda.synchronize()
     assert torch.equal(packed[:, :, 1], o.view(torch.int16))
     assert torch.all(packed[:, :, 0] == 0x7FC0)
@@ -256,15 +277,22 @@ def test_work_queue_matches_fixed_deal():
     for w in cases:
         say(f"[queue] {w.description} B {w.B} items {max(w.tiles_per_head()) * w.heads * w.B}")
         data = datagen.generate(w)
-        geom, out, _ = run_layer(w, data)
+        geom, out, (q, _, _, _, _) = run_layer(w, data)
         ks = w.k_per_head()
-        args = (out["q_t"], out["k_t"], out["v_t"], out["idx"], geom, ks)
+        args = (V.tile_permute(q, geom), out["k_t"], out["v_t"], out["idx"], geom, ks)
+        rio = (q, out["k_t"], out["v_t"], out["idx"], geom, ks)
+        io_f, iol_f = V.sparse_attn_fwd_raster_io(*rio, dynamic=False)
         o_f, lse_f = V.sparse_attn_fwd(*args, dynamic=False)
         r_f, rl_f = V.sparse_attn_fwd_raster(*args, dynamic=False)
         for _ in range(2):
             o_d, lse_d = V.sparse_attn_fwd(*args, work_queue=queue)
             r_d, rl_d = V.sparse_attn_fwd_raster(*args, work_queue=queue)
+            io_d, iol_d = V.sparse_attn_fwd_raster_io(*rio, work_queue=queue)
             torch.cuda.synchronize()
+            assert torch.equal(io_d.view(torch.int16), r_f.view(torch.int16))
+            assert torch.equal(io_f.view(torch.int16), r_f.view(torch.int16))
+            assert torch.equal(iol_d.view(torch.int32), rl_f.view(torch.int32))
+            assert torch.equal(iol_f.view(torch.int32), rl_f.view(torch.int32))
             assert torch.equal(o_d.view(torch.int16), o_f.view(torch.int16))
             assert torch.equal(lse_d.view(torch.int32), lse_f.view(torch.int32))
             assert torch.equal(r_d.view(torch.int16), r_f.view(torch.int16))
@@ -386,7 +414,8 @@ def test_topk_on_crafted_scores():
         assert np.all(idx[0, 0, rows:].cpu().numpy() == np.arange(k))
 
 
-def test_every_output_byte_is_written():
+@pytest.mark.parametrize("tiled_q", [False, True])
+def test_every_output_byte_is_written(tiled_q):
     """Outputs pre-filled with garbage end up fully defined."""
     w = W["hc"].with_heads(6)
     data = datagen.generate(w)
@@ -403,7 +432,9 @@ def test_every_output_byte_is_written():
         "bitmask": g((B, Hh, nT, (nT + 31) // 32), torch.int32).view(torch.uint32),
         "lse": g((B, Hh, nT, 128), torch.float32), "o": g((B, w.tokens, Hh, d), torch.bfloat16),
     }
-    geom, out, _ = run_layer(w, data, buffers=bufs)
+    if not tiled_q:
+        del bufs["q_t"]
+    geom, out, _ = run_layer(w, data, buffers=bufs, tiled_q=tiled_q)
     ks = w.k_per_head()
     for hd in (0, 1, 2):
         check_head(w, data, out, hd, ks, _sample_tiles(w.tiles_per_head()[hd], 6, hd))
@@ -454,10 +485,11 @@ def _guards_intact(buf):
     return bool(torch.all(buf[:_GUARD_BYTES] == 0xA5)) and bool(torch.all(buf[-_GUARD_BYTES:] == 0xA5))
 
 
-def test_outputs_stay_in_their_buffers():
+@pytest.mark.parametrize("tiled_q", [False, True])
+def test_outputs_stay_in_their_buffers(tiled_q):
     """Every call writes inside its outputs and the attention's work-queue
     workspace: 4 KiB before and after each one stay untouched (ragged boxes,
-    three tile shapes, B = 2)."""
+    three tile shapes, B = 2; the layer with and without tiled Q)."""
     V = _lib()
     w = dataclasses.replace(W["hc"].with_heads(6), B=2)
     data = datagen.generate(w)
@@ -475,11 +507,13 @@ def test_outputs_stay_in_their_buffers():
     }
     bufs, raw = {}, {}
     for name, (shape, dt) in shapes.items():
-        bufs[name], raw[name] = _guarded(shape, dt)
+        if name != "q_t" or tiled_q:
+            bufs[name], raw[name] = _guarded(shape, dt)
     bufs["bitmask"] = bufs["bitmask"].view(torch.uint32)
-    geom, out, (q, k, v, wq, wk) = run_layer(w, data, buffers=bufs)
+    geom, out, (q, k, v, wq, wk) = run_layer(w, data, buffers=bufs, tiled_q=tiled_q)
     for name, buf in raw.items():
         assert _guards_intact(buf), ("fused layer", name)
+    q_t = _tiled_q(out, data, geom)
     # the unfused route and the measurement calls, into guarded outputs too
     checks = []
     xt, b1 = _guarded(shapes["q_t"][0], torch.bfloat16)
@@ -489,14 +523,16 @@ def test_outputs_stay_in_their_buffers():
     est = {}
     for name in ("stats_q", "stats_k", "feat_q", "feat_k", "scores"):
         est[name], b3 = _guarded(*shapes[name]); checks.append(("trippool_score " + name, b3))
-    V.trippool_score(out["q_t"], out["k_t"], wq, wk, geom, est)
+    V.trippool_score(q_t, out["k_t"], wq, wk, geom, est)
     o_t, b4 = _guarded(shapes["q_t"][0], torch.bfloat16)
-    V.sparse_attn_fwd(out["q_t"], out["k_t"], out["v_t"], out["idx"], geom, w.k_per_head(), o_t=o_t)
+    V.sparse_attn_fwd(q_t, out["k_t"], out["v_t"], out["idx"], geom, w.k_per_head(), o_t=o_t)
     checks.append(("sparse_attn_fwd", b4))
     o, b5 = _guarded(shapes["o"][0], torch.bfloat16)
     V.tile_unpermute(o_t, geom, o); checks.append(("tile_unpermute", b5))
     teacher, b6 = _guarded(shapes["scores"][0], torch.float32)
-    V.teacher_tile_max(out["q_t"], out["k_t"], out["lse"], geom, out=teacher); checks.append(("teacher", b6))
+    V.teacher_tile_max(q_t, out["k_t"], out["lse"], geom, out=teacher); checks.append(("teacher", b6))
+    st, b7 = _guarded(shapes["stats_q"][0], torch.bfloat16)
+    V.tile_stats(q, geom, st); checks.append(("tile_stats", b7))
     torch.cuda.synchronize()
     for name, buf in checks:
         assert _guards_intact(buf), name

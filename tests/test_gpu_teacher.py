@@ -49,7 +49,7 @@ def test_teacher_oracle_mask_and_recall(wname, heads, qtiles):
     geom = geometry(w)
     ks = w.k_per_head()
     q, k, v = (to_dev_bf16(data[n]) for n in ("q", "k", "v"))
-    out = V.layer_forward(q, k, v, to_dev_bf16(data["wq"]), to_dev_bf16(data["wk"]), geom, ks)
+    out = V.layer_forward(q, k, v, to_dev_bf16(data["wq"]), to_dev_bf16(data["wk"]), geom, ks, tiled_q=True)
     idx_d, ks_d = V.dense_index(geom, q.device)
     _, lse_d = V.sparse_attn_fwd(out["q_t"], out["k_t"], out["v_t"], idx_d, geom, ks_d)
     T = V.teacher_tile_max(out["q_t"], out["k_t"], lse_d, geom)
