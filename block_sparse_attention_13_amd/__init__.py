@@ -312,9 +312,12 @@ def _queue_ptr(work_queue, dynamic, device):
 
 
 def _attn_args(q_t, k_t, v_t, idx, geom, k_per_head, with_lse, lse):
+    """Checks of the attention calls' tensors (q_t None: Q comes in raster
+    order and is checked by the caller); returns (k list, k_max, lse)."""
     tshape = _tiled_shape(geom, geom.head_dim)
     for name, t in (("q_tiled", q_t), ("k_tiled", k_t)):
-        _need(t, torch.bfloat16, tshape, name)
+        if t is not None:
+            _need(t, torch.bfloat16, tshape, name)
     _need(v_t, torch.bfloat16, _tiled_cm_shape(geom), "v_tiled")
     if idx.dim() != 4:
         raise ValueError("idx must be [B, heads, nT_max, k_max]")
@@ -324,7 +327,7 @@ def _attn_args(q_t, k_t, v_t, idx, geom, k_per_head, with_lse, lse):
     if len(ks) != geom.n_heads:
         raise ValueError("need one k per head")
     if with_lse and lse is None:
-        lse = torch.empty(tshape[:4], dtype=torch.float32, device=q_t.device)
+        lse = torch.empty(tshape[:4], dtype=torch.float32, device=k_t.device)
     if lse is not None:
         _need(lse, torch.float32, tshape[:4], "lse")
     return ks, k_max, lse
@@ -360,21 +363,8 @@ def sparse_attn_fwd_raster_io(q: torch.Tensor, k_t: torch.Tensor, v_t: torch.Ten
     """sparse_attn_fwd_raster reading Q in raster order too ([B, N, heads, d],
     any strided view with unit channel stride): the bytes it gives with the
     tiled Q of tile_permute(q), with no tiled copy of Q."""
-    tshape = _tiled_shape(geom, geom.head_dim)
     sq = _raster_strides(q, geom, "q")
-    _need(k_t, torch.bfloat16, tshape, "k_tiled")
-    _need(v_t, torch.bfloat16, _tiled_cm_shape(geom), "v_tiled")
-    if idx.dim() != 4:
-        raise ValueError("idx must be [B, heads, nT_max, k_max]")
-    k_max = idx.shape[3]
-    _need(idx, torch.int32, (geom.B, geom.n_heads, tshape[2], k_max), "idx")
-    ks = list(k_per_head)
-    if len(ks) != geom.n_heads:
-        raise ValueError("need one k per head")
-    if with_lse and lse is None:
-        lse = torch.empty(tshape[:4], dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _need(lse, torch.float32, tshape[:4], "lse")
+    ks, k_max, lse = _attn_args(None, k_t, v_t, idx, geom, k_per_head, with_lse, lse)
     if out is None:
         out = torch.empty((geom.B, geom.tokens, geom.n_heads, geom.head_dim), dtype=torch.bfloat16,
                           device=q.device)
