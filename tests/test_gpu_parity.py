@@ -537,3 +537,39 @@ def test_outputs_stay_in_their_buffers(tiled_q):
     for name, buf in checks:
         assert _guards_intact(buf), name
     assert torch.equal(o.view(torch.int16), out["o"].view(torch.int16))
+
+
+def test_layer_replays_in_a_graph():
+    """The layer captured in a HIP graph: its kernels only (the work-queue
+    counters are cleared by a kernel, not a memset). Between replays eager
+    work fills every output and the workspace with garbage; each replay must
+    give the eager layer's bytes again."""
+    V = _lib()
+    w = W["480p"].with_heads(4)
+    data = datagen.generate(w)
+    geom = geometry(w)
+    ks = w.k_per_head()
+    q, k, v = (to_dev_bf16(data[n]) for n in ("q", "k", "v"))
+    wq, wk = to_dev_bf16(data["wq"]), to_dev_bf16(data["wk"])
+    bufs = V.layer_forward(q, k, v, wq, wk, geom, ks)
+    torch.cuda.synchronize()
+    ref = {n: t.clone() for n, t in bufs.items() if n != "queue"}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        V.layer_forward(q, k, v, wq, wk, geom, ks, buffers=bufs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        V.layer_forward(q, k, v, wq, wk, geom, ks, buffers=bufs)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say(f"[graph] replay {rep}")
+        for t in bufs.values():
+            t.view(torch.uint8).fill_(0x5A + rep)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n, t in ref.items():
+            assert torch.equal(bufs[n].contiguous().view(torch.uint8), t.contiguous().view(torch.uint8)), (rep, n)
