@@ -268,7 +268,7 @@ def valid_pair_flops(w, idx_cpu) -> float:
     return 4.0 * w.d * total
 
 
-def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0):
+def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0, graph=True):
     """Generate the workload's inputs, run one layer to allocate every buffer,
     then time `steps` layers after `warmup` untimed ones with HIP events on
     the launch stream around each of the five stages. With `flush_mib`, time
@@ -349,6 +349,7 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0):
         flush = torch.empty(flush_mib << 20, dtype=torch.uint8, device=dev)
         out["flushed"] = timed(flush)
         del flush
+    out["graph_ms_step"] = graph_timed(step, steps) if graph else None
     out.update({"data": data if keep_data else None, "valid_flops": valid_pair_flops(w, bufs["idx"].cpu().numpy()),
                 "bitmask": bufs["bitmask"] if keep_data else None})
     if keep_data:  # head 0 of batch 0, for the parity check against the oracle
@@ -357,6 +358,34 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0):
     del bufs, q, k, v, wq, wk
     torch.cuda.empty_cache()
     return out
+
+
+def graph_timed(step, steps: int):
+    """The same layer captured once in a HIP graph and replayed `steps`
+    times (HIP events around the replays): ms per layer without the host's
+    launch overhead, which matters for the small workloads only."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del graph
+    log(f"[bench] graph replay: {ms:.4f} ms/layer")
+    return round(ms, 4)
 
 
 def dense_reference(V, w, data, trip_bitmask=None, steps=2, warmup=1):
@@ -514,6 +543,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense (every tile kept) reference")
     ap.add_argument("--no-tile-search", action="store_true", help="skip the head-aware tile search report")
     ap.add_argument("--no-distill", action="store_true", help="skip the estimator distillation report")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay timing (profiler runs: only the eager layers are traced)")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="time only the main workload (skip tiny, 480p, 720p, hc)")
     ap.add_argument("--cpu-sample-tiles", type=int, default=1920)
@@ -546,7 +577,7 @@ def main():
     w = datagen.WORKLOADS[args.workload]
     if args.heads:
         w = w.with_heads(args.heads)
-    r = run_workload(V, datagen, w, args.steps, args.warmup)
+    r = run_workload(V, datagen, w, args.steps, args.warmup, graph=not args.no_graph)
     ms_step, stage_ms, data = r["ms_step"], r["stage_ms"], r["data"]
     f_attn = attention_flops(w)
     achieved = f_attn / (stage_ms["sparse_attn"] * 1e-3) / 1e12
@@ -562,13 +593,14 @@ def main():
             if name == args.workload:
                 continue
             wo = datagen.WORKLOADS[name]
-            ro = run_workload(V, datagen, wo, 5, 2, keep_data=False, flush_mib=512)
+            ro = run_workload(V, datagen, wo, 5, 2, keep_data=False, flush_mib=512, graph=not args.no_graph)
             t_a = ro["stage_ms"]["sparse_attn"] * 1e-3
             fo, fv = attention_flops(wo), ro["valid_flops"]
             rf = ro["flushed"]
             per_config[name] = {
                 "workload": wo.description, "ms_per_layer": round(ro["ms_step"], 4),
                 "ms_per_layer_median": round(ro["ms_step_median"], 4), "ms_per_layer_min": round(ro["ms_step_min"], 4),
+                "ms_per_layer_graph": ro["graph_ms_step"],
                 "attn_ms": round(ro["stage_ms"]["sparse_attn"], 4),
                 "attn_tflops": round(fo / t_a / 1e12, 1), "attn_frac_bf16_peak": round(fo / t_a / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "attn_tflops_valid_pairs": round(fv / t_a / 1e12, 1),
@@ -585,7 +617,7 @@ def main():
     shard = None
     if not args.no_other_configs and not args.heads and w.heads >= 8:
         ws = w.with_heads(w.heads // 8)
-        rs = run_workload(V, datagen, ws, 5, 2, keep_data=False)
+        rs = run_workload(V, datagen, ws, 5, 2, keep_data=False, graph=False)
         t_a = rs["stage_ms"]["sparse_attn"] * 1e-3
         shard = {"workload": ws.description, "heads": ws.heads, "ms_per_layer": round(rs["ms_step"], 4),
                  "ms_per_layer_median": round(rs["ms_step_median"], 4), "stage_ms": rs["stage_ms"],
@@ -639,6 +671,7 @@ def main():
         "attn_frac_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
         "ms_per_layer_median": round(r["ms_step_median"], 3),
         "ms_per_layer_min": round(r["ms_step_min"], 3),
+        "ms_per_layer_graph": r["graph_ms_step"],
         "stage_ms": stage_ms,
         "stage_ms_median": r["stage_ms_median"],
         "stage_ms_min": r["stage_ms_min"],
