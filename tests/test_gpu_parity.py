@@ -573,3 +573,35 @@ def test_layer_replays_in_a_graph():
         torch.cuda.synchronize()
         for n, t in ref.items():
             assert torch.equal(bufs[n].contiguous().view(torch.uint8), t.contiguous().view(torch.uint8)), (rep, n)
+
+
+def test_concurrent_calls_with_separate_workspaces():
+    """Two attention calls in flight at once on two streams, each with its
+    own work-queue workspace (two different workloads), give the bytes the
+    same calls give one after the other."""
+    V = _lib()
+    runs = []
+    for w in (W["480p"].with_heads(6), dataclasses.replace(W["hc"].with_heads(3), B=1)):
+        data = datagen.generate(w)
+        geom, out, (q, _, _, _, _) = run_layer(w, data)
+        runs.append((geom, w.k_per_head(), q, out))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    results = []
+    for rep in range(3):
+        say(f"[streams] round {rep}")
+        outs = []
+        for (geom, ks, q, out), st in zip(runs, streams):
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                o = torch.full_like(out["o"], 7)
+                lse = torch.full_like(out["lse"], 7.0)
+                V.sparse_attn_fwd_raster_io(q, out["k_t"], out["v_t"], out["idx"], geom, ks, out=o, lse=lse,
+                                            work_queue=V.attn_queue(q.device))
+                outs.append((o, lse))
+        torch.cuda.synchronize()
+        results.append(outs)
+    for outs in results:
+        for (o, lse), (_, _, _, out) in zip(outs, runs):
+            assert torch.equal(o.view(torch.int16), out["o"].view(torch.int16))
+            assert torch.equal(lse.view(torch.int32), out["lse"].view(torch.int32))
