@@ -423,26 +423,37 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
   __syncthreads();  // every wave is done with the tile buffers
 
   // Merge the two key halves through LDS (the tile buffers are free now):
-  // m = max(m0, m1), O = O0 2^(m0-m) + O1 2^(m1-m), l likewise.
+  // m = max(m0, m1), O = O0 2^(m0-m) + O1 2^(m1-m), l likewise. Both halves
+  // share the work: half 0 finishes O^T blocks 0..kDB/2-1 and half 1 blocks
+  // kDB/2..kDB-1, each reading the other half's partials of its blocks, so
+  // all eight waves combine and store O.
+  constexpr int kOwn = S::kDB / 2;                           // O^T blocks each half finishes
   float* red = reinterpret_cast<float*>(&lds[0][0]);        // [4][kDB*16][64] partial O^T
-  float* red_ml = red + 4 * S::kDB * 16 * 64;                // [4][2][64] m, l
-  static_assert(sizeof(lds) >= (4 * S::kDB * 16 * 64 + 4 * 2 * 64) * sizeof(float), "merge space");
+  float* red_ml = red + 4 * S::kDB * 16 * 64;                // [4][2 halves][2][64] m, l
+  static_assert(sizeof(lds) >= (4 * S::kDB * 16 * 64 + 4 * 2 * 2 * 64) * sizeof(float), "merge space");
   const float l_half = w.l_run + __shfl_xor(w.l_run, 32, 64);
-  if (half == 1) {
+  // The blocks the other half finishes (register indices fixed at compile time on each branch).
+  auto give = [&](auto first) {
+    constexpr int f = decltype(first)::value;
 #pragma unroll
-    for (int db = 0; db < S::kDB; ++db)
+    for (int d2 = 0; d2 < kOwn; ++d2)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) red[((qg * S::kDB + db) * 16 + v) * 64 + lane] = w.oacc[db][v];
-    red_ml[(qg * 2 + 0) * 64 + lane] = w.m_run;
-    red_ml[(qg * 2 + 1) * 64 + lane] = l_half;
-  }
+      for (int v = 0; v < 16; ++v) red[((qg * S::kDB + f + d2) * 16 + v) * 64 + lane] = w.oacc[f + d2][v];
+  };
+  if (half == 0)
+    give(std::integral_constant<int, kOwn>{});
+  else
+    give(std::integral_constant<int, 0>{});
+  red_ml[((qg * 2 + half) * 2 + 0) * 64 + lane] = w.m_run;
+  red_ml[((qg * 2 + half) * 2 + 1) * 64 + lane] = l_half;
   __syncthreads();
-  if (half == 0) {
-    const float m1 = red_ml[(qg * 2 + 0) * 64 + lane];
-    const float l1 = red_ml[(qg * 2 + 1) * 64 + lane];
-    const float m = fmaxf(w.m_run, m1);
-    const float a0 = __builtin_amdgcn_exp2f(w.m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
-    const float l_tot = l_half * a0 + l1 * a1;
+  {
+    // m, l of half 0 and half 1, in that order on both halves, so both compute the same l_tot.
+    const float m0 = red_ml[((qg * 2 + 0) * 2 + 0) * 64 + lane], l0 = red_ml[((qg * 2 + 0) * 2 + 1) * 64 + lane];
+    const float m1 = red_ml[((qg * 2 + 1) * 2 + 0) * 64 + lane], l1 = red_ml[((qg * 2 + 1) * 2 + 1) * 64 + lane];
+    const float m = fmaxf(m0, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m0 - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+    const float l_tot = l0 * a0 + l1 * a1;
     const float inv = 1.0f / l_tot;
     const float c0 = a0 * inv, c1 = a1 * inv;
     uint16_t* orow;
@@ -452,23 +463,37 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
       const int64_t n = raster_of_slot(g, hg, box_extent(g, hg, tq), qg * 32 + l32);
       orow = n >= 0 ? o_r + int64_t(b) * osb + n * osn + int64_t(hd) * osh : nullptr;
     }
+    // Half 0's partial times c0 plus half 1's times c1, for the blocks this half finishes.
+    auto finish = [&](auto first, auto is_half0) {
+      constexpr int f = decltype(first)::value;
+      constexpr bool h0 = decltype(is_half0)::value;
 #pragma unroll
-    for (int db = 0; db < S::kDB; ++db) {
-      float o[16];
+      for (int d2 = 0; d2 < kOwn; ++d2) {
+        const int db = f + d2;
+        float o[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) o[v] = w.oacc[db][v] * c0 + red[((qg * S::kDB + db) * 16 + v) * 64 + lane] * c1;
+        for (int v = 0; v < 16; ++v) {
+          const float mine = w.oacc[db][v], theirs = red[((qg * S::kDB + db) * 16 + v) * 64 + lane];
+          o[v] = h0 ? mine * c0 + theirs * c1 : theirs * c0 + mine * c1;
+        }
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        u32x2 wd;
-        wd[0] = pack_bf16x2(o[4 * g4 + 0], o[4 * g4 + 1]);
-        wd[1] = pack_bf16x2(o[4 * g4 + 2], o[4 * g4 + 3]);
-        if (orow) *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g4 + 4 * h) = wd;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          u32x2 wd;
+          wd[0] = pack_bf16x2(o[4 * g4 + 0], o[4 * g4 + 1]);
+          wd[1] = pack_bf16x2(o[4 * g4 + 2], o[4 * g4 + 3]);
+          if (orow) *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g4 + 4 * h) = wd;
+        }
       }
-    }
+    };
+    if (half == 0)
+      finish(std::integral_constant<int, 0>{}, std::true_type{});
+    else
+      finish(std::integral_constant<int, kOwn>{}, std::false_type{});
     // A pad query slot has no token in a raster output: its LSE is -inf there.
-    const bool pad_slot = o_r && !slot_is_real(hg, box_extent(g, hg, tq), qg * 32 + l32);
-    if (lse_tile && h == 0)
+    if (half == 0 && lse_tile && h == 0) {
+      const bool pad_slot = o_r && !slot_is_real(hg, box_extent(g, hg, tq), qg * 32 + l32);
       lse_tile[qg * 32 + l32] = pad_slot ? -__builtin_inff() : (m + __log2f(l_tot)) * 0.69314718055994530942f;
+    }
   }
 }
 
