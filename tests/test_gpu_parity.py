@@ -146,6 +146,22 @@ def test_layer_matches_oracle(name, heads, tiles_per_head):
         assert np.all(np.diff(row, axis=1) > 0) and row.min() >= 0 and row.max() < nT
 
 
+def test_batched_layer_matches_oracle():
+    """Batch 2 against the oracle, per batch entry: 720p geometry with 4 heads
+    (5,760 query tiles, so the attention hands tiles out through the work
+    queue), sampled heads and query tiles of both entries."""
+    w = dataclasses.replace(W["720p"].with_heads(4), B=2)
+    say(f"[parity] {w.description} B {w.B}")
+    data = datagen.generate(w)
+    geom, out, _ = run_layer(w, data)
+    assert "queue" in out
+    ks = w.k_per_head()
+    for b, hd in ((0, 1), (1, 0), (1, 3)):
+        nT = w.tiles_per_head()[hd]
+        check_head(w, data, out, hd, ks, _sample_tiles(nT, 6, seed=10 * b + hd), b=b)
+    assert not torch.equal(out["o"][0], out["o"][1])
+
+
 def test_estimator_is_deterministic():
     V = _lib()
     w = W["480p"]
