@@ -107,10 +107,10 @@ typedef struct { int32_t T, H, W; } veda_grid;
 typedef struct { int32_t pt, ph, pw; } veda_tile;
 
 typedef struct {
-  int32_t B;                   /* batch */
+  int32_t B;                   /* batch, 1..65535 (an empty batch is VEDA_ERR_SHAPE) */
   int32_t n_heads;             /* attention heads, 1..VEDA_MAX_HEADS */
   int32_t head_dim;            /* d: 64 or 128 */
-  veda_grid grid;              /* latent grid (T, H, W) */
+  veda_grid grid;              /* latent grid (T, H, W), each extent >= 1 */
   const veda_tile* head_tile;  /* host array [n_heads]: tile shape of each head */
 } veda_geom;
 

@@ -66,6 +66,9 @@ def test_geometry_errors():
     assert L.veda_num_tiles(bad_d.c, 0) == -2
     assert L.veda_num_tiles(_geom().c, 1) == -2
     bad_grid = _geom(grid=(0, 8, 8))
+    assert L.veda_max_tiles(_geom(B=0).c) == -2    # empty batch
+    assert L.veda_max_tiles(_geom(B=65536).c) == -2
+    assert L.veda_max_tiles(_geom(B=65535).c) > 0
     assert L.veda_max_tiles(bad_grid.c) == -2
     huge = _geom(grid=(4096, 4096, 8), tiles=((4, 4, 8),))
     assert L.veda_max_tiles(huge.c) == -2          # more than VEDA_MAX_TILES boxes
