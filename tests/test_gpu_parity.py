@@ -162,6 +162,21 @@ def test_batched_layer_matches_oracle():
     assert not torch.equal(out["o"][0], out["o"][1])
 
 
+def test_head_dim_64_layer_matches_oracle():
+    """d = 64, r = 64 against the oracle: grid 9 x 27 x 33 with (2, 4, 16)
+    tiles leaves every axis ragged (105 tiles per head, k = 3), and B = 4
+    x 3 heads gives 1,260 query tiles, so the attention runs through the
+    work queue. Every query tile of four (batch, head) pairs is checked."""
+    w = dataclasses.replace(_random_workload((9, 27, 33), [(2, 4, 16)], 64, 64, heads=3, seed=4, k=3), B=4)
+    say(f"[parity] d 64: grid {w.grid} B {w.B} heads {w.heads} items {max(w.tiles_per_head()) * w.heads * w.B}")
+    data = datagen.generate(w)
+    geom, out, _ = run_layer(w, data)
+    assert "queue" in out
+    ks = w.k_per_head()
+    for b, hd in ((0, 0), (1, 2), (3, 1), (3, 2)):
+        check_head(w, data, out, hd, ks, list(range(w.tiles_per_head()[hd])), b=b)
+
+
 def test_estimator_is_deterministic():
     V = _lib()
     w = W["480p"]
