@@ -395,6 +395,21 @@ def test_largest_tile_count():
     check_head(w, data, out, 0, w.k_per_head(), _sample_tiles(8192, 6, 1))
 
 
+def test_largest_head_count():
+    """The library's limit of 128 heads (three tile shapes in turn, so the
+    last head's geometry differs from the first's) through the whole layer;
+    the oracle checks every query tile of four heads, the last among them."""
+    V = _lib()
+    w = _random_workload((3, 9, 17), [(1, 8, 16), (8, 4, 4), (2, 8, 8)], 64, 32, heads=128, seed=23, k=2)
+    assert w.heads == V._lib.VEDA_MAX_HEADS
+    say(f"[max] {w.heads} heads, tiles per head {sorted(set(w.tiles_per_head()))}")
+    data = datagen.generate(w)
+    geom, out, _ = run_layer(w, data)
+    ks = w.k_per_head()
+    for hd in (0, 1, 65, 127):
+        check_head(w, data, out, hd, ks, list(range(w.tiles_per_head()[hd])))
+
+
 def test_equal_scores_keep_the_lower_tile():
     """Duplicate key tiles give exactly equal scores: the lower index must win
     end to end, and the lists must match the oracle's."""
