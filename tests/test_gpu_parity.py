@@ -410,6 +410,22 @@ def test_largest_head_count():
         check_head(w, data, out, hd, ks, list(range(w.tiles_per_head()[hd])))
 
 
+def test_extreme_k_mixed_across_heads():
+    """One call with k = 1 on one head, k = every tile on the next and a
+    middle k on the third (three tile shapes, ragged boxes, B = 2): the
+    per-head k reaches Top-k, the masks and the attention loop unchanged."""
+    w = dataclasses.replace(_random_workload((3, 9, 17), [(1, 8, 16), (8, 4, 4), (2, 8, 8)], 128, 64, heads=3,
+                                             seed=29, k=2), B=2)
+    nT = w.tiles_per_head()
+    ks = [1, nT[1], nT[2] // 2]
+    say(f"[k] tiles per head {nT}, k {ks}")
+    data = datagen.generate(w)
+    geom, out, _ = run_layer(w, data, k_per_head=ks)
+    for b in range(w.B):
+        for hd in range(w.heads):
+            check_head(w, data, out, hd, ks, list(range(nT[hd])), b=b)
+
+
 def test_equal_scores_keep_the_lower_tile():
     """Duplicate key tiles give exactly equal scores: the lower index must win
     end to end, and the lists must match the oracle's."""
