@@ -426,6 +426,28 @@ def test_extreme_k_mixed_across_heads():
             check_head(w, data, out, hd, ks, list(range(nT[hd])), b=b)
 
 
+@pytest.mark.parametrize("scale", [0.35, 0.02])
+def test_explicit_softmax_scale(scale):
+    """A caller's softmax scale in place of 1/sqrt(d): 0.35 makes the
+    softmax sharp, 0.02 nearly uniform. O and the LSE (of the scaled
+    logits) against the oracle run with the same scale."""
+    V = _lib()
+    w = _random_workload((3, 9, 17), [(1, 8, 16), (8, 4, 4)], 128, 64, heads=2, seed=31, k=3)
+    data = datagen.generate(w)
+    geom, out, (q, _, _, _, _) = run_layer(w, data)
+    ks = w.k_per_head()
+    o, lse = V.sparse_attn_fwd_raster_io(q, out["k_t"], out["v_t"], out["idx"], geom, ks, scale=scale)
+    torch.cuda.synchronize()
+    for hd in range(w.heads):
+        nT = w.tiles_per_head()[hd]
+        r = oracle_head(data, w, 0, hd, ks[hd], query_tiles=list(range(nT)), scale=scale)
+        assert np.array_equal(out["idx"][0, hd].cpu().numpy()[:nT, :ks[hd]], r["idx"]), ("idx", hd)
+        rows = np.flatnonzero(np.isfinite(r["lse"]))
+        compare_o(f32_of_bf16(o[0, :, hd, :])[rows], r["o"][rows], f"scale {scale} head {hd} O")
+        pos = O.tiled_position(w.grid, w.head_tiles()[hd])
+        compare_lse(lse[0, hd].cpu().numpy().reshape(-1)[pos[rows]], r["lse"][rows], f"scale {scale} head {hd}")
+
+
 def test_equal_scores_keep_the_lower_tile():
     """Duplicate key tiles give exactly equal scores: the lower index must win
     end to end, and the lists must match the oracle's."""
