@@ -448,6 +448,28 @@ def test_explicit_softmax_scale(scale):
         compare_lse(lse[0, hd].cpu().numpy().reshape(-1)[pos[rows]], r["lse"][rows], f"scale {scale} head {hd}")
 
 
+def test_running_max_rescales():
+    """Logits that climb with the key tile's index: channel 0 of every query
+    is 8 and of every key 2 x its tile's index, which adds about 2 (base 2)
+    per tile at d = 128. The ascending key loop then meets a row max more
+    than 8 above the running one every few tiles, so the online softmax
+    rescales O, l and m many times per row; O and the LSE against the oracle."""
+    w = _random_workload((3, 9, 17), [(1, 8, 16), (8, 4, 4)], 128, 64, heads=2, seed=37, k=2)
+    data = datagen.generate(w)
+    nT = w.tiles_per_head()
+    ks = [t // 2 + 1 for t in nT]
+    for hd in range(w.heads):
+        tile_of = O.tiled_position(w.grid, w.head_tiles()[hd]) // 128
+        data["q"][0, :, hd, 0] = O.float_to_bf16_bits(np.full(w.tokens, 8.0, np.float32))
+        data["k"][0, :, hd, 0] = O.float_to_bf16_bits((2.0 * tile_of).astype(np.float32))
+    say(f"[rescale] tiles per head {nT}, k {ks}")
+    geom, out, _ = run_layer(w, data, k_per_head=ks)
+    for hd in range(w.heads):
+        r = check_head(w, data, out, hd, ks, list(range(nT[hd])))
+        sel = r["idx"]
+        assert (sel[:, -1] - sel[:, 0]).max() >= 8, "the selections must span enough tiles to force rescales"
+
+
 def test_equal_scores_keep_the_lower_tile():
     """Duplicate key tiles give exactly equal scores: the lower index must win
     end to end, and the lists must match the oracle's."""
