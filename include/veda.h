@@ -65,6 +65,12 @@
  * (scores and lse) or -1 (idx) and 0 (bitmask); scores outside the head's
  * nT_hd x nT_hd block are -inf; idx entries past k_hd are -1.
  *
+ * Values: device data is never inspected, and inputs are expected finite.
+ * A NaN score orders by its bit pattern (above every finite score with the
+ * sign bit clear, below with it set), so index lists stay ascending, in
+ * range and k_hd long; a NaN or inf in Q, K, V or W reaches the outputs
+ * computed from it.
+ *
  * Errors: every call returns VEDA_OK (0) or a negative status. All argument
  * checks run on the host BEFORE anything is enqueued, so a call that fails
  * them writes nothing. Checks: null pointers; B, heads or a grid edge <= 0;
