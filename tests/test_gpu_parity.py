@@ -520,6 +520,33 @@ def test_topk_on_crafted_scores():
         assert np.all(idx[0, 0, rows:].cpu().numpy() == np.arange(k))
 
 
+def test_topk_orders_nan_scores_by_bit_pattern():
+    """Three +NaN and five -NaN scores in every row (no infinities): +NaN
+    ranks above every finite score and -NaN below, so the lists equal the
+    oracle's with +NaN read as +inf and -NaN as -inf, every +NaN tile is
+    kept and no -NaN tile is."""
+    V = _lib()
+    rng = np.random.default_rng(41)
+    g = V.Geometry(1, 1, 128, (21, 30, 52), [(4, 4, 8)])
+    nT, k = g.max_tiles(), 34
+    S = rng.standard_normal((nT, nT)).astype(np.float32)
+    pos_nan = np.array([0x7FC00000], np.uint32).view(np.float32)[0]
+    neg_nan = np.array([0xFFC00000], np.uint32).view(np.float32)[0]
+    for i in range(nT):
+        c = rng.choice(nT, size=8, replace=False)
+        S[i, c[:3]] = pos_nan
+        S[i, c[3:]] = neg_nan
+    as_inf = np.where(np.isnan(S), np.where(np.signbit(S), np.float32(-np.inf), np.float32(np.inf)), S)
+    idx, _ = V.topk_mask(torch.from_numpy(S).reshape(1, 1, nT, nT).cuda(), g, [k])
+    torch.cuda.synchronize()
+    got = idx[0, 0].cpu().numpy()
+    assert np.array_equal(got, O.topk(as_inf.astype(np.float32), k))
+    for i in range(nT):
+        kept = set(got[i].tolist())
+        assert set(np.flatnonzero(np.isposinf(as_inf[i])).tolist()) <= kept
+        assert not set(np.flatnonzero(np.isneginf(as_inf[i])).tolist()) & kept
+
+
 @pytest.mark.parametrize("tiled_q", [False, True])
 def test_every_output_byte_is_written(tiled_q):
     """Outputs pre-filled with garbage end up fully defined."""
