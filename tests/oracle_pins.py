@@ -450,6 +450,72 @@ def check_tile_search_errors(O, seed=10):
     assert np.all(O.tile_search_errors(q, k, v, wq, wk, grid, cands, lambda n: n) < 1e-20)
 
 
+# ------------------------------------------------------------ whole layer
+
+def _tile_members(grid, tile):
+    """Raster tokens of each tile, from the brute-force enumeration."""
+    pos, _ = brute_force_positions(grid, tile)
+    vol = tile[0] * tile[1] * tile[2]
+    return pos // vol, pos % vol
+
+
+def check_head_forward_wiring(O):
+    """The whole layer of one head, wired step by step, against an independent
+    route from raster coordinates. Inputs are small integers, so the mean,
+    max, projections and scores are exact; W_q picks the avg block and W_k
+    the max block, so swapping the projections or pooling the wrong tensor
+    changes the scores. The expected tile statistics come from the
+    brute-force tile membership (torch float32 divide, then torch's
+    round-to-nearest-even to bfloat16); the mask from an exhaustive sort;
+    O and LSE from torch scaled_dot_product_attention with a boolean token
+    mask at its own default scale 1/sqrt(d) (the oracle's default must agree)."""
+    import torch
+    rng = np.random.default_rng(13)
+    grid, tile, d, r, k_keep = (3, 4, 7), (2, 2, 4), 4, 4, 3      # ragged on two axes: 8 boxes of 16
+    N = grid[0] * grid[1] * grid[2]
+    q = rng.integers(-8, 9, size=(N, d)).astype(np.float32)
+    k = rng.integers(-8, 9, size=(N, d)).astype(np.float32)
+    v = rng.integers(-8, 9, size=(N, d)).astype(np.float32) / np.float32(4)
+    wq = np.zeros((3 * d, r), np.float32)
+    wk = np.zeros((3 * d, r), np.float32)
+    wq[np.arange(r), np.arange(r)] = 1.0                          # avg block of Q
+    wk[d + np.arange(r), np.arange(r)] = 1.0                      # max block of K
+    res = O.head_forward(q, k, v, wq, wk, grid, tile, k_keep)
+    tile_of, _ = _tile_members(grid, tile)
+    nT = int(tile_of.max()) + 1
+    assert O.num_tiles(grid, tile) == nT == 8
+
+    def stats(x):
+        out = np.zeros((nT, 3 * d), np.float64)
+        for j in range(nT):
+            rows = x[tile_of == j]
+            mean = (torch.tensor(rows.sum(axis=0), dtype=torch.float32) / len(rows)).to(torch.bfloat16)
+            out[j] = np.concatenate([mean.double().numpy(), rows.max(axis=0), rows.min(axis=0)])
+        return out
+
+    sq, sk = stats(q), stats(k)
+    assert np.array_equal(res["stats_q"].astype(np.float64), sq)
+    assert np.array_equal(res["stats_k"].astype(np.float64), sk)
+    assert np.array_equal(res["feat_q"].astype(np.float64), sq[:, :r])
+    assert np.array_equal(res["feat_k"].astype(np.float64), sk[:, d:d + r])
+    S = sq[:, :r] @ sk[:, d:d + r].T
+    assert np.array_equal(res["scores"].astype(np.float64), S)
+    for i in range(nT):
+        best = sorted(range(nT), key=lambda j: (-S[i, j], j))[:k_keep]
+        assert res["idx"][i].tolist() == sorted(best), i
+    allowed = np.zeros((N, N), bool)
+    for n in range(N):
+        allowed[n] = np.isin(tile_of, res["idx"][tile_of[n]])
+    t = lambda a: torch.from_numpy(a.astype(np.float64))[None, None]
+    mask = torch.from_numpy(allowed)[None, None]
+    want = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=mask)[0, 0].numpy()
+    logits = (t(q) @ t(k).transpose(-1, -2))[0, 0] / math.sqrt(d)
+    want_lse = torch.logsumexp(logits.masked_fill(~torch.from_numpy(allowed), -math.inf), dim=-1).numpy()
+    assert np.max(np.abs(res["o"] - want)) < 1e-12
+    assert np.max(np.abs(res["lse"] - want_lse)) < 1e-12
+    assert np.array_equal(O.tile_unpermute(res["vt"], grid, tile), v)
+
+
 # ------------------------------------------------------------- distillation
 
 def check_distill_gradient_finite_differences(O, seed=11):
@@ -528,6 +594,7 @@ ALL_SMALL_CHECKS = [
     check_teacher_uniform_keys,
     check_recall_golden,
     check_tile_search_errors,
+    check_head_forward_wiring,
     check_distill_gradient_finite_differences,
     check_distill_kl_closed_forms,
     check_adam_first_steps,

@@ -73,6 +73,20 @@ MUTANTS = {
         ("dFq = dS @ np.asarray(feat_k, np.float64)", "dFq = dS @ np.asarray(feat_q, np.float64)"),
     "adam without bias correction":
         ("mh = m / (1 - beta1 ** step)", "mh = m"),
+    "layer projects Q with W_k and K with W_q":
+        [("feat_q = project(stats_q, wq)", "feat_q = project(stats_q, wk)"),
+         ("feat_k = project(stats_k, wk)", "feat_k = project(stats_k, wq)")],
+    "layer pools K's statistics from Q's tiles":
+        ("stats_k = trippool(kt, valid, vol)", "stats_k = trippool(qt, valid, vol)"),
+    "layer default scale 1/d":
+        ("scale = 1.0 / math.sqrt(d)\n    vol = tile[0]", "scale = 1.0 / d\n    vol = tile[0]"),
+    "tile search default scale 1/d":
+        ("scale = 1.0 / math.sqrt(d)\n    o_dense", "scale = 1.0 / d\n    o_dense"),
+    "layer scores key tiles against query tiles":
+        ("S = tile_scores(feat_q, feat_k)", "S = tile_scores(feat_k, feat_q)"),
+    "layer attends to K in place of V":
+        ("o, lse = sparse_attention(q, k, v, grid, tile, idx, scale, query_tiles)",
+         "o, lse = sparse_attention(q, k, k, grid, tile, idx, scale, query_tiles)"),
     "mask overlap counts either mask":
         ("both = np.asarray(bitmask_a, dtype=np.uint32) & np.asarray(bitmask_b, dtype=np.uint32)",
          "both = np.asarray(bitmask_a, dtype=np.uint32) | np.asarray(bitmask_b, dtype=np.uint32)"),
@@ -83,7 +97,7 @@ def _mutant(edits):
     with open(SRC) as f:
         src = f.read()
     for old, new in ([edits] if isinstance(edits, tuple) else edits):
-        assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+        assert src.count(old) == 1, f"mutation anchor must occur exactly once: {old!r}"
         src = src.replace(old, new, 1)
     mod = types.ModuleType("oracle_mutant")
     exec(compile(src, SRC + " (mutant)", "exec"), mod.__dict__)
