@@ -16,6 +16,7 @@ Python: the five steps of the layer are HIP kernels.
   sparse_attn_fwd_raster  sparse_attn_fwd writing raster O (no unpermute pass)
   tile_stats       the TripPool statistics of raster Q or K alone (no tiled copy)
   sparse_attn_fwd_raster_io  sparse_attn_fwd_raster reading raster Q (no tiled Q)
+  sparse_attn_fwd_raster_io_noalloc  the same with the library's static work queue: allocates nothing
   attn_queue       workspace of the attention calls' work queue (query tiles handed out at run time)
   layer_forward    the layer: tile_stats of Q, tile_permute_stats of K, tile_permute
                    of V, trippool_project_score, topk_mask, sparse_attn_fwd_raster_io
@@ -53,7 +54,7 @@ from ._lib import VedaError
 
 __all__ = ["Geometry", "VedaError", "tile_permute", "tile_permute_stats", "tile_unpermute", "trippool_score",
            "trippool_project_score", "topk_mask", "sparse_attn_fwd_raster", "tile_stats",
-           "sparse_attn_fwd_raster_io",
+           "sparse_attn_fwd_raster_io", "sparse_attn_fwd_raster_io_noalloc",
            "sparse_attn_fwd", "attn_queue", "layer_forward",
            "dense_index", "teacher_tile_max", "mask_overlap", "tile_recall",
            "head_sq_error", "candidate_tiles", "tile_search", "distill_kl", "distill_grad", "adam_step",
@@ -374,6 +375,25 @@ def sparse_attn_fwd_raster_io(q: torch.Tensor, k_t: torch.Tensor, v_t: torch.Ten
         geom.c, q.data_ptr(), sq, k_t.data_ptr(), v_t.data_ptr(), idx.data_ptr(), _lib.int_array(ks), int(k_max), sc,
         out.data_ptr(), so, lse.data_ptr() if lse is not None else None, _queue_ptr(work_queue, dynamic, q.device),
         _stream(q)), "veda_sparse_attn_fwd_raster_io")
+    return out, lse
+
+
+def sparse_attn_fwd_raster_io_noalloc(q: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, idx: torch.Tensor,
+                                      geom: Geometry, k_per_head: Sequence[int], out: torch.Tensor,
+                                      lse: Optional[torch.Tensor] = None,
+                                      scale: Optional[float] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """sparse_attn_fwd_raster_io for callers that cannot allocate: `out`
+    (and `lse`, if wanted) come from the caller and the work queue is the
+    library's static one, so the call allocates nothing. Calls that may
+    overlap in time on one device race on that queue."""
+    sq = _raster_strides(q, geom, "q")
+    ks, k_max, lse = _attn_args(None, k_t, v_t, idx, geom, k_per_head, False, lse)
+    so = _raster_strides(out, geom, "out")
+    sc = float(scale) if scale is not None else 0.0
+    _lib.check(_lib.lib.veda_sparse_attn_fwd_raster_io_noalloc(
+        geom.c, q.data_ptr(), sq, k_t.data_ptr(), v_t.data_ptr(), idx.data_ptr(), _lib.int_array(ks), int(k_max), sc,
+        out.data_ptr(), so, lse.data_ptr() if lse is not None else None, _stream(q)),
+        "veda_sparse_attn_fwd_raster_io_noalloc")
     return out, lse
 
 

@@ -27,7 +27,7 @@ EXPORTS = ["veda_status_str", "veda_num_tiles", "veda_max_tiles", "veda_tile_per
            "veda_topk_mask", "veda_sparse_attn_fwd", "veda_tile_unpermute", "veda_teacher_tile_max",
            "veda_mask_overlap", "veda_head_sq_error", "veda_distill_kl", "veda_distill_grad",
            "veda_adam_step", "veda_tile_permute_stats", "veda_trippool_project_score",
-           "veda_sparse_attn_fwd_raster", "veda_sparse_attn_fwd_raster_io"]
+           "veda_sparse_attn_fwd_raster", "veda_sparse_attn_fwd_raster_io", "veda_sparse_attn_fwd_raster_io_noalloc"]
 
 
 class VedaGrid(ctypes.Structure):
@@ -91,6 +91,10 @@ def _load():
                                                    c_void_p, POINTER(c_int32), c_int32, c_float, c_void_p,
                                                    VedaRasterStrides, c_void_p, c_void_p, c_void_p]
     lib.veda_sparse_attn_fwd_raster_io.restype = ctypes.c_int
+    lib.veda_sparse_attn_fwd_raster_io_noalloc.argtypes = [POINTER(VedaGeom), c_void_p, VedaRasterStrides, c_void_p,
+                                                           c_void_p, c_void_p, POINTER(c_int32), c_int32, c_float,
+                                                           c_void_p, VedaRasterStrides, c_void_p, c_void_p]
+    lib.veda_sparse_attn_fwd_raster_io_noalloc.restype = ctypes.c_int
     lib.veda_teacher_tile_max.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p,
                                           c_void_p]
     lib.veda_teacher_tile_max.restype = ctypes.c_int

@@ -41,6 +41,9 @@
 // spares the layer a separate unpermute pass. Q likewise comes from tiled Q,
 // or straight from each real token's raster row (a pad slot gets a zero
 // query, as tiled Q holds there), which spares the layer a tiled copy of Q.
+#include <atomic>
+#include <mutex>
+
 #include "attn_tiles.hpp"
 
 namespace veda {
@@ -497,7 +500,39 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
   }
 }
 
+// The work queue of the allocation-free attention call: one queue's
+// counters in a file-scope device array, so that a caller that cannot
+// allocate needs no workspace. Each device holds its own copy; host code
+// never passes the array's name to a kernel (in host code it only stands in
+// for the symbol) but the address hipGetSymbolAddress gives on that device,
+// looked up once per device with the device current.
+static __device__ __align__(256) int32_t scratch[kAttnQueueInts];
+
 }  // namespace
+
+hipError_t attn_scratch_queue(int32_t** queue) {
+  constexpr int kDevices = 64;
+  static std::atomic<int32_t*> addr[kDevices];
+  static std::mutex lock;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+  int32_t* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> g(lock);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* sym = nullptr;
+      e = hipGetSymbolAddress(&sym, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      p = static_cast<int32_t*>(sym);
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *queue = p;
+  return hipSuccess;
+}
 
 hipError_t launch_sparse_attn(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t, const uint16_t* v_t,
                               const int32_t* idx, int32_t k_max, float scale, uint16_t* o_t, float* lse,

@@ -2,7 +2,8 @@
 // launches. Every argument check runs on the host before any HIP call, so an
 // invalid call enqueues nothing and writes nothing. The library allocates no
 // device memory; the only process-wide state is a per-device cache of the
-// architecture check.
+// architecture check and, for the allocation-free attention call, of the
+// address of its static work queue on each device.
 #include <atomic>
 #include <cmath>
 #include <cstring>
@@ -297,6 +298,34 @@ int veda_sparse_attn_fwd_raster_io(const veda_geom* g, const void* q_raster, ved
       t, nullptr, static_cast<const uint16_t*>(k_tiled), static_cast<const uint16_t*>(v_tiled), idx, k_max,
       softmax_scale, nullptr, lse, static_cast<uint16_t*>(o_raster), so.b, so.n, so.h,
       static_cast<const uint16_t*>(q_raster), sq.b, sq.n, sq.h, work_queue, static_cast<hipStream_t>(stream)));
+}
+
+int veda_sparse_attn_fwd_raster_io_noalloc(const veda_geom* g, const void* q_raster, veda_raster_strides sq,
+                                           const void* k_tiled, const void* v_tiled, const int32_t* idx,
+                                           const int32_t* k_per_head, int32_t k_max, float softmax_scale,
+                                           void* o_raster, veda_raster_strides so, float* lse, void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!q_raster || !k_tiled || !v_tiled || !idx || !o_raster) return VEDA_ERR_NULL;
+  VEDA_TRY(set_k(k_per_head, k_max, &t));
+  for (const void* p : {q_raster, k_tiled, v_tiled, static_cast<const void*>(idx), static_cast<const void*>(o_raster)})
+    if (!aligned16(p)) return VEDA_ERR_ALIGN;
+  if (lse && !aligned16(lse)) return VEDA_ERR_ALIGN;
+  // The static queue counts at most 2^28 work items, as a caller's workspace does.
+  if (int64_t(t.B) * t.heads * t.nT_max > (int64_t(1) << 28)) return VEDA_ERR_SHAPE;
+  VEDA_TRY(check_strides(sq));
+  VEDA_TRY(check_strides(so));
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) softmax_scale = 1.0f / std::sqrt(float(t.d));
+  VEDA_TRY(check_device());
+  int32_t* queue = nullptr;
+  if (veda::attn_scratch_queue(&queue) != hipSuccess) {
+    (void)hipGetLastError();
+    return VEDA_ERR_DEVICE;
+  }
+  return launched(veda::launch_sparse_attn(
+      t, nullptr, static_cast<const uint16_t*>(k_tiled), static_cast<const uint16_t*>(v_tiled), idx, k_max,
+      softmax_scale, nullptr, lse, static_cast<uint16_t*>(o_raster), so.b, so.n, so.h,
+      static_cast<const uint16_t*>(q_raster), sq.b, sq.n, sq.h, queue, static_cast<hipStream_t>(stream)));
 }
 
 int veda_teacher_tile_max(const veda_geom* g, const void* q_tiled, const void* k_tiled, const float* lse_dense,

@@ -148,6 +148,9 @@ hipError_t launch_adam(int64_t n, float* w, const float* grad, float* m, float* 
                        float eps, float bc1, float bc2, uint16_t* w_bf16, hipStream_t s);
 // O goes to o_t (tiled) when o_r is null, else straight to raster o_r with
 // element strides (osb, osn, osh).
+// Address, on the current device, of the static work queue used by the
+// allocation-free attention call (looked up once per device).
+hipError_t attn_scratch_queue(int32_t** queue);
 hipError_t launch_sparse_attn(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t, const uint16_t* v_t,
                               const int32_t* idx, int32_t k_max, float scale, uint16_t* o_t, float* lse,
                               uint16_t* o_r, int64_t osb, int64_t osn, int64_t osh, const uint16_t* q_r,

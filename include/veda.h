@@ -34,7 +34,9 @@
  * --------------------------------
  * Tensors are DEVICE pointers allocated and owned by the caller; the library
  * never allocates, frees or caches device memory and keeps no state between
- * calls (re-entrant, thread-safe). Small arrays marked "host" are read during
+ * calls (re-entrant, thread-safe). The one exception is
+ * veda_sparse_attn_fwd_raster_io_noalloc, whose 64-byte work queue is a static
+ * device array of the library, shared by every call on a device. Small arrays marked "host" are read during
  * the call only. `stream` is a hipStream_t (NULL = the default stream); every
  * call only enqueues work on it and never synchronises, so results are
  * visible in stream order. Inputs are read-only; outputs must not overlap
@@ -283,6 +285,24 @@ int veda_sparse_attn_fwd_raster_io(const veda_geom* g, const void* q_raster, ved
                                    const int32_t* k_per_head, int32_t k_max, float softmax_scale,
                                    void* o_raster, veda_raster_strides so, float* lse,
                                    int32_t* work_queue, void* stream);
+
+/*
+ * Allocation-free form of veda_sparse_attn_fwd_raster_io, for callers that cannot allocate device
+ * memory or bring a workspace (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). Arguments and outputs are those of veda_sparse_attn_fwd_raster_io with a work
+ * queue, minus work_queue: the queue lives in a static 64-byte device array of the library (one per
+ * device, held until the process ends), whose address is looked up once per device. The call itself
+ * allocates nothing; it clears the queue with a kernel on `stream` before each launch (as with a
+ * caller's workspace), so the outputs are the bytes veda_sparse_attn_fwd_raster_io gives.
+ * Limit: B * heads * nT_max <= 2^28 work items (else VEDA_ERR_SHAPE), as for a workspace.
+ * Every call on one device shares that device's array: calls that may overlap in time on one device
+ * (other streams, other threads) race on it; give those veda_sparse_attn_fwd_raster_io with
+ * workspaces of their own. A failed symbol lookup returns VEDA_ERR_DEVICE.
+ */
+int veda_sparse_attn_fwd_raster_io_noalloc(const veda_geom* g, const void* q_raster, veda_raster_strides sq,
+                                           const void* k_tiled, const void* v_tiled, const int32_t* idx,
+                                           const int32_t* k_per_head, int32_t k_max, float softmax_scale,
+                                           void* o_raster, veda_raster_strides so, float* lse, void* stream);
 
 /*
  * Inverse re-tiling: raster x[b, n, hd, :] = tiled x at the slot of token n
