@@ -201,6 +201,20 @@ def tile_scores(feat_q: np.ndarray, feat_k: np.ndarray) -> np.ndarray:
     return fp32_dot_rows(feat_q, np.ascontiguousarray(np.asarray(feat_k, np.float32).T))
 
 
+def avgpool_scores(stats_q: np.ndarray, stats_k: np.ndarray) -> np.ndarray:
+    """Average-pooling tile scores, the baseline the pages set Veda's mask
+    against at the same budget ([Veda] "Empirical Study", 02 "Controlled Mask
+    Intervention"): S[i, j] = <mean of query tile i, mean of key tile j> over
+    all d channels, i.e. the avg block of the TripPool statistics alone, with
+    no projection. Reading: the same float32 evaluation order as the
+    estimator's scores (ascending channel, from +0), so that its Top-k mask is
+    reproducible bit for bit."""
+    d = np.asarray(stats_q).shape[1] // 3
+    mq = np.asarray(stats_q, np.float32)[:, :d]
+    mk = np.asarray(stats_k, np.float32)[:, :d]
+    return fp32_dot_rows(mq, np.ascontiguousarray(mk.T))
+
+
 # --------------------------------------------------------------------------
 # O5: head-aware Top-k ([Veda] "Attention Structure Distillation", Execution:
 # Top-k selection per query tile gives the tile mask)

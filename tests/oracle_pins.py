@@ -206,6 +206,46 @@ def check_average_pooling_special_case(O, seed=3):
     assert np.all(np.abs(S - want) <= tol)
 
 
+def check_avgpool_scores(O, seed=14):
+    """Average-pooling scores three ways. (1) Small-integer tokens in full
+    boxes of 16 make every tile mean exact in bf16 and every score exact in
+    float32, so the scores equal the dot products of tile means gathered by
+    brute force from raster coordinates (all d channels; query means on the
+    left, key means on the right, so a transposed or max-pooled score fails).
+    (2) On a ragged grid with general bf16 values they equal the estimator
+    with rank d and W = [I; 0; 0], bit for bit (same evaluation order).
+    (3) They stay within the float32 accumulation bound of the exact dot
+    product of the bf16 means."""
+    rng = np.random.default_rng(seed)
+    grid, tile, d = (2, 4, 8), (1, 2, 8), 8                 # 64 tokens, 4 full boxes of 16
+    N = 64
+    q = rng.integers(-8, 9, size=(N, d)).astype(np.float32)
+    k = rng.integers(-8, 9, size=(N, d)).astype(np.float32)
+    qt, valid = O.tile_permute(q, grid, tile)
+    kt, _ = O.tile_permute(k, grid, tile)
+    S = O.avgpool_scores(O.trippool(qt, valid, 16), O.trippool(kt, valid, 16))
+    pos, _ = brute_force_positions(grid, tile)
+    tile_of = pos // 16
+    mq = np.stack([q[tile_of == j].astype(np.float64).mean(axis=0) for j in range(4)])
+    mk = np.stack([k[tile_of == j].astype(np.float64).mean(axis=0) for j in range(4)])
+    assert np.array_equal(S.astype(np.float64), mq @ mk.T)
+    assert not np.array_equal(mq @ mk.T, (mq @ mk.T).T)            # the check sees a transposition
+    grid, tile, d = (3, 5, 6), (2, 2, 4), 8                 # ragged: 2 x 3 x 2 boxes of 16
+    q = _bf16_vals(rng, (90, d))
+    k = _bf16_vals(rng, (90, d))
+    qt, valid = O.tile_permute(q, grid, tile)
+    kt, _ = O.tile_permute(k, grid, tile)
+    sq, sk = O.trippool(qt, valid, 16), O.trippool(kt, valid, 16)
+    W = np.zeros((3 * d, d), np.float32)
+    W[np.arange(d), np.arange(d)] = 1.0
+    S = O.avgpool_scores(sq, sk)
+    assert np.array_equal(S, O.tile_scores(O.project(sq, W), O.project(sk, W)))
+    a = sq[:, :d].astype(np.float64)
+    b = sk[:, :d].astype(np.float64)
+    gamma = d * 2.0 ** -24 / (1 - d * 2.0 ** -24)
+    assert np.all(np.abs(S - a @ b.T) <= gamma * (np.abs(a) @ np.abs(b).T) + 1e-30)
+
+
 # ------------------------------------------------------------------ O5
 
 def check_topk_golden(O):
@@ -583,6 +623,7 @@ ALL_SMALL_CHECKS = [
     check_dot_error_bound,
     check_projection_rounds_to_bf16,
     check_average_pooling_special_case,
+    check_avgpool_scores,
     check_topk_golden,
     check_topk_bruteforce,
     check_attention_two_keys,

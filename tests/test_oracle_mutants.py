@@ -87,6 +87,12 @@ MUTANTS = {
     "layer attends to K in place of V":
         ("o, lse = sparse_attention(q, k, v, grid, tile, idx, scale, query_tiles)",
          "o, lse = sparse_attention(q, k, k, grid, tile, idx, scale, query_tiles)"),
+    "average pooling scores the max block":
+        ("mq = np.asarray(stats_q, np.float32)[:, :d]", "mq = np.asarray(stats_q, np.float32)[:, d:2 * d]"),
+    "average pooling over half the channels":
+        ("mk = np.asarray(stats_k, np.float32)[:, :d]", "mk = np.asarray(stats_k, np.float32)[:, :d // 2]; mq = mq[:, :d // 2]"),
+    "average pooling scores transposed":
+        ("return fp32_dot_rows(mq, np.ascontiguousarray(mk.T))", "return fp32_dot_rows(mk, np.ascontiguousarray(mq.T))"),
     "mask overlap counts either mask":
         ("both = np.asarray(bitmask_a, dtype=np.uint32) & np.asarray(bitmask_b, dtype=np.uint32)",
          "both = np.asarray(bitmask_a, dtype=np.uint32) | np.asarray(bitmask_b, dtype=np.uint32)"),
