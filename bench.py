@@ -512,7 +512,7 @@ def distill_report(V, datagen, name="480p", steps=300, lr=3e-3):
     def recall(g, q_t, k_t, wq, wk, oracle_bm, ks):
         est = V.trippool_score(q_t, k_t, wq, wk, g)
         _, bm = V.topk_mask(est["scores"], g, ks)
-        return float(np.mean(V.tile_recall(V.mask_overlap(bm, oracle_bm, g), g, ks)))
+        return float(np.mean(V.tile_recall(bm, oracle_bm, g, ks).cpu().numpy()))
 
     w = datagen.WORKLOADS[name]
     ks = w.k_per_head()

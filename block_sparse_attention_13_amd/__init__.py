@@ -25,13 +25,15 @@ Measuring a mask against the method's own target:
   dense_index      index lists that keep every key tile (dense attention through sparse_attn_fwd)
   teacher_tile_max max-pooled dense attention per (query tile, key tile); topk_mask of it is the
                    oracle tile mask
+  avgpool_score    average-pooling tile scores (the pages' baseline mask at the same budget)
   mask_overlap     kept tiles two masks have in common, per (batch, head)
-  tile_recall      overlap / (k_hd * nT_hd)
+  tile_recall      those kept tiles over the oracle mask's k_hd * nT_hd, per (batch, head)
 
 Head-aware tile search:
   head_sq_error    per-head squared difference of two raster tensors
   candidate_tiles  tile shapes (power-of-two edges, product 128) that fit a grid
   tile_search      per head, the candidate tiling whose sparse output is closest to dense attention
+  k_from_keep      k per head from a keep fraction
 
 Distilling the estimator toward the teacher:
   distill_kl       KL(teacher row || softmax(scores)) per query tile, and d/d scores
@@ -56,9 +58,9 @@ __all__ = ["Geometry", "VedaError", "tile_permute", "tile_permute_stats", "tile_
            "trippool_project_score", "topk_mask", "sparse_attn_fwd_raster", "tile_stats",
            "sparse_attn_fwd_raster_io", "sparse_attn_fwd_raster_io_noalloc",
            "sparse_attn_fwd", "attn_queue", "layer_forward",
-           "dense_index", "teacher_tile_max", "mask_overlap", "tile_recall",
+           "dense_index", "teacher_tile_max", "avgpool_score", "mask_overlap", "tile_recall",
            "head_sq_error", "candidate_tiles", "tile_search", "distill_kl", "distill_grad", "adam_step",
-           "distill_train", "TILE_TOKENS", "TOKEN_MAJOR", "CHANNEL_MAJOR"]
+           "distill_train", "k_from_keep", "TILE_TOKENS", "TOKEN_MAJOR", "CHANNEL_MAJOR"]
 
 TILE_TOKENS = _lib.VEDA_TILE_TOKENS
 TOKEN_MAJOR = _lib.VEDA_TILED_TOKEN_MAJOR
@@ -260,6 +262,24 @@ def trippool_project_score(stats_q: torch.Tensor, stats_k: torch.Tensor, w_q: to
         geom.c, stats_q.data_ptr(), stats_k.data_ptr(), w_q.data_ptr(), w_k.data_ptr(), int(r),
         out["feat_q"].data_ptr(), out["feat_k"].data_ptr(), out["scores"].data_ptr(), _stream(stats_q)),
         "veda_trippool_project_score")
+    return out
+
+
+def avgpool_score(stats_q: torch.Tensor, stats_k: torch.Tensor, geom: Geometry,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Average-pooling tile scores [B, heads, nT_max, nT_max] fp32: the dot
+    product of the tile means (the avg block of the statistics) over all d
+    channels; -inf outside each head's block. topk_mask of it is the pages'
+    average-pooling baseline mask."""
+    nT = geom.max_tiles()
+    shp = (geom.B, geom.n_heads, nT, 3 * geom.head_dim)
+    _need(stats_q, torch.bfloat16, shp, "stats_q")
+    _need(stats_k, torch.bfloat16, shp, "stats_k")
+    if out is None:
+        out = torch.empty((geom.B, geom.n_heads, nT, nT), dtype=torch.float32, device=stats_q.device)
+    _need(out, torch.float32, (geom.B, geom.n_heads, nT, nT), "scores")
+    _lib.check(_lib.lib.veda_avgpool_score(geom.c, stats_q.data_ptr(), stats_k.data_ptr(), out.data_ptr(),
+                                           _stream(stats_q)), "veda_avgpool_score")
     return out
 
 
@@ -517,11 +537,28 @@ def mask_overlap(bitmask_a: torch.Tensor, bitmask_b: torch.Tensor, geom: Geometr
     return out
 
 
-def tile_recall(counts: torch.Tensor, geom: Geometry, k_per_head: Sequence[int]) -> List[List[float]]:
-    """Tile recall per (batch, head): common kept tiles / (k_hd * nT_hd)."""
-    c = counts.cpu().tolist()
-    return [[int(c[b][hd]) / (k_per_head[hd] * geom.num_tiles(hd)) for hd in range(geom.n_heads)]
-            for b in range(geom.B)]
+def tile_recall(bitmask: torch.Tensor, bitmask_oracle: torch.Tensor, geom: Geometry, k_per_head: Sequence[int],
+                out: Optional[torch.Tensor] = None, counts: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Tile recall per (batch, head), fp64 [B, heads] on the device: kept
+    tiles the mask shares with the oracle mask over the oracle mask's
+    k_hd * nT_hd (k_per_head is the oracle mask's k). `counts` (int64
+    [B, heads]), when given, receives the numerators."""
+    nT = geom.max_tiles()
+    shape = (geom.B, geom.n_heads, nT, (nT + 31) // 32)
+    _need(bitmask, torch.uint32, shape, "bitmask")
+    _need(bitmask_oracle, torch.uint32, shape, "bitmask_oracle")
+    ks = list(k_per_head)
+    if len(ks) != geom.n_heads:
+        raise ValueError("need one k per head")
+    if out is None:
+        out = torch.empty((geom.B, geom.n_heads), dtype=torch.float64, device=bitmask.device)
+    _need(out, torch.float64, (geom.B, geom.n_heads), "recall")
+    if counts is not None:
+        _need(counts, torch.int64, (geom.B, geom.n_heads), "counts")
+    _lib.check(_lib.lib.veda_tile_recall(geom.c, bitmask.data_ptr(), bitmask_oracle.data_ptr(), _lib.int_array(ks),
+                                         counts.data_ptr() if counts is not None else None, out.data_ptr(),
+                                         _stream(bitmask)), "veda_tile_recall")
+    return out
 
 
 def head_sq_error(a: torch.Tensor, b: torch.Tensor, geom: Geometry,
@@ -541,22 +578,21 @@ def head_sq_error(a: torch.Tensor, b: torch.Tensor, geom: Geometry,
 def candidate_tiles(grid: Sequence[int]) -> List[Tuple[int, int, int]]:
     """Every (pt, ph, pw) of powers of two with pt * ph * pw = 128 whose edges
     do not exceed the grid's (T, H, W) and whose tile count stays within the
-    library's limit."""
-    T, H, W = grid
-    out = []
-    for a in range(8):
-        for b_ in range(8 - a):
-            pt, ph, pw = 1 << a, 1 << b_, 1 << (7 - a - b_)
-            if pt <= T and ph <= H and pw <= W:
-                n = -(-T // pt) * -(-H // ph) * -(-W // pw)
-                if n <= _lib.VEDA_MAX_TILES:
-                    out.append((pt, ph, pw))
-    return out
+    library's limit (veda_candidate_tiles)."""
+    out = (_lib.VedaTile * 36)()
+    n = _lib.check(_lib.lib.veda_candidate_tiles(_lib.VedaGrid(*map(int, grid)), out, 36), "veda_candidate_tiles")
+    return [(out[i].pt, out[i].ph, out[i].pw) for i in range(n)]
 
 
-def _k_of(keep, n: int) -> int:
+def _k_of(keep, geom: Geometry, head: int) -> int:
+    """k_hd = ceil(keep * nT_hd) (veda_k_from_keep, exact in integers)."""
     f = keep if isinstance(keep, fractions.Fraction) else fractions.Fraction(str(keep))
-    return max(1, min(n, math.ceil(f * n)))
+    return _lib.check(_lib.lib.veda_k_from_keep(geom.c, int(head), f.numerator, f.denominator), "veda_k_from_keep")
+
+
+def k_from_keep(geom: Geometry, keep) -> List[int]:
+    """k per head for a keep fraction (e.g. 0.05 for 95% sparsity)."""
+    return [_k_of(keep, geom, hd) for hd in range(geom.n_heads)]
 
 
 def tile_search(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
@@ -581,15 +617,17 @@ def tile_search(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.Te
     idx, ks_all = dense_index(g0, q.device)
     o_dense, _ = sparse_attn_fwd_raster(q_t, k_t, v_t, idx, g0, ks_all, scale, with_lse=False)
     del q_t, k_t, v_t, idx
-    errs = []
-    for tile in cands:
+    err = torch.empty((len(cands), B, Hh), dtype=torch.float64, device=q.device)
+    for ci, tile in enumerate(cands):
         g = Geometry(B, Hh, d, tuple(grid), [tuple(tile)] * Hh)
-        ks = [_k_of(keep, g.num_tiles(hd)) for hd in range(Hh)]
+        ks = k_from_keep(g, keep)
         o = layer_forward(q, k, v, w_q, w_k, g, ks, scale)["o"]
-        errs.append(head_sq_error(o, o_dense, g).cpu())
-    err = torch.stack(errs).numpy()
-    best_i = err.sum(axis=1).argmin(axis=0)
-    return {"candidates": cands, "err": err, "best": [tuple(cands[i]) for i in best_i], "o_dense": o_dense}
+        head_sq_error(o, o_dense, g, out=err[ci])
+    best = torch.empty((Hh,), dtype=torch.int32, device=q.device)
+    _lib.check(_lib.lib.veda_tile_search_select(len(cands), B, Hh, err.data_ptr(), None, best.data_ptr(),
+                                                _stream(q)), "veda_tile_search_select")
+    return {"candidates": cands, "err": err.cpu().numpy(), "best": [tuple(cands[i]) for i in best.cpu().tolist()],
+            "o_dense": o_dense}
 
 
 def distill_kl(scores: torch.Tensor, teacher: torch.Tensor, geom: Geometry, grad_scale: float = 1.0,
@@ -667,7 +705,7 @@ def distill_train(q_t: torch.Tensor, k_t: torch.Tensor, teacher: torch.Tensor, w
     wq_b, wk_b = w_q.clone(), w_k.clone()
     mq, vq, mk, vk = (torch.zeros_like(wq_m) for _ in range(4))
     rows = sum(geom.num_tiles(hd) for hd in range(geom.n_heads)) * geom.B
-    losses = []
+    losses = torch.empty((steps,), dtype=torch.float64, device=q_t.device)
     est = trippool_score(q_t, k_t, wq_b, wk_b, geom)   # the statistics do not depend on W: taken once
     grads, kl, ds = None, None, None
     for step in range(1, steps + 1):
@@ -678,6 +716,6 @@ def distill_train(q_t: torch.Tensor, k_t: torch.Tensor, teacher: torch.Tensor, w
         grads = distill_grad(est, ds, geom, grads)
         adam_step(wq_m, grads["d_w_q"], mq, vq, step, lr, betas, eps, wq_b)
         adam_step(wk_m, grads["d_w_k"], mk, vk, step, lr, betas, eps, wk_b)
-        losses.append(kl)
-        kl = None
-    return {"w_q": wq_b, "w_k": wk_b, "loss": [float(x.cpu().numpy().astype("float64").sum()) / rows for x in losses]}
+        _lib.check(_lib.lib.veda_distill_mean_kl(geom.c, kl.data_ptr(), losses[step - 1:step].data_ptr(),
+                                                 _stream(kl)), "veda_distill_mean_kl")
+    return {"w_q": wq_b, "w_k": wk_b, "loss": losses.cpu().tolist()}

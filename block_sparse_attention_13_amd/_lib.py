@@ -27,7 +27,9 @@ EXPORTS = ["veda_status_str", "veda_num_tiles", "veda_max_tiles", "veda_tile_per
            "veda_topk_mask", "veda_sparse_attn_fwd", "veda_tile_unpermute", "veda_teacher_tile_max",
            "veda_mask_overlap", "veda_head_sq_error", "veda_distill_kl", "veda_distill_grad",
            "veda_adam_step", "veda_tile_permute_stats", "veda_trippool_project_score",
-           "veda_sparse_attn_fwd_raster", "veda_sparse_attn_fwd_raster_io", "veda_sparse_attn_fwd_raster_io_noalloc"]
+           "veda_sparse_attn_fwd_raster", "veda_sparse_attn_fwd_raster_io", "veda_sparse_attn_fwd_raster_io_noalloc",
+           "veda_avgpool_score", "veda_tile_recall", "veda_tile_search_select", "veda_k_from_keep",
+           "veda_distill_mean_kl", "veda_candidate_tiles"]
 
 
 class VedaGrid(ctypes.Structure):
@@ -76,6 +78,8 @@ def _load():
     lib.veda_trippool_score.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.veda_trippool_score.restype = ctypes.c_int
+    lib.veda_avgpool_score.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.veda_avgpool_score.restype = ctypes.c_int
     lib.veda_topk_mask.argtypes = [POINTER(VedaGeom), c_void_p, POINTER(c_int32), c_int32, c_void_p, c_void_p,
                                    c_void_p]
     lib.veda_topk_mask.restype = ctypes.c_int
@@ -100,6 +104,17 @@ def _load():
     lib.veda_teacher_tile_max.restype = ctypes.c_int
     lib.veda_mask_overlap.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_void_p]
     lib.veda_mask_overlap.restype = ctypes.c_int
+    lib.veda_tile_recall.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, POINTER(c_int32), c_void_p, c_void_p,
+                                     c_void_p]
+    lib.veda_tile_recall.restype = ctypes.c_int
+    lib.veda_tile_search_select.argtypes = [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.veda_tile_search_select.restype = ctypes.c_int
+    lib.veda_candidate_tiles.argtypes = [VedaGrid, POINTER(VedaTile), c_int32]
+    lib.veda_candidate_tiles.restype = ctypes.c_int
+    lib.veda_k_from_keep.argtypes = [POINTER(VedaGeom), c_int32, c_int64, c_int64]
+    lib.veda_k_from_keep.restype = ctypes.c_int
+    lib.veda_distill_mean_kl.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p]
+    lib.veda_distill_mean_kl.restype = ctypes.c_int
     lib.veda_head_sq_error.argtypes = [POINTER(VedaGeom), c_void_p, VedaRasterStrides, c_void_p, VedaRasterStrides,
                                        c_void_p, c_void_p]
     lib.veda_head_sq_error.restype = ctypes.c_int

@@ -53,7 +53,65 @@ __global__ __launch_bounds__(kSqThreads) void head_sq_error_kernel(GeoTable g, c
   if (threadIdx.x == 0) err[int64_t(bb) * g.heads + hd] = part[0];
 }
 
+// Head-aware tile search, the choice (Veda page, "Head-Aware Tile Search"):
+// per head, the candidate whose squared error summed over the batch (fp64,
+// ascending batch index) is smallest; equal sums keep the lower candidate,
+// and a NaN sum is never taken over a number. One thread per head.
+__global__ void search_select_kernel(int32_t n_cand, int32_t B, int32_t heads, const double* __restrict__ err,
+                                     double* __restrict__ err_sum, int32_t* __restrict__ best) {
+  const int hd = blockIdx.x * blockDim.x + threadIdx.x;
+  if (hd >= heads) return;
+  int32_t pick = 0;
+  double pick_s = __builtin_nan("");
+  for (int32_t c = 0; c < n_cand; ++c) {
+    double s = 0.0;
+    for (int32_t b = 0; b < B; ++b) s += err[(int64_t(c) * B + b) * heads + hd];
+    if (err_sum) err_sum[int64_t(c) * heads + hd] = s;
+    if (s < pick_s || (pick_s != pick_s && s == s)) {
+      pick = c;
+      pick_s = s;
+    }
+  }
+  best[hd] = pick;
+}
+
+// Mean of the per-query-tile KL over the rows that exist (b, hd, tq < nT_hd):
+// one workgroup, fp64 per thread over a fixed stride, then a fixed tree
+// order, so the value is reproducible.
+constexpr int kMeanThreads = 1024;
+__global__ __launch_bounds__(kMeanThreads) void distill_mean_kernel(GeoTable g, const float* __restrict__ kl_rows,
+                                                                   double* __restrict__ mean) {
+  double acc = 0.0;
+  int64_t rows = 0;
+  for (int b = 0; b < g.B; ++b)
+    for (int hd = 0; hd < g.heads; ++hd) {
+      const int32_t nT = g.h[hd].nT;
+      const float* r = kl_rows + (int64_t(b) * g.heads + hd) * g.nT_max;
+      for (int32_t t = threadIdx.x; t < nT; t += kMeanThreads) acc += double(r[t]);
+      rows += nT;
+    }
+  __shared__ double part[kMeanThreads];
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = kMeanThreads / 2; s > 0; s >>= 1) {
+    if (int(threadIdx.x) < s) part[threadIdx.x] += part[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *mean = part[0] / double(rows);
+}
+
 }  // namespace
+
+hipError_t launch_search_select(int32_t n_cand, int32_t B, int32_t heads, const double* err, double* err_sum,
+                                int32_t* best, hipStream_t s) {
+  search_select_kernel<<<(heads + 63) / 64, 64, 0, s>>>(n_cand, B, heads, err, err_sum, best);
+  return hipGetLastError();
+}
+
+hipError_t launch_distill_mean(const GeoTable& g, const float* kl_rows, double* mean, hipStream_t s) {
+  distill_mean_kernel<<<1, kMeanThreads, 0, s>>>(g, kl_rows, mean);
+  return hipGetLastError();
+}
 
 hipError_t launch_head_sq_error(const GeoTable& g, const uint16_t* a, int64_t sab, int64_t san, int64_t sah,
                                 const uint16_t* b, int64_t sbb, int64_t sbn, int64_t sbh, double* err,

@@ -185,9 +185,12 @@ __global__ __launch_bounds__(kThreads, 2) void teacher_kernel(GeoTable g, const 
 
 // Common set bits of two tile masks, per (batch, head): the sum over the
 // head's query tiles of popcount(a & b) over their words.
+// Kept tiles two masks share per (batch, head), and optionally the tile
+// recall: that count over the oracle mask's k_hd * nT_hd kept tiles.
 __global__ __launch_bounds__(256) void mask_overlap_kernel(GeoTable g, const uint32_t* __restrict__ a,
                                                            const uint32_t* __restrict__ bmask,
-                                                           unsigned long long* __restrict__ counts) {
+                                                           unsigned long long* __restrict__ counts,
+                                                           double* __restrict__ recall) {
   const int hd = blockIdx.x, b = blockIdx.y;
   const int32_t nT = g.h[hd].nT;
   const int words = (g.nT_max + 31) / 32;
@@ -201,7 +204,10 @@ __global__ __launch_bounds__(256) void mask_overlap_kernel(GeoTable g, const uin
     if (int(threadIdx.x) < s) part[threadIdx.x] += part[threadIdx.x + s];
     __syncthreads();
   }
-  if (threadIdx.x == 0) counts[int64_t(b) * g.heads + hd] = part[0];
+  if (threadIdx.x == 0) {
+    if (counts) counts[int64_t(b) * g.heads + hd] = part[0];
+    if (recall) recall[int64_t(b) * g.heads + hd] = double(part[0]) / (double(g.h[hd].k) * double(nT));
+  }
 }
 
 }  // namespace
@@ -221,8 +227,8 @@ hipError_t launch_teacher(const GeoTable& g, const uint16_t* q_t, const uint16_t
 }
 
 hipError_t launch_mask_overlap(const GeoTable& g, const uint32_t* a, const uint32_t* b, unsigned long long* counts,
-                               hipStream_t s) {
-  mask_overlap_kernel<<<dim3(g.heads, g.B), 256, 0, s>>>(g, a, b, counts);
+                               double* recall, hipStream_t s) {
+  mask_overlap_kernel<<<dim3(g.heads, g.B), 256, 0, s>>>(g, a, b, counts, recall);
   return hipGetLastError();
 }
 

@@ -211,9 +211,13 @@ __global__ __launch_bounds__(kThreads) void trippool_project_kernel(
 constexpr int kScoreTile = 128;   // scores per workgroup: 128 x 128, 8 x 8 per thread
 constexpr int kScorePad = 4;      // LDS row padding (floats): spreads the transposing stores over banks
 
+// S[i, j] = sum over c < R of feat_q[i, c] * feat_k[j, c], fp32 FMA in
+// ascending c from +0. Rows are `ld` elements apart: ld = R for the
+// estimator's features; ld = 3d with R = d reads the avg block of the
+// TripPool statistics, which gives the average-pooling scores.
 template <int R>
 __global__ __launch_bounds__(kThreads) void tile_scores_kernel(GeoTable g, const uint16_t* __restrict__ feat_q,
-                                                              const uint16_t* __restrict__ feat_k,
+                                                              const uint16_t* __restrict__ feat_k, int32_t ld,
                                                               float* __restrict__ scores) {
   __shared__ __attribute__((aligned(16))) float fq_s[R][kScoreTile + kScorePad];  // transposed: [channel][row]
   __shared__ __attribute__((aligned(16))) float fk_s[R][kScoreTile + kScorePad];
@@ -229,8 +233,8 @@ __global__ __launch_bounds__(kThreads) void tile_scores_kernel(GeoTable g, const
     const int r = e / (R / 8), c0 = (e % (R / 8)) * 8;
     const int i = i0 + r, j = j0 + r;
     const uint4 zero4 = make_uint4(0, 0, 0, 0);
-    const uint4 qa = i < hg.nT ? *reinterpret_cast<const uint4*>(feat_q + (head_row + i) * R + c0) : zero4;
-    const uint4 ka = j < hg.nT ? *reinterpret_cast<const uint4*>(feat_k + (head_row + j) * R + c0) : zero4;
+    const uint4 qa = i < hg.nT ? *reinterpret_cast<const uint4*>(feat_q + (head_row + i) * ld + c0) : zero4;
+    const uint4 ka = j < hg.nT ? *reinterpret_cast<const uint4*>(feat_k + (head_row + j) * ld + c0) : zero4;
     const uint32_t qw[4] = {qa.x, qa.y, qa.z, qa.w}, kw[4] = {ka.x, ka.y, ka.z, ka.w};
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -320,9 +324,20 @@ hipError_t launch_tile_scores(const GeoTable& g, const uint16_t* feat_q, const u
   const int nb = (g.nT_max + kScoreTile - 1) / kScoreTile;
   const dim3 grid(nb * nb, g.heads, g.B);
   if (r == 64)
-    tile_scores_kernel<64><<<grid, kThreads, 0, s>>>(g, feat_q, feat_k, scores);
+    tile_scores_kernel<64><<<grid, kThreads, 0, s>>>(g, feat_q, feat_k, 64, scores);
   else
-    tile_scores_kernel<32><<<grid, kThreads, 0, s>>>(g, feat_q, feat_k, scores);
+    tile_scores_kernel<32><<<grid, kThreads, 0, s>>>(g, feat_q, feat_k, 32, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_avgpool_scores(const GeoTable& g, const uint16_t* stats_q, const uint16_t* stats_k, float* scores,
+                                 hipStream_t s) {
+  const int nb = (g.nT_max + kScoreTile - 1) / kScoreTile;
+  const dim3 grid(nb * nb, g.heads, g.B);
+  if (g.d == 128)
+    tile_scores_kernel<128><<<grid, kThreads, 0, s>>>(g, stats_q, stats_k, 3 * 128, scores);
+  else
+    tile_scores_kernel<64><<<grid, kThreads, 0, s>>>(g, stats_q, stats_k, 3 * 64, scores);
   return hipGetLastError();
 }
 

@@ -227,6 +227,18 @@ int veda_trippool_project_score(const veda_geom* g, const void* stats_q, const v
                                            static_cast<const uint16_t*>(feat_k), rank, scores, st));
 }
 
+int veda_avgpool_score(const veda_geom* g, const void* stats_q, const void* stats_k, float* scores, void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!stats_q || !stats_k || !scores) return VEDA_ERR_NULL;
+  for (const void* p : {stats_q, stats_k, static_cast<const void*>(scores)})
+    if (!aligned16(p)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_device());
+  return launched(veda::launch_avgpool_scores(t, static_cast<const uint16_t*>(stats_q),
+                                              static_cast<const uint16_t*>(stats_k), scores,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int veda_topk_mask(const veda_geom* g, const float* scores, const int32_t* k_per_head, int32_t k_max,
                    int32_t* idx, uint32_t* bitmask, void* stream) {
   GeoTable t;
@@ -353,7 +365,61 @@ int veda_mask_overlap(const veda_geom* g, const uint32_t* bitmask_a, const uint3
     if (!aligned16(p)) return VEDA_ERR_ALIGN;
   VEDA_TRY(check_device());
   return launched(veda::launch_mask_overlap(t, bitmask_a, bitmask_b, reinterpret_cast<unsigned long long*>(counts),
-                                            static_cast<hipStream_t>(stream)));
+                                            nullptr, static_cast<hipStream_t>(stream)));
+}
+
+int veda_tile_recall(const veda_geom* g, const uint32_t* bitmask, const uint32_t* bitmask_oracle,
+                     const int32_t* k_per_head, uint64_t* counts, double* recall, void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!bitmask || !bitmask_oracle || !k_per_head || !recall) return VEDA_ERR_NULL;
+  int32_t k_max = 0;
+  for (int hd = 0; hd < t.heads; ++hd) k_max = k_per_head[hd] > k_max ? k_per_head[hd] : k_max;
+  VEDA_TRY(set_k(k_per_head, k_max, &t));
+  for (const void* p : {static_cast<const void*>(bitmask), static_cast<const void*>(bitmask_oracle),
+                        static_cast<const void*>(recall)})
+    if (!aligned16(p)) return VEDA_ERR_ALIGN;
+  if (counts && !aligned16(counts)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_device());
+  return launched(veda::launch_mask_overlap(t, bitmask, bitmask_oracle, reinterpret_cast<unsigned long long*>(counts),
+                                            recall, static_cast<hipStream_t>(stream)));
+}
+
+int veda_tile_search_select(int32_t n_candidates, int32_t B, int32_t heads, const double* err, double* err_sum,
+                            int32_t* best, void* stream) {
+  if (!err || !best) return VEDA_ERR_NULL;
+  if (n_candidates <= 0 || B <= 0 || B > 65535 || heads <= 0 || heads > VEDA_MAX_HEADS) return VEDA_ERR_SHAPE;
+  if (!aligned16(err) || !aligned16(best) || (err_sum && !aligned16(err_sum))) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_device());
+  return launched(veda::launch_search_select(n_candidates, B, heads, err, err_sum, best,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int veda_candidate_tiles(veda_grid grid, veda_tile* tiles, int32_t capacity) {
+  if (!tiles) return VEDA_ERR_NULL;
+  if (grid.T <= 0 || grid.H <= 0 || grid.W <= 0 || capacity < 0) return VEDA_ERR_SHAPE;
+  int n = 0;
+  for (int a = 0; a < 8; ++a)
+    for (int b = 0; a + b < 8; ++b) {
+      const int32_t pt = 1 << a, ph = 1 << b, pw = 1 << (7 - a - b);
+      if (pt > grid.T || ph > grid.H || pw > grid.W) continue;
+      const int64_t nT = ((int64_t(grid.T) + pt - 1) / pt) * ((int64_t(grid.H) + ph - 1) / ph) *
+                         ((int64_t(grid.W) + pw - 1) / pw);
+      if (nT > VEDA_MAX_TILES) continue;
+      if (n >= capacity) return VEDA_ERR_SHAPE;
+      tiles[n++] = veda_tile{pt, ph, pw};
+    }
+  return n;
+}
+
+int veda_k_from_keep(const veda_geom* g, int32_t head, int64_t keep_num, int64_t keep_den) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (head < 0 || head >= t.heads) return VEDA_ERR_SHAPE;
+  if (keep_den <= 0 || keep_num <= 0 || keep_num > keep_den) return VEDA_ERR_K;
+  const __int128 n = t.h[head].nT;
+  const __int128 k = (__int128(keep_num) * n + keep_den - 1) / keep_den;   // ceil(keep * nT_hd)
+  return int(k < 1 ? 1 : (k > n ? n : k));
 }
 
 int veda_head_sq_error(const veda_geom* g, const void* a_raster, veda_raster_strides sa, const void* b_raster,
@@ -382,6 +448,15 @@ int veda_distill_kl(const veda_geom* g, const float* scores, const float* teache
   VEDA_TRY(check_device());
   return launched(veda::launch_distill_kl(t, scores, teacher, grad_scale, kl_rows, d_scores,
                                           static_cast<hipStream_t>(stream)));
+}
+
+int veda_distill_mean_kl(const veda_geom* g, const float* kl_rows, double* mean, void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!kl_rows || !mean) return VEDA_ERR_NULL;
+  if (!aligned16(kl_rows) || (reinterpret_cast<uintptr_t>(mean) & 7u)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_device());
+  return launched(veda::launch_distill_mean(t, kl_rows, mean, static_cast<hipStream_t>(stream)));
 }
 
 int veda_distill_grad(const veda_geom* g, int32_t rank, const void* stats_q, const void* stats_k, const void* feat_q,

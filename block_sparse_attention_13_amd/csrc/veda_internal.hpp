@@ -130,12 +130,17 @@ hipError_t launch_trippool_project(const GeoTable& g, const uint16_t* stats_q, c
                                    uint16_t* feat_k, hipStream_t s);
 hipError_t launch_tile_scores(const GeoTable& g, const uint16_t* feat_q, const uint16_t* feat_k, int32_t r,
                               float* scores, hipStream_t s);
+hipError_t launch_avgpool_scores(const GeoTable& g, const uint16_t* stats_q, const uint16_t* stats_k, float* scores,
+                                 hipStream_t s);
 hipError_t launch_topk(const GeoTable& g, const float* scores, int32_t k_max, int32_t* idx, uint32_t* bitmask,
                        hipStream_t s);
 hipError_t launch_teacher(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t, const float* lse, float scale,
                           float* teacher, int32_t* queue, hipStream_t s);
 hipError_t launch_mask_overlap(const GeoTable& g, const uint32_t* a, const uint32_t* b, unsigned long long* counts,
-                               hipStream_t s);
+                               double* recall, hipStream_t s);
+hipError_t launch_search_select(int32_t n_cand, int32_t B, int32_t heads, const double* err, double* err_sum,
+                                int32_t* best, hipStream_t s);
+hipError_t launch_distill_mean(const GeoTable& g, const float* kl_rows, double* mean, hipStream_t s);
 hipError_t launch_head_sq_error(const GeoTable& g, const uint16_t* a, int64_t sab, int64_t san, int64_t sah,
                                 const uint16_t* b, int64_t sbb, int64_t sbn, int64_t sbh, double* err,
                                 hipStream_t s);

@@ -19,14 +19,20 @@
  * and with Q never tiled: veda_tile_permute_stats of Q with no tiled output (statistics
  * only), then veda_sparse_attn_fwd_raster_io, which also reads Q in raster order.
  *
- * Two more calls measure the mask against the method's own target:
+ * More calls measure the mask against the method's own target:
  *   veda_teacher_tile_max      max-pooled dense attention per (query tile, key tile); its
  *                              veda_topk_mask is the oracle tile mask
- *   veda_mask_overlap          common kept tiles of two masks (tile recall)
+ *   veda_avgpool_score         average-pooling tile scores, the pages' baseline mask
+ *   veda_mask_overlap          common kept tiles of two masks
+ *   veda_tile_recall           tile recall of a mask against the oracle mask
  *   veda_head_sq_error         squared output error per head (objective of the head-aware tile search)
+ *   veda_candidate_tiles       the tile shapes the search tries (host only)
+ *   veda_tile_search_select    per head, the candidate tiling with the smallest error
+ *   veda_k_from_keep           k_hd from a keep fraction (host only)
  *
  * Distilling the estimator's projections toward the teacher:
  *   veda_distill_kl            KL(teacher row || softmax(scores)) per query tile and its gradient
+ *   veda_distill_mean_kl       the mean KL over the query tiles (the reported loss)
  *   veda_distill_grad          that gradient back to W_q and W_k
  *   veda_adam_step             one Adam update of fp32 master weights (+ their bf16 copy)
  *
@@ -204,6 +210,20 @@ int veda_trippool_project_score(const veda_geom* g, const void* stats_q, const v
                                 void* feat_q, void* feat_k, float* scores, void* stream);
 
 /*
+ * Average-pooling tile scores, the baseline mask the pages compare Veda's against at the same budget
+ * (Veda page, "Empirical Study", 02 "Controlled Mask Intervention"): the dot product of the tile
+ * means alone, over all d channels, with no projection. veda_topk_mask of these scores gives the
+ * average-pooling mask; veda_mask_overlap against the teacher's oracle mask gives its tile recall.
+ *   stats_q, stats_k  in   bf16 [B, heads, nT_max, 3d] (veda_tile_permute_stats or
+ *                          veda_trippool_score); only the avg block (channels 0..d-1) is read
+ *   scores            out  fp32 [B, heads, nT_max, nT_max]: sum over c < d of avg_q[i, c] * avg_k[j, c],
+ *                          fp32 accumulated in ascending c from +0; -inf outside the head's block
+ * Errors: null or unaligned pointers, and the geometry checks of every call.
+ */
+int veda_avgpool_score(const veda_geom* g, const void* stats_q, const void* stats_k, float* scores,
+                       void* stream);
+
+/*
  * Head-aware Top-k tile mask (Veda page, "Attention Structure Distillation",
  * Execution: Top-k per query tile gives the binary tile mask). For every
  * (b, hd, query tile) the k_hd largest scores among key tiles 0..nT_hd-1;
@@ -341,6 +361,18 @@ int veda_mask_overlap(const veda_geom* g, const uint32_t* bitmask_a, const uint3
                       void* stream);
 
 /*
+ * Tile recall of a mask against the oracle mask (Veda page, "Empirical Study", 02 "Controlled Mask
+ * Intervention": the share of the oracle mask's kept tiles that a mask also keeps):
+ *   recall[b, hd] = (sum over the head's query tiles of popcount(mask & oracle)) / (k_hd * nT_hd)
+ *   bitmask, bitmask_oracle  in   uint32 [B, heads, nT_max, ceil(nT_max/32)] from veda_topk_mask
+ *   k_per_head               in   host int32 [heads]: the oracle mask's k_hd (1 <= k_hd <= nT_hd)
+ *   counts                   out  uint64 [B, heads], the numerators (as veda_mask_overlap); may be NULL
+ *   recall                   out  fp64 [B, heads]
+ */
+int veda_tile_recall(const veda_geom* g, const uint32_t* bitmask, const uint32_t* bitmask_oracle,
+                     const int32_t* k_per_head, uint64_t* counts, double* recall, void* stream);
+
+/*
  * Squared error per (batch, head) between two raster tensors (Veda page, "Head-Aware Tile Search":
  * each head takes the tiling that minimises ||O_full - O_sparse||_F^2 on calibration samples):
  *   err[b, hd] = sum over tokens n and channels c of (a[b, n, hd, c] - b[b, n, hd, c])^2,
@@ -350,6 +382,39 @@ int veda_mask_overlap(const veda_geom* g, const uint32_t* bitmask_a, const uint3
  */
 int veda_head_sq_error(const veda_geom* g, const void* a_raster, veda_raster_strides sa, const void* b_raster,
                        veda_raster_strides sb, double* err, void* stream);
+
+/*
+ * The head-aware tile search's choice (Veda page, "Head-Aware Tile Search": each head takes the
+ * candidate tiling that minimises ||O_full - O_sparse||_F^2 on calibration samples):
+ *   err_sum[c, hd] = sum over b (ascending) of err[c, b, hd] in fp64;
+ *   best[hd] = the c with the smallest err_sum[c, hd]; equal sums keep the lower c, and a NaN sum is
+ *              never taken over a number.
+ *   err      in   fp64 [n_candidates, B, heads] (veda_head_sq_error of each candidate's layer)
+ *   err_sum  out  fp64 [n_candidates, heads]; may be NULL
+ *   best     out  int32 [heads]
+ * Errors: n_candidates, B or heads <= 0, heads > VEDA_MAX_HEADS or B > 65535 (VEDA_ERR_SHAPE).
+ */
+int veda_tile_search_select(int32_t n_candidates, int32_t B, int32_t heads, const double* err, double* err_sum,
+                            int32_t* best, void* stream);
+
+/*
+ * Candidates of the head-aware tile search (host only; Veda page, "Head-Aware Tile Search": tile
+ * shapes whose three edges multiply to the 128-token budget): every (pt, ph, pw) of powers of two
+ * with pt*ph*pw = 128, each edge at most the grid's, and at most VEDA_MAX_TILES tiles, in order of
+ * increasing pt, then ph. There are at most 36.
+ *   tiles     out  host array of `capacity` entries
+ * Returns the number written, or VEDA_ERR_NULL, or VEDA_ERR_SHAPE (a grid edge <= 0, or more
+ * candidates than `capacity`).
+ */
+int veda_candidate_tiles(veda_grid grid, veda_tile* tiles, int32_t capacity);
+
+/*
+ * k from a keep fraction (host only, no device work; reading of "top-k = p% of key tiles"):
+ * k_hd = ceil(keep * nT_hd) with keep = keep_num / keep_den in (0, 1], exactly in integers,
+ * clamped to [1, nT_hd]. Returns k_hd, or VEDA_ERR_K for a fraction outside (0, 1] and the
+ * geometry errors of every call (VEDA_ERR_SHAPE for a head outside [0, heads)).
+ */
+int veda_k_from_keep(const veda_geom* g, int32_t head, int64_t keep_num, int64_t keep_den);
 
 /*
  * Distillation objective (Veda page, "Theoretical Rationale" 4, "Distillation Objective": the
@@ -366,6 +431,14 @@ int veda_head_sq_error(const veda_geom* g, const void* a_raster, veda_raster_str
  */
 int veda_distill_kl(const veda_geom* g, const float* scores, const float* teacher, float grad_scale, float* kl_rows,
                     float* d_scores, void* stream);
+
+/*
+ * The distillation loss as reported: the mean of kl_rows (veda_distill_kl) over the query tiles
+ * that exist, (b, hd, tq < nT_hd), summed in fp64 in a fixed order (reproducible).
+ *   kl_rows  in   fp32 [B, heads, nT_max]
+ *   mean     out  one fp64 value (8-byte aligned)
+ */
+int veda_distill_mean_kl(const veda_geom* g, const float* kl_rows, double* mean, void* stream);
 
 /*
  * Gradient of the distillation loss with respect to the head-specific projections, through

@@ -111,3 +111,26 @@ def test_distillation_lowers_the_loss():
     say(f"[distill] loss {r1['loss'][0]:.3f} -> {r1['loss'][-1]:.3f}")
     assert r1["loss"][-1] < 0.1 * r1["loss"][0]
     assert r1["loss"] == r2["loss"] and torch.equal(r1["w_q"].view(torch.int16), r2["w_q"].view(torch.int16))
+
+
+def test_distill_mean_kl_over_existing_rows():
+    """veda_distill_mean_kl: the mean of kl_rows over the query tiles that
+    exist (padded rows of shorter heads excluded), against numpy's fp64 mean
+    of the same rows; B = 2 and three tile shapes give rows of different
+    lengths. Rows past nT_hd are filled with garbage that must not count."""
+    from block_sparse_attention_13_amd import _lib
+    w = dataclasses.replace(W["hc"].with_heads(3), B=2)
+    g = geometry(w)
+    nT = g.max_tiles()
+    rng = np.random.default_rng(17)
+    rows = rng.uniform(0, 5, size=(w.B, w.heads, nT)).astype(np.float32)
+    want = np.mean(np.concatenate([rows[b, hd, :g.num_tiles(hd)].astype(np.float64)
+                                   for b in range(w.B) for hd in range(w.heads)]))
+    for hd in range(w.heads):
+        rows[:, hd, g.num_tiles(hd):] = 1e30
+    t = torch.from_numpy(rows).cuda()
+    mean = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
+    assert _lib.lib.veda_distill_mean_kl(g.c, t.data_ptr(), mean.data_ptr(), None) == 0
+    got = mean.item()
+    say(f"[distill] mean KL {got:.12f} vs {want:.12f}")
+    assert abs(got - want) <= 1e-12 * want

@@ -10,6 +10,7 @@ best candidates are within that tolerance of each other."""
 
 import dataclasses
 import fractions
+import math
 
 import numpy as np
 import pytest
@@ -41,7 +42,7 @@ def test_tile_search_matches_oracle(grid, keep):
     res = V.tile_search(q, k, v, wq, wk, grid, keep)
     cands = res["candidates"]
     assert cands == V.candidate_tiles(grid)
-    k_of = lambda n: V._k_of(keep, n)
+    k_of = lambda n: max(1, min(n, math.ceil(keep * n)))         # k_hd = ceil(keep * nT_hd), exact in Fraction
     for hd in range(w.heads):
         qh, kh, vh = (O.bf16_bits_to_float(data[n][0, :, hd, :]) for n in ("q", "k", "v"))
         wqh, wkh = (O.bf16_bits_to_float(data[n][hd]) for n in ("wq", "wk"))
@@ -54,6 +55,34 @@ def test_tile_search_matches_oracle(grid, keep):
         order = np.argsort(want)
         if res["best"][hd] != cands[order[0]]:
             assert want[order[1]] <= want[order[0]] * (1 + 2 * REL), (hd, res["best"][hd], cands[order[0]])
+        # the library's choice is the argmin of its own errors, lower candidate on ties
+        assert res["best"][hd] == cands[int(np.argmin(got))], (hd, res["best"][hd])
+
+
+def test_search_select_ties_and_nan():
+    """veda_tile_search_select on crafted errors: sums over the batch in fp64,
+    the smallest sum wins, equal sums keep the lower candidate, NaN sums lose
+    to numbers (and the first candidate stands when every sum is NaN)."""
+    from block_sparse_attention_13_amd import _lib
+    nan = float("nan")
+    # err[c, b, hd] for 4 candidates, 2 batch entries, 5 heads
+    err = np.array([[[3, 1, nan, 2, nan], [1, 1, 5, 2, nan]],
+                    [[2, 0.5, 1, 1, nan], [2, 1.5, 1, 3, nan]],
+                    [[1, 2, 9, 0, nan], [1, 0, 9, 0, nan]],
+                    [[0.5, 1, 2, 4, nan], [3.5, 1, 0, 0, nan]]], dtype=np.float64)
+    want_sum = err.sum(axis=1)
+    want_best = []
+    for hd in range(5):
+        col = want_sum[:, hd]
+        ok = np.flatnonzero(~np.isnan(col))
+        want_best.append(int(ok[np.argmin(col[ok])]) if len(ok) else 0)   # argmin takes the first minimum
+    t = torch.from_numpy(err).cuda()
+    best = torch.full((5,), -1, dtype=torch.int32, device="cuda")
+    sums = torch.empty((4, 5), dtype=torch.float64, device="cuda")
+    assert _lib.lib.veda_tile_search_select(4, 2, 5, t.data_ptr(), sums.data_ptr(), best.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    assert best.cpu().tolist() == want_best == [2, 0, 1, 2, 0]
+    assert np.array_equal(sums.cpu().numpy(), want_sum, equal_nan=True)
 
 
 def test_head_sq_error_strided():

@@ -56,6 +56,7 @@ def test_teacher_oracle_mask_and_recall(wname, heads, qtiles):
     T_fixed = V.teacher_tile_max(out["q_t"], out["k_t"], lse_d, geom, dynamic=False)
     o_idx, o_bm = V.topk_mask(T, geom, ks)
     counts = V.mask_overlap(out["bitmask"], o_bm, geom)
+    recall = V.tile_recall(out["bitmask"], o_bm, geom, ks).cpu().numpy()
     torch.cuda.synchronize()
     # the work queue (used from 1024 query tiles on) only changes which workgroup computes a row
     assert torch.equal(T.view(torch.int32), T_fixed.view(torch.int32))
@@ -94,9 +95,11 @@ def test_teacher_oracle_mask_and_recall(wname, heads, qtiles):
             for j in sel_g ^ sel_r:
                 assert abs(math.log(ref[j]) - math.log(kth)) <= 2 * LOG_TOL, ("mask not a near-tie", hd, t, j)
                 ties += 1
-        recall = int(counts_c[0, hd]) / (kk * nT)
+        # the library's recall is the oracle's recall of the GPU's own index lists, exactly
+        want_rec = O.tile_recall(out["idx"][0, hd].cpu().numpy()[:nT, :kk], gidx[:nT, :kk])
+        assert recall[0, hd] == want_rec, ("recall", hd, recall[0, hd], want_rec)
         say(f"[teacher] {w.name} head {hd}: log-error {worst:.2e}, near-tie swaps {ties}, "
-            f"TripPool tile recall {recall:.3f} (k/nT = {kk / nT:.3f})")
+            f"TripPool tile recall {recall[0, hd]:.3f} (k/nT = {kk / nT:.3f})")
 
 
 def test_mask_overlap_counts_random_bits():
@@ -117,3 +120,48 @@ def test_mask_overlap_counts_random_bits():
         for hd in range(w.heads):
             n = geom.num_tiles(hd)
             assert int(got[bb, hd]) == O.mask_overlap(a[bb, hd, :n], b[bb, hd, :n]), (bb, hd)
+
+
+@pytest.mark.parametrize("wname,heads,with_teacher", [("tiny", None, True), ("480p", 2, True), ("hc", 3, False),
+                                                      ("long", 2, False)])
+def test_avgpool_scores_mask_and_recall(wname, heads, with_teacher):
+    """Average-pooling baseline ("Empirical Study", 02): its scores and Top-k
+    mask bit for bit against the oracle (statistics recomputed by the oracle
+    from the host bytes), and its overlap with the teacher's oracle mask."""
+    V = _lib()
+    w = W[wname] if heads is None else W[wname].with_heads(heads)
+    say(f"[avgpool] workload {w.name} heads {w.heads}")
+    data = datagen.generate(w)
+    geom = geometry(w)
+    ks = w.k_per_head()
+    q, k, v = (to_dev_bf16(data[n]) for n in ("q", "k", "v"))
+    out = V.layer_forward(q, k, v, to_dev_bf16(data["wq"]), to_dev_bf16(data["wk"]), geom, ks, tiled_q=True)
+    S = V.avgpool_score(out["stats_q"], out["stats_k"], geom)
+    a_idx, a_bm = V.topk_mask(S, geom, ks)
+    if with_teacher:
+        idx_d, ks_d = V.dense_index(geom, q.device)
+        _, lse_d = V.sparse_attn_fwd(out["q_t"], out["k_t"], out["v_t"], idx_d, geom, ks_d)
+        T = V.teacher_tile_max(out["q_t"], out["k_t"], lse_d, geom)
+        _, o_bm = V.topk_mask(T, geom, ks)
+        counts = V.mask_overlap(a_bm, o_bm, geom).cpu().numpy().astype(np.uint64)
+        orc_bm = bits_of(o_bm)
+    torch.cuda.synchronize()
+    Sc = S.cpu().numpy()
+    aidx = a_idx.cpu().numpy()
+    abm = bits_of(a_bm)
+    for hd in range(w.heads):
+        nT, kk = geom.num_tiles(hd), ks[hd]
+        tile = w.head_tiles()[hd]
+        qh, kh_ = (O.bf16_bits_to_float(data[n][0, :, hd, :]) for n in ("q", "k"))
+        qt, valid = O.tile_permute(qh, w.grid, tile)
+        kt, _ = O.tile_permute(kh_, w.grid, tile)
+        want = O.avgpool_scores(O.trippool(qt, valid), O.trippool(kt, valid))
+        got = Sc[0, hd]
+        assert np.array_equal(got[:nT, :nT].view(np.uint32), want.view(np.uint32)), ("avgpool scores", hd)
+        assert np.all(np.isneginf(got[:nT, nT:])) and np.all(np.isneginf(got[nT:])), ("avgpool pad", hd)
+        assert np.array_equal(aidx[0, hd, :nT, :kk], O.topk(want, kk)), ("avgpool mask", hd)
+        msg = f"[avgpool] {w.name} head {hd}: scores and mask bit-exact"
+        if with_teacher:
+            assert int(counts[0, hd]) == O.mask_overlap(abm[0, hd, :nT], orc_bm[0, hd, :nT]), ("overlap", hd)
+            msg += f", tile recall {int(counts[0, hd]) / (kk * nT):.3f} (k/nT = {kk / nT:.3f})"
+        say(msg)
