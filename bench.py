@@ -354,7 +354,8 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0, grap
         del flush
     out["graph_ms_step"] = graph_timed(step, steps) if graph else None
     out.update({"data": data if keep_data else None, "valid_flops": valid_pair_flops(w, bufs["idx"].cpu().numpy()),
-                "bitmask": bufs["bitmask"] if keep_data else None})
+                "bitmask": bufs["bitmask"] if keep_data else None,
+                "stats": (bufs["stats_q"], bufs["stats_k"]) if keep_data else None})
     if keep_data:  # head 0 of batch 0, for the parity check against the oracle
         out["gpu_head0"] = {"idx": bufs["idx"][0, 0].cpu().numpy(), "o": bufs["o"][0, :, 0, :].float().cpu().numpy(),
                             "lse": bufs["lse"][0, 0].cpu().numpy()}
@@ -391,12 +392,14 @@ def graph_timed(step, steps: int):
     return round(ms, 4)
 
 
-def dense_reference(V, w, data, trip_bitmask=None, steps=2, warmup=1):
-    """Dense attention on the same inputs: every key tile kept (k = nT per
-    head) through the same tile-skipping kernel. Times the attention call
-    only, with HIP events on the launch stream. Then, from the dense LSE, the
+def dense_reference(V, w, data, trip_bitmask=None, stats=None, steps=2, warmup=1):
+    """Dense attention on the same inputs through the dedicated dense kernel
+    (every key tile kept, no index list). Times the attention call only,
+    with HIP events on the launch stream. Then, from the dense LSE, the
     teacher (max-pooled dense attention), the oracle tile mask (Top-k of the
-    teacher) and the tile recall of the layer's TripPool mask against it."""
+    teacher), and the tile recall against it of the layer's TripPool mask
+    and of the average-pooling mask (the pages' baseline at the same budget,
+    from the layer's statistics)."""
     import numpy as np
     import torch
     dev = torch.device("cuda:0")
@@ -407,25 +410,25 @@ def dense_reference(V, w, data, trip_bitmask=None, steps=2, warmup=1):
     q_t = V.tile_permute(to(data["q"]), geom)
     k_t = V.tile_permute(to(data["k"]), geom)
     v_t = V.tile_permute(to(data["v"]), geom, layout=V.CHANNEL_MAJOR)
-    idx = torch.arange(nT, dtype=torch.int32, device=dev).expand(w.B, w.heads, nT, nT).contiguous()
     o_t = torch.empty_like(q_t)
     lse = torch.empty((w.B, w.heads, nT, 128), dtype=torch.float32, device=dev)
     queue = V.attn_queue(dev)
     stream = torch.cuda.current_stream(dev)
     for _ in range(warmup):
-        V.sparse_attn_fwd(q_t, k_t, v_t, idx, geom, nts, o_t=o_t, lse=lse, work_queue=queue)
+        V.dense_attn_fwd(q_t, k_t, v_t, geom, o_t=o_t, lse=lse, work_queue=queue)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     ev[0].record(stream)
     for i in range(steps):
-        V.sparse_attn_fwd(q_t, k_t, v_t, idx, geom, nts, o_t=o_t, lse=lse, work_queue=queue)
+        V.dense_attn_fwd(q_t, k_t, v_t, geom, o_t=o_t, lse=lse, work_queue=queue)
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
     flops = 4.0 * w.d * 128 * 128 * sum(n * n for n in nts) * w.B
-    del idx, o_t, v_t
+    del o_t, v_t
     res = {"attn_ms": round(ms, 3), "attn_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
            "attn_frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "kernel": "dedicated dense forward (veda_dense_attn_fwd: every key tile in order, no index list)",
            "kept_tiles": "all", "steps": steps}
     if trip_bitmask is not None:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -434,20 +437,30 @@ def dense_reference(V, w, data, trip_bitmask=None, steps=2, warmup=1):
         e1.record(stream)
         ks = w.k_per_head()
         _, oracle_bm = V.topk_mask(teacher, geom, ks)
-        rec = V.tile_recall(V.mask_overlap(trip_bitmask, oracle_bm, geom), geom, ks)
+        del teacher
+        rec = V.tile_recall(trip_bitmask, oracle_bm, geom, ks).cpu().numpy()
+        avg_rec = None
+        if stats is not None:
+            avg_scores = V.avgpool_score(stats[0], stats[1], geom)
+            _, avg_bm = V.topk_mask(avg_scores, geom, ks)
+            del avg_scores
+            avg_rec = V.tile_recall(avg_bm, oracle_bm, geom, ks).cpu().numpy()
         torch.cuda.synchronize()
         t_ms = e0.elapsed_time(e1)
-        flat = [r for row in rec for r in row]
         res["teacher"] = {
             "ms": round(t_ms, 3),
             "tflops_qk": round(0.5 * flops / (t_ms * 1e-3) / 1e12, 1),
-            "trippool_tile_recall_mean": round(float(np.mean(flat)), 4),
-            "trippool_tile_recall_min": round(float(np.min(flat)), 4),
-            "trippool_tile_recall_max": round(float(np.max(flat)), 4),
+            "trippool_tile_recall_mean": round(float(rec.mean()), 4),
+            "trippool_tile_recall_min": round(float(rec.min()), 4),
+            "trippool_tile_recall_max": round(float(rec.max()), 4),
+            "avgpool_tile_recall_mean": round(float(avg_rec.mean()), 4) if avg_rec is not None else None,
+            "avgpool_tile_recall_min": round(float(avg_rec.min()), 4) if avg_rec is not None else None,
+            "avgpool_tile_recall_max": round(float(avg_rec.max()), 4) if avg_rec is not None else None,
             "chance_k_over_nT": round(float(np.mean([k / n for k, n in zip(ks, nts)])), 4),
-            "note": "random-init TripPool projections (no distillation): recall near chance is expected",
+            "note": "random-init TripPool projections (no distillation): recall near chance is expected; the "
+                    "average-pooling mask (mean-only scores, the pages' baseline) needs no weights",
         }
-        del teacher, oracle_bm
+        del oracle_bm
     del q_t, k_t, lse
     torch.cuda.empty_cache()
     return res
@@ -503,8 +516,7 @@ def distill_report(V, datagen, name="480p", steps=300, lr=3e-3):
         g = V.Geometry(w.B, w.heads, w.d, w.grid, w.head_tiles())
         q, k, v, wq, wk = (to(data[n]) for n in ("q", "k", "v", "wq", "wk"))
         out = V.layer_forward(q, k, v, wq, wk, g, w.k_per_head(), tiled_q=True)
-        idx_d, ks_d = V.dense_index(g, dev)
-        _, lse = V.sparse_attn_fwd(out["q_t"], out["k_t"], out["v_t"], idx_d, g, ks_d)
+        _, lse = V.dense_attn_fwd(out["q_t"], out["k_t"], out["v_t"], g)
         teacher = V.teacher_tile_max(out["q_t"], out["k_t"], lse, g)
         _, oracle_bm = V.topk_mask(teacher, g, w.k_per_head())
         return g, out["q_t"], out["k_t"], teacher, oracle_bm, wq, wk
@@ -642,8 +654,8 @@ def main():
 
     dense = None
     if not args.no_dense and not args.heads:
-        log("[bench] dense reference: every key tile kept, same kernel")
-        dense = dense_reference(V, w, data, trip_bitmask=r["bitmask"])
+        log("[bench] dense reference: every key tile kept, dedicated dense kernel")
+        dense = dense_reference(V, w, data, trip_bitmask=r["bitmask"], stats=r["stats"])
         dense["sparse_speedup"] = round(dense["attn_ms"] / stage_ms["sparse_attn"], 2)
         log(f"[bench] dense: {dense}")
 

@@ -21,7 +21,8 @@ Python: the five steps of the layer are HIP kernels.
   layer_forward    the layer: tile_stats of Q, tile_permute_stats of K, tile_permute
                    of V, trippool_project_score, topk_mask, sparse_attn_fwd_raster_io
 
-Measuring a mask against the method's own target:
+Dense attention (the baseline) and measuring a mask against the method's own target:
+  dense_attn_fwd   every key tile kept, no index list (tiled O + LSE; dense_attn_fwd_raster: raster O)
   dense_index      index lists that keep every key tile (dense attention through sparse_attn_fwd)
   teacher_tile_max max-pooled dense attention per (query tile, key tile); topk_mask of it is the
                    oracle tile mask
@@ -58,7 +59,7 @@ __all__ = ["Geometry", "VedaError", "tile_permute", "tile_permute_stats", "tile_
            "trippool_project_score", "topk_mask", "sparse_attn_fwd_raster", "tile_stats",
            "sparse_attn_fwd_raster_io", "sparse_attn_fwd_raster_io_noalloc",
            "sparse_attn_fwd", "attn_queue", "layer_forward",
-           "dense_index", "teacher_tile_max", "avgpool_score", "mask_overlap", "tile_recall",
+           "dense_attn_fwd", "dense_attn_fwd_raster", "dense_index", "teacher_tile_max", "avgpool_score", "mask_overlap", "tile_recall",
            "head_sq_error", "candidate_tiles", "tile_search", "distill_kl", "distill_grad", "adam_step",
            "distill_train", "k_from_keep", "TILE_TOKENS", "TOKEN_MAJOR", "CHANNEL_MAJOR"]
 
@@ -490,6 +491,56 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.
     return b
 
 
+def dense_attn_fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, geom: Geometry,
+                   scale: Optional[float] = None, with_lse: bool = True, o_t: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, work_queue: Optional[torch.Tensor] = None,
+                   dynamic: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Dense attention (every key tile kept, no index list) on tiled Q, K
+    and channel-major V: tiled O and LSE, the bytes sparse_attn_fwd gives
+    with dense_index."""
+    tshape = _tiled_shape(geom, geom.head_dim)
+    _need(q_t, torch.bfloat16, tshape, "q_tiled")
+    _need(k_t, torch.bfloat16, tshape, "k_tiled")
+    _need(v_t, torch.bfloat16, _tiled_cm_shape(geom), "v_tiled")
+    if o_t is None:
+        o_t = torch.empty(tshape, dtype=torch.bfloat16, device=q_t.device)
+    _need(o_t, torch.bfloat16, tshape, "o_tiled")
+    if with_lse and lse is None:
+        lse = torch.empty(tshape[:4], dtype=torch.float32, device=q_t.device)
+    if lse is not None:
+        _need(lse, torch.float32, tshape[:4], "lse")
+    sc = float(scale) if scale is not None else 0.0
+    _lib.check(_lib.lib.veda_dense_attn_fwd(geom.c, q_t.data_ptr(), k_t.data_ptr(), v_t.data_ptr(), sc, o_t.data_ptr(),
+                                            lse.data_ptr() if lse is not None else None,
+                                            _queue_ptr(work_queue, dynamic, q_t.device), _stream(q_t)),
+               "veda_dense_attn_fwd")
+    return o_t, lse
+
+
+def dense_attn_fwd_raster(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, geom: Geometry,
+                          scale: Optional[float] = None, with_lse: bool = True, out: Optional[torch.Tensor] = None,
+                          lse: Optional[torch.Tensor] = None, work_queue: Optional[torch.Tensor] = None,
+                          dynamic: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """dense_attn_fwd writing O in raster order [B, N, heads, d]."""
+    tshape = _tiled_shape(geom, geom.head_dim)
+    _need(q_t, torch.bfloat16, tshape, "q_tiled")
+    _need(k_t, torch.bfloat16, tshape, "k_tiled")
+    _need(v_t, torch.bfloat16, _tiled_cm_shape(geom), "v_tiled")
+    if out is None:
+        out = torch.empty((geom.B, geom.tokens, geom.n_heads, geom.head_dim), dtype=torch.bfloat16, device=q_t.device)
+    so = _raster_strides(out, geom, "out")
+    if with_lse and lse is None:
+        lse = torch.empty(tshape[:4], dtype=torch.float32, device=q_t.device)
+    if lse is not None:
+        _need(lse, torch.float32, tshape[:4], "lse")
+    sc = float(scale) if scale is not None else 0.0
+    _lib.check(_lib.lib.veda_dense_attn_fwd_raster(geom.c, q_t.data_ptr(), k_t.data_ptr(), v_t.data_ptr(), sc,
+                                                   out.data_ptr(), so, lse.data_ptr() if lse is not None else None,
+                                                   _queue_ptr(work_queue, dynamic, q_t.device), _stream(q_t)),
+               "veda_dense_attn_fwd_raster")
+    return out, lse
+
+
 def dense_index(geom: Geometry, device) -> Tuple[torch.Tensor, List[int]]:
     """Index lists that keep every key tile of every head (idx[..., j] = j)
     and the matching k per head: sparse_attn_fwd with these is dense
@@ -504,8 +555,8 @@ def teacher_tile_max(q_t: torch.Tensor, k_t: torch.Tensor, lse_dense: torch.Tens
                      work_queue: Optional[torch.Tensor] = None, dynamic: bool = True) -> torch.Tensor:
     """Max-pooled dense attention: [B, heads, nT_max, nT_max] fp32, the
     largest dense softmax probability between each query tile and key tile
-    (-inf outside the head's block). lse_dense is the LSE of sparse_attn_fwd
-    run with dense_index. `work_queue` and `dynamic` as in sparse_attn_fwd."""
+    (-inf outside the head's block). lse_dense is the LSE of dense_attn_fwd
+    (or of sparse_attn_fwd with dense_index). `work_queue` and `dynamic` as in sparse_attn_fwd."""
     tshape = _tiled_shape(geom, geom.head_dim)
     _need(q_t, torch.bfloat16, tshape, "q_tiled")
     _need(k_t, torch.bfloat16, tshape, "k_tiled")
@@ -614,9 +665,8 @@ def tile_search(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.Te
     q_t = tile_permute(q, g0)
     k_t = tile_permute(k, g0)
     v_t = tile_permute(v, g0, layout=CHANNEL_MAJOR)
-    idx, ks_all = dense_index(g0, q.device)
-    o_dense, _ = sparse_attn_fwd_raster(q_t, k_t, v_t, idx, g0, ks_all, scale, with_lse=False)
-    del q_t, k_t, v_t, idx
+    o_dense, _ = dense_attn_fwd_raster(q_t, k_t, v_t, g0, scale, with_lse=False)
+    del q_t, k_t, v_t
     err = torch.empty((len(cands), B, Hh), dtype=torch.float64, device=q.device)
     for ci, tile in enumerate(cands):
         g = Geometry(B, Hh, d, tuple(grid), [tuple(tile)] * Hh)

@@ -29,7 +29,7 @@ EXPORTS = ["veda_status_str", "veda_num_tiles", "veda_max_tiles", "veda_tile_per
            "veda_adam_step", "veda_tile_permute_stats", "veda_trippool_project_score",
            "veda_sparse_attn_fwd_raster", "veda_sparse_attn_fwd_raster_io", "veda_sparse_attn_fwd_raster_io_noalloc",
            "veda_avgpool_score", "veda_tile_recall", "veda_tile_search_select", "veda_k_from_keep",
-           "veda_distill_mean_kl", "veda_candidate_tiles"]
+           "veda_distill_mean_kl", "veda_candidate_tiles", "veda_dense_attn_fwd", "veda_dense_attn_fwd_raster"]
 
 
 class VedaGrid(ctypes.Structure):
@@ -99,6 +99,12 @@ def _load():
                                                            c_void_p, c_void_p, POINTER(c_int32), c_int32, c_float,
                                                            c_void_p, VedaRasterStrides, c_void_p, c_void_p]
     lib.veda_sparse_attn_fwd_raster_io_noalloc.restype = ctypes.c_int
+    lib.veda_dense_attn_fwd.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p,
+                                        c_void_p, c_void_p]
+    lib.veda_dense_attn_fwd.restype = ctypes.c_int
+    lib.veda_dense_attn_fwd_raster.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_float, c_void_p,
+                                               VedaRasterStrides, c_void_p, c_void_p, c_void_p]
+    lib.veda_dense_attn_fwd_raster.restype = ctypes.c_int
     lib.veda_teacher_tile_max.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p,
                                           c_void_p]
     lib.veda_teacher_tile_max.restype = ctypes.c_int

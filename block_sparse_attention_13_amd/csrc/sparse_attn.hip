@@ -270,7 +270,10 @@ __device__ __forceinline__ void hot_tile(WaveState<D>& w, const floatx16 (&s_cur
   if constexpr (!kLast) mx_next = row_max_base2(mx, scale_log2);
 }
 
-template <int D>
+// kDense: dense attention. The kept tiles of query tile tq are all key
+// tiles 0..nT_hd-1 in order, so the tile index is the loop counter and no
+// index list is read (idx and k_max unused; the host sets k_hd = nT_hd).
+template <int D, bool kDense>
 __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
     GeoTable g, const uint16_t* __restrict__ q_t, const uint16_t* __restrict__ k_t,
     const uint16_t* __restrict__ v_t, const int32_t* __restrict__ idx, int32_t k_max, float scale_log2,
@@ -310,9 +313,11 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
   const int qg = (wave >> 1) & 3, half = wave & 1;
   const int l32 = lane % 32, h = lane / 32;
-  const int32_t* sel = idx + (head_base + tq) * k_max;
+  const int32_t* sel = kDense ? nullptr : idx + (head_base + tq) * k_max;
   const unsigned nT = unsigned(hg.nT);
-  const int kh = hg.k;
+  const int kh = kDense ? hg.nT : hg.k;
+  // Key tile of iteration x (x < kh): the list's entry, or x itself when dense.
+  auto tile_at = [&](int x) -> int32_t { return kDense ? x : sel[x]; };
   const DmaPlan<D> plan = dma_plan<D>(wave, lane, k_t + head_base * tile_elems, v_t + head_base * tile_elems, g.nT_max);
   // Byte offset of a copy source tile; entries outside [0, nT_hd) contribute
   // no keys and tile 0 stands in as a harmless source.
@@ -352,7 +357,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
   // past the end: such copies and products are never used). The next one is
   // loaded just before each iteration's closing barrier, so no scalar load is
   // in flight while the LDS operand reads are being waited for.
-  int32_t j = sel[0], jn = sel[min(1, kh - 1)], jn2 = sel[min(2, kh - 1)];
+  int32_t j = tile_at(0), jn = tile_at(min(1, kh - 1)), jn2 = tile_at(min(2, kh - 1));
   if (plan.is_k) {
     dma_issue<D>(plan, tile_src(j), lbuf);
     dma_issue<D>(plan, tile_src(jn), lbuf + S::kTileElems);
@@ -385,7 +390,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
       mx_cur = mx_next;
       j = jn;
       jn = jn2;
-      jn2 = sel[min(i + 3, kh - 1)];
+      jn2 = tile_at(min(i + 3, kh - 1));
       __builtin_amdgcn_s_waitcnt(0);  // this wave's copies and the next index have landed
       __syncthreads();
     }
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_fwd_kernel(
       const int cur = i & 1;
       dma_issue<D>(plan, tile_src(plan.is_k ? jn2 : jn), lbuf + (plan.is_k ? cur : 2 + (cur ^ 1)) * S::kTileElems);
       jn = jn2;
-      jn2 = sel[min(i + 3, kh - 1)];
+      jn2 = tile_at(min(i + 3, kh - 1));
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
@@ -543,12 +548,19 @@ hipError_t launch_sparse_attn(const GeoTable& g, const uint16_t* q_t, const uint
   const hipError_t e = queue_launch(g, queue, &grid, &n_static, s);
   if (e != hipSuccess) return e;
   const float scale_log2 = scale * 1.44269504088896340736f;
-  if (g.d == 128)
-    sparse_attn_fwd_kernel<128><<<grid, kThreads, 0, s>>>(g, q_t, k_t, v_t, idx, k_max, scale_log2, o_t, lse, o_r,
-                                                         osb, osn, osh, q_r, qsb, qsn, qsh, queue, n_static);
+  const bool dense = idx == nullptr;
+  if (g.d == 128 && dense)
+    sparse_attn_fwd_kernel<128, true><<<grid, kThreads, 0, s>>>(g, q_t, k_t, v_t, idx, k_max, scale_log2, o_t, lse,
+                                                               o_r, osb, osn, osh, q_r, qsb, qsn, qsh, queue, n_static);
+  else if (g.d == 128)
+    sparse_attn_fwd_kernel<128, false><<<grid, kThreads, 0, s>>>(g, q_t, k_t, v_t, idx, k_max, scale_log2, o_t, lse,
+                                                                o_r, osb, osn, osh, q_r, qsb, qsn, qsh, queue, n_static);
+  else if (dense)
+    sparse_attn_fwd_kernel<64, true><<<grid, kThreads, 0, s>>>(g, q_t, k_t, v_t, idx, k_max, scale_log2, o_t, lse,
+                                                              o_r, osb, osn, osh, q_r, qsb, qsn, qsh, queue, n_static);
   else
-    sparse_attn_fwd_kernel<64><<<grid, kThreads, 0, s>>>(g, q_t, k_t, v_t, idx, k_max, scale_log2, o_t, lse, o_r,
-                                                        osb, osn, osh, q_r, qsb, qsn, qsh, queue, n_static);
+    sparse_attn_fwd_kernel<64, false><<<grid, kThreads, 0, s>>>(g, q_t, k_t, v_t, idx, k_max, scale_log2, o_t, lse,
+                                                               o_r, osb, osn, osh, q_r, qsb, qsn, qsh, queue, n_static);
   return hipGetLastError();
 }
 

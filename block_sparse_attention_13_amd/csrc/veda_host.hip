@@ -312,6 +312,51 @@ int veda_sparse_attn_fwd_raster_io(const veda_geom* g, const void* q_raster, ved
       static_cast<const uint16_t*>(q_raster), sq.b, sq.n, sq.h, work_queue, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+// Dense attention keeps every key tile: k_hd = nT_hd for every head.
+void set_dense(GeoTable* t) {
+  for (int hd = 0; hd < t->heads; ++hd) t->h[hd].k = t->h[hd].nT;
+}
+}  // namespace
+
+int veda_dense_attn_fwd(const veda_geom* g, const void* q_tiled, const void* k_tiled, const void* v_tiled,
+                        float softmax_scale, void* o_tiled, float* lse, int32_t* work_queue, void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!q_tiled || !k_tiled || !v_tiled || !o_tiled) return VEDA_ERR_NULL;
+  set_dense(&t);
+  for (const void* p : {q_tiled, k_tiled, v_tiled, static_cast<const void*>(o_tiled)})
+    if (!aligned16(p)) return VEDA_ERR_ALIGN;
+  if (lse && !aligned16(lse)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_queue(t, work_queue));
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) softmax_scale = 1.0f / std::sqrt(float(t.d));
+  VEDA_TRY(check_device());
+  return launched(veda::launch_sparse_attn(
+      t, static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_tiled),
+      static_cast<const uint16_t*>(v_tiled), nullptr, t.nT_max, softmax_scale, static_cast<uint16_t*>(o_tiled), lse,
+      nullptr, 0, 0, 0, nullptr, 0, 0, 0, work_queue, static_cast<hipStream_t>(stream)));
+}
+
+int veda_dense_attn_fwd_raster(const veda_geom* g, const void* q_tiled, const void* k_tiled, const void* v_tiled,
+                               float softmax_scale, void* o_raster, veda_raster_strides s, float* lse,
+                               int32_t* work_queue, void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!q_tiled || !k_tiled || !v_tiled || !o_raster) return VEDA_ERR_NULL;
+  set_dense(&t);
+  for (const void* p : {q_tiled, k_tiled, v_tiled, static_cast<const void*>(o_raster)})
+    if (!aligned16(p)) return VEDA_ERR_ALIGN;
+  if (lse && !aligned16(lse)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_queue(t, work_queue));
+  VEDA_TRY(check_strides(s));
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) softmax_scale = 1.0f / std::sqrt(float(t.d));
+  VEDA_TRY(check_device());
+  return launched(veda::launch_sparse_attn(
+      t, static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_tiled),
+      static_cast<const uint16_t*>(v_tiled), nullptr, t.nT_max, softmax_scale, nullptr, lse,
+      static_cast<uint16_t*>(o_raster), s.b, s.n, s.h, nullptr, 0, 0, 0, work_queue, static_cast<hipStream_t>(stream)));
+}
+
 int veda_sparse_attn_fwd_raster_io_noalloc(const veda_geom* g, const void* q_raster, veda_raster_strides sq,
                                            const void* k_tiled, const void* v_tiled, const int32_t* idx,
                                            const int32_t* k_per_head, int32_t k_max, float softmax_scale,

@@ -156,6 +156,8 @@ hipError_t launch_adam(int64_t n, float* w, const float* grad, float* m, float* 
 // Address, on the current device, of the static work queue used by the
 // allocation-free attention call (looked up once per device).
 hipError_t attn_scratch_queue(int32_t** queue);
+// Attention forward; idx == nullptr runs the dense kernel (every key tile of
+// the head, in order; the table's k_hd must then be nT_hd).
 hipError_t launch_sparse_attn(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t, const uint16_t* v_t,
                               const int32_t* idx, int32_t k_max, float scale, uint16_t* o_t, float* lse,
                               uint16_t* o_r, int64_t osb, int64_t osn, int64_t osh, const uint16_t* q_r,

@@ -19,6 +19,9 @@
  * and with Q never tiled: veda_tile_permute_stats of Q with no tiled output (statistics
  * only), then veda_sparse_attn_fwd_raster_io, which also reads Q in raster order.
  *
+ * Dense attention, the baseline the tile-sparse layer is measured against:
+ *   veda_dense_attn_fwd        every key tile kept, no index list (also veda_dense_attn_fwd_raster)
+ *
  * More calls measure the mask against the method's own target:
  *   veda_teacher_tile_max      max-pooled dense attention per (query tile, key tile); its
  *                              veda_topk_mask is the oracle tile mask
@@ -305,6 +308,27 @@ int veda_sparse_attn_fwd_raster_io(const veda_geom* g, const void* q_raster, ved
                                    const int32_t* k_per_head, int32_t k_max, float softmax_scale,
                                    void* o_raster, veda_raster_strides so, float* lse,
                                    int32_t* work_queue, void* stream);
+
+/*
+ * Dense attention forward: every key tile kept (Veda page, "Scaling Law in Practice": the dense
+ * FlashAttention baseline the tile-sparse layer is timed against; "Attention Structure Distillation",
+ * Teacher: the full attention whose LSE the teacher needs). The same kernel as the tile-sparse
+ * forward with the kept tiles of every query tile being key tiles 0..nT_hd-1 in order, so no index
+ * list exists or is read; the outputs are the bytes veda_sparse_attn_fwd gives with idx[.., j] = j
+ * and k_hd = nT_hd.
+ *   q_tiled, k_tiled, v_tiled, softmax_scale, lse, work_queue   as veda_sparse_attn_fwd
+ *   o_tiled                                                     out  tiled bf16 O, as veda_sparse_attn_fwd
+ */
+int veda_dense_attn_fwd(const veda_geom* g, const void* q_tiled, const void* k_tiled, const void* v_tiled,
+                        float softmax_scale, void* o_tiled, float* lse, int32_t* work_queue, void* stream);
+
+/*
+ * Dense attention writing raster O (as veda_sparse_attn_fwd_raster does for the tile-sparse call).
+ *   o_raster, s   out  raster bf16 O with element strides `s`; lse as veda_sparse_attn_fwd_raster
+ */
+int veda_dense_attn_fwd_raster(const veda_geom* g, const void* q_tiled, const void* k_tiled, const void* v_tiled,
+                               float softmax_scale, void* o_raster, veda_raster_strides s, float* lse,
+                               int32_t* work_queue, void* stream);
 
 /*
  * Allocation-free form of veda_sparse_attn_fwd_raster_io, for callers that cannot allocate device

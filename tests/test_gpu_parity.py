@@ -357,6 +357,70 @@ def test_dense_when_every_tile_is_kept(grid, tiles, d, r):
         check_head(w, data, out, hd, ks, list(range(ks[hd])))
 
 
+@pytest.mark.parametrize("grid,tiles,d,r,B", [
+    ((5, 6, 20), [(2, 4, 16)], 64, 64, 1),
+    ((3, 9, 17), [(1, 8, 16), (8, 4, 4)], 128, 32, 1),
+    ((9, 27, 33), [(2, 4, 16), (1, 8, 16)], 128, 64, 4),     # 1,600 work items: through the work queue
+])
+def test_dense_kernel(grid, tiles, d, r, B):
+    """The dedicated dense forward (no index list): raster O and LSE against
+    the oracle's dense attention, and the same bytes as the tile-sparse
+    kernel with every tile kept (tiled O, raster O, LSE)."""
+    V = _lib()
+    w = dataclasses.replace(_random_workload(grid, tiles, d, r, heads=len(tiles), seed=31), B=B)
+    say(f"[dense kernel] grid {grid} tiles {tiles} d {d} B {B}")
+    data = datagen.generate(w)
+    geom = geometry(w)
+    q, k, v = (to_dev_bf16(data[n]) for n in ("q", "k", "v"))
+    q_t, k_t = V.tile_permute(q, geom), V.tile_permute(k, geom)
+    v_t = V.tile_permute(v, geom, layout=V.CHANNEL_MAJOR)
+    o_t, lse = V.dense_attn_fwd(q_t, k_t, v_t, geom)
+    o_r, lse_r = V.dense_attn_fwd_raster(q_t, k_t, v_t, geom)
+    idx, ks = V.dense_index(geom, q.device)
+    o_s, lse_s = V.sparse_attn_fwd(q_t, k_t, v_t, idx, geom, ks)
+    o_sr, _ = V.sparse_attn_fwd_raster(q_t, k_t, v_t, idx, geom, ks)
+    torch.cuda.synchronize()
+    assert torch.equal(o_t.view(torch.int16), o_s.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse_s.view(torch.int32))
+    assert torch.equal(o_r.view(torch.int16), o_sr.view(torch.int16))
+    for b in range(B):
+        for hd in range(w.heads):
+            qh, kh, vh = (O.bf16_bits_to_float(data[n][b, :, hd, :]) for n in ("q", "k", "v"))
+            od, lsed = O.dense_attention(qh, kh, vh, 1.0 / math.sqrt(d))
+            compare_o(f32_of_bf16(o_r[b, :, hd, :]), od, f"dense kernel b {b} head {hd}")
+            pos = O.tiled_position(grid, tiles[hd])
+            compare_lse(lse[b, hd].cpu().numpy().reshape(-1)[pos], lsed, f"dense kernel b {b} head {hd}")
+            real = lse_r[b, hd].cpu().numpy().reshape(-1)[pos]
+            assert np.array_equal(real.view(np.uint32), lse[b, hd].cpu().numpy().reshape(-1)[pos].view(np.uint32))
+
+
+def test_dense_kernel_long_sampled():
+    """Dense forward on one head of the 245,760-token workload (1920 x 1920
+    tile pairs), sampled query tiles against the oracle (every key tile
+    kept, raster order)."""
+    V = _lib()
+    w = W["long"].with_heads(1)
+    say("[dense kernel] long, 1 head")
+    data = datagen.generate(w)
+    geom = geometry(w)
+    q, k, v = (to_dev_bf16(data[n]) for n in ("q", "k", "v"))
+    q_t, k_t = V.tile_permute(q, geom), V.tile_permute(k, geom)
+    v_t = V.tile_permute(v, geom, layout=V.CHANNEL_MAJOR)
+    o_r, lse = V.dense_attn_fwd_raster(q_t, k_t, v_t, geom)
+    torch.cuda.synchronize()
+    tile = w.head_tiles()[0]
+    nT = geom.num_tiles(0)
+    tiles = [0, 777, nT - 1]
+    qh, kh, vh = (O.bf16_bits_to_float(data[n][0, :, 0, :]) for n in ("q", "k", "v"))
+    sel = np.tile(np.arange(nT), (nT, 1))
+    od, lsed = O.sparse_attention(qh, kh, vh, w.grid, tile, sel, 1.0 / math.sqrt(w.d), query_tiles=tiles)
+    rows = np.flatnonzero(np.isfinite(lsed))
+    assert len(rows) == 128 * len(tiles)
+    compare_o(f32_of_bf16(o_r[0, :, 0, :])[rows], od[rows], "dense kernel long")
+    pos = O.tiled_position(w.grid, tile)
+    compare_lse(lse[0, 0].cpu().numpy().reshape(-1)[pos[rows]], lsed[rows], "dense kernel long")
+
+
 def test_single_tile_kept():
     w = _random_workload((4, 16, 16), [(2, 8, 8)], 64, 32, heads=2, seed=5)
     data = datagen.generate(w)
