@@ -99,7 +99,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(GeoTable g, const float*
     const uint64_t eq_mask = __ballot(eq);
     const bool take = gt || (eq && eq_seen + int(count_below(eq_mask)) < need_eq);
     const uint64_t take_mask = __ballot(take);
-    if (take) out[kept + int(count_below(take_mask))] = i * 64 + lane;
+    const int pos = kept + int(count_below(take_mask));
+    if (take && pos < k) out[pos] = i * 64 + lane;   // exactly k are taken; the bound keeps writes in the row
     kept += __popcll(take_mask);
     eq_seen += __popcll(eq_mask);
     if (bm) {

@@ -584,6 +584,46 @@ def test_topk_on_crafted_scores():
         assert np.all(idx[0, 0, rows:].cpu().numpy() == np.arange(k))
 
 
+def test_topk_on_narrow_and_skewed_rows():
+    """Rows whose scores share long leading bits (a band of width 2^-12
+    around 1, or around -3), two-valued rows, rows with one outlier above a
+    constant, values spanning the whole float range, constant rows and
+    rows whose threshold lies many octaves below the maximum: the lists equal
+    the oracle's. The row length (1,500 tiles) leaves pad slots in the last
+    64-wide chunk of every row."""
+    V = _lib()
+    rng = np.random.default_rng(43)
+    g = V.Geometry(1, 1, 128, (60, 40, 80), [(4, 4, 8)])
+    nT, k = g.max_tiles(), 75
+    assert nT == 1500 and nT % 64
+    S = np.empty((nT, nT), np.float32)
+    for i in range(nT):
+        kind = i % 8
+        if kind == 0:
+            S[i] = 1.0 + rng.integers(0, 64, nT) * np.float32(2.0 ** -18)
+        elif kind == 1:
+            S[i] = -3.0 - rng.integers(0, 64, nT) * np.float32(2.0 ** -17)
+        elif kind == 2:
+            S[i] = np.where(rng.random(nT) < 0.3, np.float32(2.5), np.float32(-2.5))
+        elif kind == 3:
+            S[i] = 7.0
+            S[i, rng.integers(0, nT)] = 7.0 + 2.0 ** -20
+        elif kind == 4:
+            S[i] = (rng.standard_normal(nT) * 10.0 ** rng.uniform(-30, 30, nT)).astype(np.float32)
+        elif kind == 5:
+            S[i] = -rng.uniform(0, 1, nT).astype(np.float32) ** 8
+        elif kind == 6:
+            S[i] = 0.5
+        else:   # one huge value, the rest spread far below it
+            S[i] = np.exp(rng.standard_normal(nT) * 3).astype(np.float32)
+            S[i, rng.integers(0, nT)] = 1e30
+    idx, bm = V.topk_mask(torch.from_numpy(S).reshape(1, 1, nT, nT).cuda(), g, [k])
+    torch.cuda.synchronize()
+    got = idx[0, 0].cpu().numpy()
+    assert np.array_equal(got, O.topk(S, k))
+    assert np.array_equal(bits_of(bm[0, 0]), O.bitmask(got, nT))
+
+
 def test_topk_orders_nan_scores_by_bit_pattern():
     """Three +NaN and five -NaN scores in every row (no infinities): +NaN
     ranks above every finite score and -NaN below, so the lists equal the
