@@ -696,7 +696,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": attention_traffic(args.workload),
                      "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": attention_bytes(w),
-                     "kernel": "sparse_attn_fwd_kernel<128>", "flops_per_launch": f_attn,
+                     "kernel": "sparse_attn_fwd_kernel<128, false>", "flops_per_launch": f_attn,
                      "counters": attention_mfma_counters(args.workload)},
         "cpu_baseline": cpu,
         "parity_head0": parity,
