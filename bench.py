@@ -353,6 +353,8 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0, grap
         out["flushed"] = timed(flush)
         del flush
     out["graph_ms_step"] = graph_timed(step, steps) if graph else None
+    if keep_data:
+        out["scores_mfma"] = mfma_scores_report(V, geom, ks, bufs, sum(w.tiles_per_head()) * w.B)
     out.update({"data": data if keep_data else None, "valid_flops": valid_pair_flops(w, bufs["idx"].cpu().numpy()),
                 "bitmask": bufs["bitmask"] if keep_data else None,
                 "stats": (bufs["stats_q"], bufs["stats_k"]) if keep_data else None})
@@ -362,6 +364,34 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0, grap
     del bufs, q, k, v, wq, wk
     torch.cuda.empty_cache()
     return out
+
+
+def mfma_scores_report(V, geom, ks, bufs, n_rows, reps=10):
+    """The estimator's scores computed on the matrix cores (veda_tile_scores_mfma)
+    from the layer's own features: its time beside the layer's ordered
+    projection-and-scores stage, and how many query tiles' Top-k lists differ
+    from the layer's (near-ties only; the layer keeps the ordered scores)."""
+    import numpy as np
+    import torch
+    s = torch.empty_like(bufs["scores"])
+    V.tile_scores_mfma(bufs["feat_q"], bufs["feat_k"], geom, out=s)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        V.tile_scores_mfma(bufs["feat_q"], bufs["feat_k"], geom, out=s)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    idx, _ = V.topk_mask(s, geom, ks, with_bitmask=False)
+    differ = int((idx != bufs["idx"]).any(dim=-1).sum().item())
+    same = float((s == bufs["scores"]).float().mean().item())
+    del s, idx
+    res = {"scores_ms_median": round(float(np.median(ts)), 4), "scores_bit_equal_fraction": round(same, 4),
+           "topk_rows_differing": differ, "topk_rows": int(n_rows),
+           "note": "bf16 MFMA scores from the layer's features; the layer keeps the ordered fp32 scores (bit-exact masks)"}
+    log(f"[bench] MFMA scores: {res}")
+    return res
 
 
 def graph_timed(step, steps: int):
@@ -709,6 +739,7 @@ def main():
         "per_config": per_config,
         "head_shard": shard,
         "dense_reference": dense,
+        "estimator_scores_mfma": r.get("scores_mfma"),
         "tile_search": search,
         "distillation": distill,
     }

@@ -13,6 +13,8 @@ Python: the five steps of the layer are HIP kernels.
   tile_unpermute   tiled -> raster
   tile_permute_stats      raster Q or K -> token-major tiles + TripPool stats, one pass
   trippool_project_score  stats + W_q, W_k -> features, tile scores
+  tile_scores_mfma the same scores from the features on the matrix cores (within rounding, not
+                   bit-identical; the layer keeps the ordered scores)
   sparse_attn_fwd_raster  sparse_attn_fwd writing raster O (no unpermute pass)
   tile_stats       the TripPool statistics of raster Q or K alone (no tiled copy)
   sparse_attn_fwd_raster_io  sparse_attn_fwd_raster reading raster Q (no tiled Q)
@@ -59,7 +61,7 @@ __all__ = ["Geometry", "VedaError", "tile_permute", "tile_permute_stats", "tile_
            "trippool_project_score", "topk_mask", "sparse_attn_fwd_raster", "tile_stats",
            "sparse_attn_fwd_raster_io", "sparse_attn_fwd_raster_io_noalloc",
            "sparse_attn_fwd", "attn_queue", "layer_forward",
-           "dense_attn_fwd", "dense_attn_fwd_raster", "dense_index", "teacher_tile_max", "avgpool_score", "mask_overlap", "tile_recall",
+           "dense_attn_fwd", "dense_attn_fwd_raster", "dense_index", "teacher_tile_max", "avgpool_score", "tile_scores_mfma", "mask_overlap", "tile_recall",
            "head_sq_error", "candidate_tiles", "tile_search", "distill_kl", "distill_grad", "adam_step",
            "distill_train", "k_from_keep", "TILE_TOKENS", "TOKEN_MAJOR", "CHANNEL_MAJOR"]
 
@@ -281,6 +283,25 @@ def avgpool_score(stats_q: torch.Tensor, stats_k: torch.Tensor, geom: Geometry,
     _need(out, torch.float32, (geom.B, geom.n_heads, nT, nT), "scores")
     _lib.check(_lib.lib.veda_avgpool_score(geom.c, stats_q.data_ptr(), stats_k.data_ptr(), out.data_ptr(),
                                            _stream(stats_q)), "veda_avgpool_score")
+    return out
+
+
+def tile_scores_mfma(feat_q: torch.Tensor, feat_k: torch.Tensor, geom: Geometry,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The estimator's tile scores [B, heads, nT_max, nT_max] fp32 from the
+    projected features, computed with bf16 MFMA (fp32 accumulation in the
+    matrix core's order): within fp32 rounding of trippool_project_score's
+    ordered scores, not always bit-identical to them."""
+    nT = geom.max_tiles()
+    r = feat_q.shape[-1] if feat_q.dim() == 4 else -1
+    shp = (geom.B, geom.n_heads, nT, r)
+    _need(feat_q, torch.bfloat16, shp, "feat_q")
+    _need(feat_k, torch.bfloat16, shp, "feat_k")
+    if out is None:
+        out = torch.empty((geom.B, geom.n_heads, nT, nT), dtype=torch.float32, device=feat_q.device)
+    _need(out, torch.float32, (geom.B, geom.n_heads, nT, nT), "scores")
+    _lib.check(_lib.lib.veda_tile_scores_mfma(geom.c, feat_q.data_ptr(), feat_k.data_ptr(), int(r), out.data_ptr(),
+                                              _stream(feat_q)), "veda_tile_scores_mfma")
     return out
 
 

@@ -18,6 +18,9 @@
 // Every accumulation runs in a fixed ascending order with one rounding per
 // step (products of bf16 values are exact in fp32), so the results are
 // reproducible bit for bit and independent of the launch shape.
+//   tile_scores_mfma_kernel  the same S as the small bf16 GEMM the estimator
+//     is (32x32x16 bf16 MFMA, fp32 accumulation in the matrix core's own
+//     order): not bit-identical to the ordered sum, within its rounding bound.
 #include "veda_internal.hpp"
 
 namespace veda {
@@ -286,6 +289,59 @@ __global__ __launch_bounds__(kThreads) void tile_scores_kernel(GeoTable g, const
   }
 }
 
+// S = feat_q . feat_k^T on the matrix cores. A workgroup of 4 waves takes a
+// 128 x 128 block of one head; wave w owns rows 32w..32w+31 against all 128
+// columns as four 32 x 32 MFMA outputs, each accumulated over r / 16 k-steps.
+// Operands come straight from the bf16 feature rows: lane l of a k-step
+// holds 8 consecutive channels (16 bytes) of row l % 32, channels 8 (l / 32)
+// onward of the step. Output element v of lane l is row 8 (v / 4) + 4 (l / 32)
+// + v % 4, column l % 32, so 32 lanes write 128 contiguous bytes of a row.
+typedef __bf16 bf16x8_s __attribute__((ext_vector_type(8)));
+typedef float floatx16_s __attribute__((ext_vector_type(16)));
+template <int R>
+__global__ __launch_bounds__(256) void tile_scores_mfma_kernel(GeoTable g, const uint16_t* __restrict__ feat_q,
+                                                              const uint16_t* __restrict__ feat_k,
+                                                              float* __restrict__ scores) {
+  constexpr int kSteps = R / 16;
+  const int hd = blockIdx.y, b = blockIdx.z;
+  const HeadGeo hg = g.h[hd];
+  const int nb = (g.nT_max + kScoreTile - 1) / kScoreTile;
+  const int i0 = blockIdx.x / nb * kScoreTile, j0 = blockIdx.x % nb * kScoreTile;
+  const int64_t head_row = (int64_t(b) * g.heads + hd) * g.nT_max;
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, l32 = lane % 32, h = lane / 32;
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+  const int ia = i0 + 32 * wave + l32;   // rows past the head read as zeros and are written -inf
+  uint4 qf[kSteps];
+#pragma unroll
+  for (int kk = 0; kk < kSteps; ++kk)
+    qf[kk] = ia < hg.nT ? *reinterpret_cast<const uint4*>(feat_q + (head_row + ia) * R + 16 * kk + 8 * h) : zero4;
+  floatx16_s acc[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int jb = j0 + 32 * n + l32;
+    floatx16_s c = {};
+#pragma unroll
+    for (int kk = 0; kk < kSteps; ++kk) {
+      const uint4 kf =
+          jb < hg.nT ? *reinterpret_cast<const uint4*>(feat_k + (head_row + jb) * R + 16 * kk + 8 * h) : zero4;
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_s, qf[kk]),
+                                                  __builtin_bit_cast(bf16x8_s, kf), c, 0, 0, 0);
+    }
+    acc[n] = c;
+  }
+  const float ninf = -__builtin_inff();
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int j = j0 + 32 * n + l32;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int i = i0 + 32 * wave + 8 * (v / 4) + 4 * h + v % 4;
+      if (i < g.nT_max && j < g.nT_max)
+        scores[(head_row + i) * g.nT_max + j] = (i < hg.nT && j < hg.nT) ? acc[n][v] : ninf;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_trippool_features(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t,
@@ -327,6 +383,17 @@ hipError_t launch_tile_scores(const GeoTable& g, const uint16_t* feat_q, const u
     tile_scores_kernel<64><<<grid, kThreads, 0, s>>>(g, feat_q, feat_k, 64, scores);
   else
     tile_scores_kernel<32><<<grid, kThreads, 0, s>>>(g, feat_q, feat_k, 32, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_scores_mfma(const GeoTable& g, const uint16_t* feat_q, const uint16_t* feat_k, int32_t r,
+                                   float* scores, hipStream_t s) {
+  const int nb = (g.nT_max + kScoreTile - 1) / kScoreTile;
+  const dim3 grid(nb * nb, g.heads, g.B);
+  if (r == 64)
+    tile_scores_mfma_kernel<64><<<grid, 256, 0, s>>>(g, feat_q, feat_k, scores);
+  else
+    tile_scores_mfma_kernel<32><<<grid, 256, 0, s>>>(g, feat_q, feat_k, scores);
   return hipGetLastError();
 }
 

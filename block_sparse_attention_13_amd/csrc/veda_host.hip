@@ -227,6 +227,20 @@ int veda_trippool_project_score(const veda_geom* g, const void* stats_q, const v
                                            static_cast<const uint16_t*>(feat_k), rank, scores, st));
 }
 
+int veda_tile_scores_mfma(const veda_geom* g, const void* feat_q, const void* feat_k, int32_t rank, float* scores,
+                          void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!feat_q || !feat_k || !scores) return VEDA_ERR_NULL;
+  if (rank != 32 && rank != 64) return VEDA_ERR_SHAPE;
+  for (const void* p : {feat_q, feat_k, static_cast<const void*>(scores)})
+    if (!aligned16(p)) return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_device());
+  return launched(veda::launch_tile_scores_mfma(t, static_cast<const uint16_t*>(feat_q),
+                                                static_cast<const uint16_t*>(feat_k), rank, scores,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 int veda_avgpool_score(const veda_geom* g, const void* stats_q, const void* stats_k, float* scores, void* stream) {
   GeoTable t;
   VEDA_TRY(build_table(g, &t));

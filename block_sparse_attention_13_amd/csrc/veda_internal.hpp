@@ -130,6 +130,8 @@ hipError_t launch_trippool_project(const GeoTable& g, const uint16_t* stats_q, c
                                    uint16_t* feat_k, hipStream_t s);
 hipError_t launch_tile_scores(const GeoTable& g, const uint16_t* feat_q, const uint16_t* feat_k, int32_t r,
                               float* scores, hipStream_t s);
+hipError_t launch_tile_scores_mfma(const GeoTable& g, const uint16_t* feat_q, const uint16_t* feat_k, int32_t r,
+                                   float* scores, hipStream_t s);
 hipError_t launch_avgpool_scores(const GeoTable& g, const uint16_t* stats_q, const uint16_t* stats_k, float* scores,
                                  hipStream_t s);
 hipError_t launch_topk(const GeoTable& g, const float* scores, int32_t k_max, int32_t* idx, uint32_t* bitmask,

@@ -26,6 +26,8 @@
  *   veda_teacher_tile_max      max-pooled dense attention per (query tile, key tile); its
  *                              veda_topk_mask is the oracle tile mask
  *   veda_avgpool_score         average-pooling tile scores, the pages' baseline mask
+ *   veda_tile_scores_mfma      the estimator's scores on the matrix cores (within rounding of the
+ *                              ordered scores, not bit-identical)
  *   veda_mask_overlap          common kept tiles of two masks
  *   veda_tile_recall           tile recall of a mask against the oracle mask
  *   veda_head_sq_error         squared output error per head (objective of the head-aware tile search)
@@ -211,6 +213,25 @@ int veda_trippool_score(const veda_geom* g, const void* q_tiled, const void* k_t
 int veda_trippool_project_score(const veda_geom* g, const void* stats_q, const void* stats_k,
                                 const void* w_q, const void* w_k, int32_t rank,
                                 void* feat_q, void* feat_k, float* scores, void* stream);
+
+/*
+ * Tile scores as the small bf16 GEMM the estimator is (Veda page, "Attention Structure Distillation",
+ * Estimator: the scores of every (query tile, key tile) pair are the products of the head-specific
+ * projections), computed on the matrix cores: S[b, hd, i, j] = sum over c of feat_q[i, c] * feat_k[j, c]
+ * with bf16 MFMA instructions accumulating in fp32 in the hardware's own order.
+ *   feat_q, feat_k    in   bf16 [B, heads, nT_max, rank], as veda_trippool_project_score writes them
+ *   rank              in   32 or 64 (else VEDA_ERR_SHAPE)
+ *   scores            out  fp32 [B, heads, nT_max, nT_max]; -inf outside the head's nT_hd x nT_hd block
+ * Each product of two bf16 values is exact in fp32, so each score differs from the ordered sum that
+ * veda_trippool_project_score computes by at most the rounding of an fp32 sum of rank terms:
+ * |S_mfma - S_ordered| <= 2 * gamma_rank * sum over c of |feat_q[i, c] * feat_k[j, c]|, with
+ * gamma_n = n u / (1 - n u), u = 2^-24. The two are often bit-identical but not always, so a
+ * veda_topk_mask of these scores can differ from the ordered path's where two key tiles are that
+ * close. The layer's route uses the ordered path, whose masks are reproducible bit for bit; this call
+ * is the faster alternative for callers that accept near-tie differences.
+ */
+int veda_tile_scores_mfma(const veda_geom* g, const void* feat_q, const void* feat_k, int32_t rank,
+                          float* scores, void* stream);
 
 /*
  * Average-pooling tile scores, the baseline mask the pages compare Veda's against at the same budget
