@@ -66,6 +66,52 @@ __global__ __launch_bounds__(kThreads) void tile_permute_kernel(GeoTable g, cons
   for (int p = 0; p < M::kPasses; ++p) store_stream(&dst[(row0 + p * M::kRowsPerPass) * M::kChunks + chunk], val[p]);
 }
 
+// The TripPool statistics of one tile held in LDS (tile_s: 128 slot rows of d
+// bf16 values): threads 0..d-1 each sum one channel over the real slots in slot
+// order (fp32 from +0, then a correctly rounded divide by the real-token count
+// and a round to bf16); threads d..2d-1 take that channel's maximum and
+// minimum (IEEE total order, -0 below +0). Writes the tile's 3d statistics.
+template <int D>
+__device__ __forceinline__ void tile_stats_from_lds(const HeadGeo& hg, const BoxExtent& e, const uint4* tile_s,
+                                                    uint16_t* st_out) {
+  const int c = threadIdx.x % D;
+  const uint16_t* col = reinterpret_cast<const uint16_t*>(tile_s) + c;  // slot s of channel c at col[s * D]
+  const bool full = box_is_full(hg, e);
+  if (int(threadIdx.x) < D) {
+    float sum = 0.0f;
+    if (full) {
+#pragma unroll 16
+      for (int sl = 0; sl < VEDA_TILE_TOKENS; ++sl) sum = sum + bf16_to_f32(col[sl * D]);
+    } else {
+      for (int sl = 0; sl < VEDA_TILE_TOKENS; ++sl)
+        if (slot_is_real(hg, e, sl)) sum = sum + bf16_to_f32(col[sl * D]);
+    }
+    // sum / n in double then to float is the correctly rounded float quotient
+    // (53 >= 2*24 + 2, so the double rounding is innocuous).
+    const int32_t n_real = e.vt * e.vh * e.vw;
+    st_out[c] = f32_to_bf16_rne(float(double(sum) / double(n_real)));
+  } else if (int(threadIdx.x) < 2 * D) {
+    int32_t mx = -(1 << 20), mn = 1 << 20;
+    if (full) {
+#pragma unroll 16
+      for (int sl = 0; sl < VEDA_TILE_TOKENS; ++sl) {
+        const int32_t key = total_order_key(col[sl * D]);
+        mx = max(mx, key);
+        mn = min(mn, key);
+      }
+    } else {
+      for (int sl = 0; sl < VEDA_TILE_TOKENS; ++sl) {
+        if (!slot_is_real(hg, e, sl)) continue;
+        const int32_t key = total_order_key(col[sl * D]);
+        mx = max(mx, key);
+        mn = min(mn, key);
+      }
+    }
+    st_out[D + c] = from_total_order_key(mx);
+    st_out[2 * D + c] = from_total_order_key(mn);
+  }
+}
+
 // Token-major permute of Q or K fused with the TripPool statistics of each
 // tile (Veda page, "Attention Structure Distillation", Estimator: average,
 // maximum and minimum per tile; "Theoretical Rationale" 2): the tile is moved
@@ -112,41 +158,52 @@ __global__ __launch_bounds__(kThreads) void tile_permute_stats_kernel(GeoTable g
   }
   __syncthreads();
 
-  const int c = threadIdx.x % D;
-  const uint16_t* col = reinterpret_cast<const uint16_t*>(tile_s) + c;  // slot s of channel c at col[s * D]
-  const bool full = box_is_full(hg, e);
-  if (int(threadIdx.x) < D) {
-    float sum = 0.0f;
-    if (full) {
-#pragma unroll 16
-      for (int sl = 0; sl < VEDA_TILE_TOKENS; ++sl) sum = sum + bf16_to_f32(col[sl * D]);
-    } else {
-      for (int sl = 0; sl < VEDA_TILE_TOKENS; ++sl)
-        if (slot_is_real(hg, e, sl)) sum = sum + bf16_to_f32(col[sl * D]);
+  tile_stats_from_lds<D>(hg, e, tile_s, st_out);
+}
+
+// Statistics only (no tiled copy, as for Q): a workgroup takes kStatTiles
+// consecutive tiles of one (batch, head) and loads the next tile's rows into
+// registers while the current tile's statistics are taken from LDS, so the
+// loads of one tile run under the serial per-channel sums of the previous one.
+// The statistics are the same code as above, so the bytes are identical.
+constexpr int kStatTiles = 4;
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void tile_stats_kernel(GeoTable g, const uint16_t* __restrict__ x, int64_t sb,
+                                                             int64_t sn, int64_t sh, uint16_t* __restrict__ stats) {
+  using M = RowMap<D>;
+  static_assert(2 * D <= kThreads, "one thread per channel and statistic group");
+  __shared__ uint4 tile_s[VEDA_TILE_TOKENS * M::kChunks];
+  const int hd = blockIdx.y, b = blockIdx.z;
+  const HeadGeo hg = g.h[hd];
+  const int chunk = threadIdx.x % M::kChunks;
+  const int row0 = threadIdx.x / M::kChunks;
+  const int64_t head_row = (int64_t(b) * g.heads + hd) * g.nT_max;
+  const uint16_t* src = x + int64_t(b) * sb + int64_t(hd) * sh + chunk * 8;
+  const int32_t t0 = blockIdx.x * kStatTiles;
+  const int32_t t_end = min(t0 + kStatTiles, g.nT_max);
+  uint4 val[M::kPasses];
+  auto load = [&](int32_t tau) {  // tau < nT_hd
+    const BoxExtent e = box_extent(g, hg, tau);
+#pragma unroll
+    for (int p = 0; p < M::kPasses; ++p) {
+      const int64_t n = raster_of_slot(g, hg, e, row0 + p * M::kRowsPerPass);
+      val[p] = n >= 0 ? load_stream(src + n * sn) : make_uint4(0, 0, 0, 0);
     }
-    // sum / n in double then to float is the correctly rounded float quotient
-    // (53 >= 2*24 + 2, so the double rounding is innocuous).
-    const int32_t n_real = e.vt * e.vh * e.vw;
-    st_out[c] = f32_to_bf16_rne(float(double(sum) / double(n_real)));
-  } else if (int(threadIdx.x) < 2 * D) {
-    int32_t mx = -(1 << 20), mn = 1 << 20;
-    if (full) {
-#pragma unroll 16
-      for (int sl = 0; sl < VEDA_TILE_TOKENS; ++sl) {
-        const int32_t key = total_order_key(col[sl * D]);
-        mx = max(mx, key);
-        mn = min(mn, key);
-      }
-    } else {
-      for (int sl = 0; sl < VEDA_TILE_TOKENS; ++sl) {
-        if (!slot_is_real(hg, e, sl)) continue;
-        const int32_t key = total_order_key(col[sl * D]);
-        mx = max(mx, key);
-        mn = min(mn, key);
-      }
+  };
+  if (t0 < hg.nT) load(t0);
+  for (int32_t tau = t0; tau < t_end; ++tau) {
+    uint16_t* st_out = stats + (head_row + tau) * 3 * D;
+    if (tau >= hg.nT) {  // tile beyond this head's grid: defined zeros
+      for (int c = threadIdx.x; c < 3 * D; c += kThreads) st_out[c] = 0;
+      continue;
     }
-    st_out[D + c] = from_total_order_key(mx);
-    st_out[2 * D + c] = from_total_order_key(mn);
+    __syncthreads();  // the previous tile's statistics are done with tile_s
+#pragma unroll
+    for (int p = 0; p < M::kPasses; ++p) tile_s[(row0 + p * M::kRowsPerPass) * M::kChunks + chunk] = val[p];
+    __syncthreads();
+    if (tau + 1 < t_end && tau + 1 < hg.nT) load(tau + 1);  // in flight during this tile's statistics
+    tile_stats_from_lds<D>(hg, box_extent(g, hg, tau), tile_s, st_out);
   }
 }
 
@@ -237,6 +294,14 @@ hipError_t launch_tile_permute(const GeoTable& g, const uint16_t* x, int64_t sb,
 
 hipError_t launch_tile_permute_stats(const GeoTable& g, const uint16_t* x, int64_t sb, int64_t sn, int64_t sh,
                                      uint16_t* xt, uint16_t* stats, hipStream_t s) {
+  if (!xt) {  // statistics only
+    const dim3 grid((g.nT_max + kStatTiles - 1) / kStatTiles, g.heads, g.B);
+    if (g.d == 128)
+      tile_stats_kernel<128><<<grid, kThreads, 0, s>>>(g, x, sb, sn, sh, stats);
+    else
+      tile_stats_kernel<64><<<grid, kThreads, 0, s>>>(g, x, sb, sn, sh, stats);
+    return hipGetLastError();
+  }
   const dim3 grid(g.nT_max, g.heads, g.B);
   if (g.d == 128)
     tile_permute_stats_kernel<128><<<grid, kThreads, 0, s>>>(g, x, sb, sn, sh, xt, stats);
