@@ -2,14 +2,21 @@
 // Execution: Top-k over the estimator's scores, per query tile and per head,
 // yields the binary tile mask passed to the tile-skipping kernel).
 //
-// One wave per row (b, head, query tile). Each score becomes a 32-bit key
+// One wave per row (b, head, query tile). A row of up to 2048 scores is
+// first copied into the wave's own LDS area in 1-KiB pieces with the gfx950
+// LDS-DMA buffer loads (a per-row buffer, so pieces past the row read zeros),
+// then read back one score per lane and chunk; longer rows are read straight
+// into registers with streaming loads. Each score becomes a 32-bit key
 // whose unsigned order is the float order (-0 is first made +0, so signed
 // zeros tie). The row's keys stay in registers (chunk i, lane l holds key
 // tile j = 64*i + l). A bitwise search from the top bit finds a threshold t:
 // the k-th largest key, or (stopping early) any t with exactly k keys >= t.
 // One ascending pass over the chunks then keeps every key > t and the
 // lowest-indexed keys == t until k are kept, which is exactly the
-// lower-index tie rule. Ballots give output positions and bitmask words.
+// lower-index tie rule. Ballots give output positions and bitmask words; each
+// chunk's two bitmask words go into one lane each of a register, and the
+// row's words are stored together at the end, instead of one single-lane store
+// per word.
 #include "veda_internal.hpp"
 
 namespace veda {
@@ -47,6 +54,11 @@ __device__ __forceinline__ uint32_t count_below(uint64_t mask) {  // set bits of
 template <int NCH>
 __global__ __launch_bounds__(kThreads) void topk_kernel(GeoTable g, const float* __restrict__ scores, int32_t k_max,
                                                        int32_t* __restrict__ idx, uint32_t* __restrict__ bitmask) {
+  constexpr bool kStaged = NCH <= 32;   // rows of up to 2048 scores go through LDS
+  // Each wave's area is whole 1-KiB pieces: a piece always writes all 64 lanes'
+  // 16 bytes (zeros past the row), so a shorter area would spill into the next.
+  constexpr int kRowWords = kStaged ? (NCH * 64 + 255) / 256 * 256 : 1;
+  __shared__ __attribute__((aligned(16))) uint32_t row_s[kRowsPerBlock][kRowWords];
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int32_t tq = blockIdx.x * kRowsPerBlock + wave;
   const int hd = blockIdx.y, b = blockIdx.z;
@@ -65,11 +77,27 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(GeoTable g, const float*
   }
   const int n = hg.nT, k = hg.k;
   const float* s = scores + row * g.nT_max;
-  uint32_t key[NCH];
+  uint32_t key[NCH];  // key of score j = 64 i + lane in key[i]; 0 (below every finite score's key) past the row
+  if constexpr (kStaged) {
+    typedef __attribute__((address_space(3))) uint32_t lds_u32;
+    lds_u32* dst = (lds_u32*)&row_s[wave][0];
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(s), 0, n * 4, 0x00020000);
+    const int pieces = (n * 4 + 1023) / 1024;
+    for (int c = 0; c < pieces; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst + c * 256, 16, 16 * lane, c * 1024, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's pieces have landed (only this wave reads them)
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int j = i * 64 + lane;
-    key[i] = j < n ? order_key(s[j]) : 0u;  // 0 lies below every finite score's key
+    for (int i = 0; i < NCH; ++i) {
+      const int j = i * 64 + lane;
+      key[i] = j < n ? order_key(__uint_as_float(row_s[wave][j])) : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int j = i * 64 + lane;
+      key[i] = j < n ? order_key(__builtin_nontemporal_load(s + j)) : 0u;
+    }
   }
   // Largest t with #{key >= t} >= k: the k-th largest key. The search may
   // stop early at a t with exactly k keys >= t; those k keys are then the
@@ -91,6 +119,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(GeoTable g, const float*
   for (int i = 0; i < NCH; ++i) c_gt += key[i] > t;
   const int need_eq = k - wave_sum(c_gt);  // keys equal to t still to keep, lowest index first
 
+  constexpr int kWordRegs = (2 * NCH + 63) / 64;  // bitmask words of the row, 64 per register
+  uint32_t bmw[kWordRegs];
+#pragma unroll
+  for (int r = 0; r < kWordRegs; ++r) bmw[r] = 0u;
   int kept = 0, eq_seen = 0;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
@@ -103,10 +135,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(GeoTable g, const float*
     if (take && pos < k) out[pos] = i * 64 + lane;   // exactly k are taken; the bound keeps writes in the row
     kept += __popcll(take_mask);
     eq_seen += __popcll(eq_mask);
-    if (bm) {
-      if (lane == 0 && 2 * i < n_words) bm[2 * i] = uint32_t(take_mask);
-      if (lane == 1 && 2 * i + 1 < n_words) bm[2 * i + 1] = uint32_t(take_mask >> 32);
-    }
+    if (lane == (2 * i) % 64) bmw[(2 * i) / 64] = uint32_t(take_mask);
+    if (lane == (2 * i + 1) % 64) bmw[(2 * i + 1) / 64] = uint32_t(take_mask >> 32);
+  }
+  if (bm) {
+#pragma unroll
+    for (int r = 0; r < kWordRegs; ++r)
+      if (64 * r + lane < n_words) bm[64 * r + lane] = bmw[r];
   }
   for (int i = k + lane; i < k_max; i += 64) out[i] = -1;
 }
