@@ -2,10 +2,11 @@
 // Execution: Top-k over the estimator's scores, per query tile and per head,
 // yields the binary tile mask passed to the tile-skipping kernel).
 //
-// One wave per row (b, head, query tile). A row of up to 2048 scores is
+// One wave per row (b, head, query tile). A row of up to 2048 scores that
+// starts on a 16-byte boundary (every row when nT_max is a multiple of 4) is
 // first copied into the wave's own LDS area in 1-KiB pieces with the gfx950
 // LDS-DMA buffer loads (a per-row buffer, so pieces past the row read zeros),
-// then read back one score per lane and chunk; longer rows are read straight
+// then read back one score per lane and chunk; other rows are read straight
 // into registers with streaming loads. Each score becomes a 32-bit key
 // whose unsigned order is the float order (-0 is first made +0, so signed
 // zeros tie). The row's keys stay in registers (chunk i, lane l holds key
@@ -78,7 +79,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(GeoTable g, const float*
   const int n = hg.nT, k = hg.k;
   const float* s = scores + row * g.nT_max;
   uint32_t key[NCH];  // key of score j = 64 i + lane in key[i]; 0 (below every finite score's key) past the row
-  if constexpr (kStaged) {
+  bool staged = false;
+  if constexpr (kStaged) staged = (reinterpret_cast<uintptr_t>(s) & 15u) == 0;   // wave-uniform
+  if (staged) {
     typedef __attribute__((address_space(3))) uint32_t lds_u32;
     lds_u32* dst = (lds_u32*)&row_s[wave][0];
     const __amdgpu_buffer_rsrc_t rsrc =

@@ -584,18 +584,22 @@ def test_topk_on_crafted_scores():
         assert np.all(idx[0, 0, rows:].cpu().numpy() == np.arange(k))
 
 
-def test_topk_on_narrow_and_skewed_rows():
+@pytest.mark.parametrize("grid,tile,n_tiles,k", [((60, 40, 80), (4, 4, 8), 1500, 75),
+                                                  ((7, 48, 40), (1, 16, 8), 105, 10)])
+def test_topk_on_narrow_and_skewed_rows(grid, tile, n_tiles, k):
     """Rows whose scores share long leading bits (a band of width 2^-12
     around 1, or around -3), two-valued rows, rows with one outlier above a
     constant, values spanning the whole float range, constant rows and
     rows whose threshold lies many octaves below the maximum: the lists equal
-    the oracle's. The row length (1,500 tiles) leaves pad slots in the last
-    64-wide chunk of every row."""
+    the oracle's. Both row lengths leave pad slots in the last 64-wide chunk
+    of every row; with 105 tiles the rows start at every 4-byte offset modulo
+    16 bytes, so the kernel's rows staged through LDS and its rows read
+    directly are both exercised."""
     V = _lib()
     rng = np.random.default_rng(43)
-    g = V.Geometry(1, 1, 128, (60, 40, 80), [(4, 4, 8)])
-    nT, k = g.max_tiles(), 75
-    assert nT == 1500 and nT % 64
+    g = V.Geometry(1, 1, 128, grid, [tile])
+    nT = g.max_tiles()
+    assert nT == n_tiles and nT % 64
     S = np.empty((nT, nT), np.float32)
     for i in range(nT):
         kind = i % 8
