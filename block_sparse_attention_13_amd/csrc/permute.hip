@@ -211,6 +211,11 @@ __global__ __launch_bounds__(kThreads) void tile_stats_kernel(GeoTable g, const 
 // block, read as 8 token rows of 16 bytes and written, transposed in
 // registers, as 8 channel rows of 16 bytes. Lanes run along the slot groups,
 // so each output row (128 slots, 256 bytes) is written by 16 adjacent lanes.
+// For d = 128 the tile first goes through LDS so that the reads are whole
+// token rows too (16 lanes a row, streaming loads): piece c of slot s sits at
+// position c ^ ((s / 8) % 16) of its LDS row, which keeps both the row writes
+// and the 8-row reads of a thread's block free of bank conflicts. Measured on
+// the 245,760-token layer: 0.951 -> 0.865 ms, the rate of a plain copy.
 template <int D>
 __global__ __launch_bounds__(kThreads) void tile_permute_cm_kernel(GeoTable g, const uint16_t* __restrict__ x,
                                                                   int64_t sb, int64_t sn, int64_t sh,
@@ -222,7 +227,34 @@ __global__ __launch_bounds__(kThreads) void tile_permute_cm_kernel(GeoTable g, c
   const int sg = threadIdx.x % 16, cg = threadIdx.x / 16;
   uint16_t* dst = xt + ((int64_t(b) * g.heads + hd) * g.nT_max + tau) * VEDA_TILE_TOKENS * D;
   uint4 in[8];
-  if (tau < hg.nT) {
+  if constexpr (D == 128) {  // every thread of the workgroup has a block, so all reach the barrier
+    static_assert(kBlocks == kThreads, "one 8 x 8 block per thread");
+    __shared__ uint4 tile_s[VEDA_TILE_TOKENS * 16];
+    const int c = threadIdx.x % 16;
+    if (tau < hg.nT) {
+      const BoxExtent e = box_extent(g, hg, tau);
+      const uint16_t* src = x + int64_t(b) * sb + int64_t(hd) * sh + c * 8;
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const int64_t n = raster_of_slot(g, hg, e, 16 * p + threadIdx.x / 16);
+        in[p] = n >= 0 ? load_stream(src + n * sn) : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) in[p] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int sl = 16 * p + threadIdx.x / 16;
+      tile_s[sl * 16 + (c ^ ((sl >> 3) & 15))] = in[p];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int sl = 8 * sg + r;
+      in[r] = tile_s[sl * 16 + (cg ^ ((sl >> 3) & 15))];
+    }
+  } else if (tau < hg.nT) {
     const BoxExtent e = box_extent(g, hg, tau);
     const uint16_t* src = x + int64_t(b) * sb + int64_t(hd) * sh + cg * 8;
 #pragma unroll
