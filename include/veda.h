@@ -64,7 +64,11 @@
  * Layouts (row-major, contiguous unless a stride is given):
  *   raster x        [B, N, heads, d] bf16 with element strides veda_raster_strides (channel stride 1)
  *   tiled x         [B, heads, nT_max, 128, d] bf16 (token-major), or
- *                   [B, heads, nT_max, d, 128] bf16 (channel-major: each tile transposed)
+ *                   [B, heads, nT_max, d, 128] bf16 (channel-major: each tile transposed).
+ *                   The attention calls take V channel-major: its rows are the rows of V^T, the
+ *                   operand the PV matrix product reads, 8 consecutive keys of one channel per
+ *                   16-byte read. (Token-major V read through the LDS transpose reads measured
+ *                   9% slower.)
  *   stats           [B, heads, nT_max, 3d] bf16, [avg | max | min]
  *   features        [B, heads, nT_max, r] bf16
  *   W_q, W_k        [heads, 3d, r] bf16 (features = stats @ W)
