@@ -4,8 +4,9 @@
 A step is the whole layer on one batch of seeded synthetic input already
 resident in HBM: each tile's TripPool statistics of Q (a read-only pass),
 the tile permute of K with its statistics and of V (stage "prep_qkv");
-head-specific projections and tile scores ("project_score"); head-aware
-Top-k; tile-skipping attention forward, which gathers Q from raster order
+head-specific projections ("project"); tile scores and their head-aware
+Top-k in one pass ("score_topk", no score matrix in HBM); tile-skipping
+attention forward, which gathers Q from raster order
 and writes O back in raster order itself (no tiled Q, no unpermute pass). Default workload: 245,760 tokens (64x48x80
 latents), 40 heads, d = 128, tile (4,4,8) -> 1920 tiles, k = 96 (95% sparse).
 
@@ -45,13 +46,14 @@ def attention_flops(w) -> float:
     return 4.0 * w.d * 128 * 128 * pairs
 
 
-def estimator_flops(w) -> float:
-    """Projections of the Q and K statistics (3d -> r) and the tile scores
-    (nT x nT dot products of length r), 2 flop per multiply-add."""
-    nts = w.tiles_per_head()
-    proj = sum(2 * 2 * n * 3 * w.d * w.r for n in nts)
-    scores = sum(2 * n * n * w.r for n in nts)
-    return float((proj + scores) * w.B)
+def projection_flops(w) -> float:
+    """Projections of the Q and K statistics (3d -> r), 2 flop per multiply-add."""
+    return float(sum(2 * 2 * n * 3 * w.d * w.r for n in w.tiles_per_head()) * w.B)
+
+
+def score_flops(w) -> float:
+    """The tile scores (nT x nT dot products of length r), 2 flop per multiply-add."""
+    return float(sum(2 * n * n * w.r for n in w.tiles_per_head()) * w.B)
 
 
 def device_report() -> dict:
@@ -80,8 +82,8 @@ def layer_floor(w, stage_ms: dict) -> dict:
     roofline fraction: the sum of the floors over the measured time."""
     sb = stage_bytes(w)
     sb["sparse_attn"] = attention_bytes(w)
-    fl = {"prep_qkv": 0.0, "project_score": estimator_flops(w) / PEAK_FP32_VALU_TFLOPS,
-          "topk": 0.0, "sparse_attn": attention_flops(w) / PEAK_BF16_TFLOPS}
+    fl = {"prep_qkv": 0.0, "project": projection_flops(w) / PEAK_FP32_VALU_TFLOPS,
+          "score_topk": score_flops(w) / PEAK_FP32_VALU_TFLOPS, "sparse_attn": attention_flops(w) / PEAK_BF16_TFLOPS}
     floor = {n: max(fl[n] / 1e9, sb[n] / (PEAK_HBM_GBS * 1e6)) for n in fl}   # ms
     total = sum(floor.values())
     return {"floor_ms": {n: round(v, 4) for n, v in floor.items()}, "floor_ms_layer": round(total, 3),
@@ -103,8 +105,8 @@ def stage_bytes(w) -> dict:
     idx = B * Hh * nT * kmax * 4 + B * Hh * nT * ((nT + 31) // 32) * 4
     return {
         "prep_qkv": raster + 2 * (raster + tiled) + 2 * stats,
-        "project_score": 2 * stats + 2 * feats + scores + 2 * Hh * 3 * d * w.r * 2,
-        "topk": scores + idx,
+        "project": 2 * stats + 2 * feats + 2 * Hh * 3 * d * w.r * 2,
+        "score_topk": 2 * feats + idx,     # the scores stay on chip
     }
 
 
@@ -294,7 +296,11 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0, grap
     torch.cuda.synchronize()
     log("[bench] first layer done")
 
-    stages = ["prep_qkv", "project_score", "topk", "sparse_attn"]
+    stages = ["prep_qkv", "project", "score_topk", "sparse_attn"]
+    one_pass = geom.max_tiles() <= V.SCORE_TOPK_MAX_TILES   # else the score matrix goes through HBM
+    if not one_pass:
+        bufs["scores"] = torch.empty((w.B, w.heads, geom.max_tiles(), geom.max_tiles()), dtype=torch.float32,
+                                     device=dev)
 
     def step(ev=None):
         if ev is not None:
@@ -305,10 +311,13 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0, grap
         if ev is not None:
             ev[1].record(stream)
         V.trippool_project_score(bufs["stats_q"], bufs["stats_k"], wq, wk, geom,
-                                 {n: bufs[n] for n in ("feat_q", "feat_k", "scores")})
+                                 {n: bufs.get(n) for n in ("feat_q", "feat_k", "scores")}, with_scores=not one_pass)
         if ev is not None:
             ev[2].record(stream)
-        V.topk_mask(bufs["scores"], geom, ks, idx=bufs["idx"], bitmask=bufs["bitmask"])
+        if one_pass:
+            V.score_topk(bufs["feat_q"], bufs["feat_k"], geom, ks, idx=bufs["idx"], bitmask=bufs["bitmask"])
+        else:
+            V.topk_mask(bufs["scores"], geom, ks, idx=bufs["idx"], bitmask=bufs["bitmask"])
         if ev is not None:
             ev[3].record(stream)
         V.sparse_attn_fwd_raster_io(q, bufs["k_t"], bufs["v_t"], bufs["idx"], geom, ks,
@@ -354,7 +363,7 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0, grap
         del flush
     out["graph_ms_step"] = graph_timed(step, steps) if graph else None
     if keep_data:
-        out["scores_mfma"] = mfma_scores_report(V, geom, ks, bufs, sum(w.tiles_per_head()) * w.B)
+        out["score_routes"] = score_routes_report(V, geom, ks, bufs, wq, wk, sum(w.tiles_per_head()) * w.B)
     out.update({"data": data if keep_data else None, "valid_flops": valid_pair_flops(w, bufs["idx"].cpu().numpy()),
                 "bitmask": bufs["bitmask"] if keep_data else None,
                 "stats": (bufs["stats_q"], bufs["stats_k"]) if keep_data else None})
@@ -366,31 +375,55 @@ def run_workload(V, datagen, w, steps, warmup, keep_data=True, flush_mib=0, grap
     return out
 
 
-def mfma_scores_report(V, geom, ks, bufs, n_rows, reps=10):
-    """The estimator's scores computed on the matrix cores (veda_tile_scores_mfma)
-    from the layer's own features: its time beside the layer's ordered
-    projection-and-scores stage, and how many query tiles' Top-k lists differ
-    from the layer's (near-ties only; the layer keeps the ordered scores)."""
+def _median_ms(fn, reps):
     import numpy as np
     import torch
-    s = torch.empty_like(bufs["scores"])
-    V.tile_scores_mfma(bufs["feat_q"], bufs["feat_k"], geom, out=s)
     ts = []
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        V.tile_scores_mfma(bufs["feat_q"], bufs["feat_k"], geom, out=s)
+        fn()
         e1.record()
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
+    return round(float(np.median(ts)), 4)
+
+
+def score_routes_report(V, geom, ks, bufs, wq, wk, n_rows, reps=10):
+    """The estimator's scoring and Top-k three ways, from the layer's own
+    statistics and features: the two calls (the score matrix written by
+    trippool_project_score, read by topk_mask), the one-pass score_topk the
+    layer runs, and the matrix-core scores (veda_tile_scores_mfma): times,
+    and for the matrix-core scores how many are bit-equal to the ordered
+    ones and how many query tiles' Top-k lists differ from the layer's
+    (near-ties only; the layer keeps the ordered scores)."""
+    import torch
+    est = V.trippool_project_score(bufs["stats_q"], bufs["stats_k"], wq, wk, geom)
+    s_ord = est["scores"]
+    idx2, bm2 = V.topk_mask(s_ord, geom, ks)
+    same_lists = bool(torch.equal(idx2, bufs["idx"])) and bool(torch.equal(bm2.view(torch.int32),
+                                                                           bufs["bitmask"].view(torch.int32)))
+    t_scores = _median_ms(lambda: V.trippool_project_score(bufs["stats_q"], bufs["stats_k"], wq, wk, geom, est), reps)
+    t_proj = _median_ms(lambda: V.trippool_project_score(bufs["stats_q"], bufs["stats_k"], wq, wk, geom,
+                                                         {n: est[n] for n in ("feat_q", "feat_k")},
+                                                         with_scores=False), reps)
+    t_topk = _median_ms(lambda: V.topk_mask(s_ord, geom, ks, idx=idx2, bitmask=bm2), reps)
+    t_one = _median_ms(lambda: V.score_topk(est["feat_q"], est["feat_k"], geom, ks, idx=idx2, bitmask=bm2), reps)
+    s = torch.empty_like(s_ord)
+    t_mfma = _median_ms(lambda: V.tile_scores_mfma(bufs["feat_q"], bufs["feat_k"], geom, out=s), reps)
     idx, _ = V.topk_mask(s, geom, ks, with_bitmask=False)
     differ = int((idx != bufs["idx"]).any(dim=-1).sum().item())
-    same = float((s == bufs["scores"]).float().mean().item())
-    del s, idx
-    res = {"scores_ms_median": round(float(np.median(ts)), 4), "scores_bit_equal_fraction": round(same, 4),
-           "topk_rows_differing": differ, "topk_rows": int(n_rows),
-           "note": "bf16 MFMA scores from the layer's features; the layer keeps the ordered fp32 scores (bit-exact masks)"}
-    log(f"[bench] MFMA scores: {res}")
+    same = float((s == s_ord).float().mean().item())
+    del s, idx, s_ord, idx2, bm2, est
+    res = {"two_calls": {"project_and_scores_ms": t_scores, "topk_ms": t_topk,
+                         "scores_and_topk_ms": round(t_scores - t_proj + t_topk, 4)},
+           "one_pass": {"project_ms": t_proj, "score_topk_ms": t_one},
+           "one_pass_lists_equal_two_calls": same_lists,
+           "mfma_scores": {"scores_ms": t_mfma, "scores_bit_equal_fraction": round(same, 4),
+                           "topk_rows_differing": differ, "topk_rows": int(n_rows)},
+           "note": "scores_and_topk_ms of the two calls: their scores share (project_and_scores minus project) "
+                   "plus topk; the layer runs project then score_topk (bit-identical lists and bitmasks)"}
+    log(f"[bench] scoring routes: {res}")
     return res
 
 
@@ -739,7 +772,7 @@ def main():
         "per_config": per_config,
         "head_shard": shard,
         "dense_reference": dense,
-        "estimator_scores_mfma": r.get("scores_mfma"),
+        "estimator_score_routes": r.get("score_routes"),
         "tile_search": search,
         "distillation": distill,
     }

@@ -12,7 +12,8 @@ Python: the five steps of the layer are HIP kernels.
   sparse_attn_fwd  tiled Q, K, V + index lists -> tiled O (+ LSE)
   tile_unpermute   tiled -> raster
   tile_permute_stats      raster Q or K -> token-major tiles + TripPool stats, one pass
-  trippool_project_score  stats + W_q, W_k -> features, tile scores
+  trippool_project_score  stats + W_q, W_k -> features, tile scores (or the features alone)
+  score_topk       features -> the tile scores and their Top-k in one pass, with no score matrix
   tile_scores_mfma the same scores from the features on the matrix cores (within rounding, not
                    bit-identical; the layer keeps the ordered scores)
   sparse_attn_fwd_raster  sparse_attn_fwd writing raster O (no unpermute pass)
@@ -21,7 +22,7 @@ Python: the five steps of the layer are HIP kernels.
   sparse_attn_fwd_raster_io_noalloc  the same with the library's static work queue: allocates nothing
   attn_queue       workspace of the attention calls' work queue (query tiles handed out at run time)
   layer_forward    the layer: tile_stats of Q, tile_permute_stats of K, tile_permute
-                   of V, trippool_project_score, topk_mask, sparse_attn_fwd_raster_io
+                   of V, trippool_project_score (features), score_topk, sparse_attn_fwd_raster_io
 
 Dense attention (the baseline) and measuring a mask against the method's own target:
   dense_attn_fwd   every key tile kept, no index list (tiled O + LSE; dense_attn_fwd_raster: raster O)
@@ -58,7 +59,7 @@ from . import _lib
 from ._lib import VedaError
 
 __all__ = ["Geometry", "VedaError", "tile_permute", "tile_permute_stats", "tile_unpermute", "trippool_score",
-           "trippool_project_score", "topk_mask", "sparse_attn_fwd_raster", "tile_stats",
+           "trippool_project_score", "topk_mask", "score_topk", "sparse_attn_fwd_raster", "tile_stats",
            "sparse_attn_fwd_raster_io", "sparse_attn_fwd_raster_io_noalloc",
            "sparse_attn_fwd", "attn_queue", "layer_forward",
            "dense_attn_fwd", "dense_attn_fwd_raster", "dense_index", "teacher_tile_max", "avgpool_score", "tile_scores_mfma", "mask_overlap", "tile_recall",
@@ -238,10 +239,13 @@ def trippool_score(q_t: torch.Tensor, k_t: torch.Tensor, w_q: torch.Tensor, w_k:
 
 
 def trippool_project_score(stats_q: torch.Tensor, stats_k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
-                           geom: Geometry, out: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+                           geom: Geometry, out: Optional[Dict[str, torch.Tensor]] = None,
+                           with_scores: bool = True) -> Dict[str, torch.Tensor]:
     """Projections and tile scores from statistics already computed (by
     tile_permute_stats): feat_q, feat_k [B, heads, nT_max, r] bf16 and scores
-    [B, heads, nT_max, nT_max] fp32, as trippool_score."""
+    [B, heads, nT_max, nT_max] fp32, as trippool_score. With `with_scores`
+    false only the features are computed (score_topk takes the mask from
+    them)."""
     d, nT = geom.head_dim, geom.max_tiles()
     B, Hh = geom.B, geom.n_heads
     _need(stats_q, torch.bfloat16, (B, Hh, nT, 3 * d), "stats_q")
@@ -252,20 +256,19 @@ def trippool_project_score(stats_q: torch.Tensor, stats_k: torch.Tensor, w_q: to
     _need(w_q, torch.bfloat16, (Hh, 3 * d, r), "w_q")
     _need(w_k, torch.bfloat16, (Hh, 3 * d, r), "w_k")
     dev = stats_q.device
-    if out is None:
-        out = {
-            "feat_q": torch.empty((B, Hh, nT, r), dtype=torch.bfloat16, device=dev),
-            "feat_k": torch.empty((B, Hh, nT, r), dtype=torch.bfloat16, device=dev),
-            "scores": torch.empty((B, Hh, nT, nT), dtype=torch.float32, device=dev),
-        }
-    for name, shape, dt in (("feat_q", (B, Hh, nT, r), torch.bfloat16), ("feat_k", (B, Hh, nT, r), torch.bfloat16),
-                            ("scores", (B, Hh, nT, nT), torch.float32)):
+    shapes = {"feat_q": ((B, Hh, nT, r), torch.bfloat16), "feat_k": ((B, Hh, nT, r), torch.bfloat16)}
+    if with_scores:
+        shapes["scores"] = ((B, Hh, nT, nT), torch.float32)
+    out = dict(out) if out is not None else {}
+    for name, (shape, dt) in shapes.items():
+        if out.get(name) is None:
+            out[name] = torch.empty(shape, dtype=dt, device=dev)
         _need(out[name], dt, shape, name)
     _lib.check(_lib.lib.veda_trippool_project_score(
         geom.c, stats_q.data_ptr(), stats_k.data_ptr(), w_q.data_ptr(), w_k.data_ptr(), int(r),
-        out["feat_q"].data_ptr(), out["feat_k"].data_ptr(), out["scores"].data_ptr(), _stream(stats_q)),
-        "veda_trippool_project_score")
-    return out
+        out["feat_q"].data_ptr(), out["feat_k"].data_ptr(), out["scores"].data_ptr() if with_scores else None,
+        _stream(stats_q)), "veda_trippool_project_score")
+    return {n: out[n] for n in shapes}
 
 
 def avgpool_score(stats_q: torch.Tensor, stats_k: torch.Tensor, geom: Geometry,
@@ -328,6 +331,41 @@ def topk_mask(scores: torch.Tensor, geom: Geometry, k_per_head: Sequence[int], k
     _lib.check(_lib.lib.veda_topk_mask(geom.c, scores.data_ptr(), _lib.int_array(ks), int(k_max), idx.data_ptr(),
                                        bitmask.data_ptr() if bitmask is not None else None, _stream(scores)),
                "veda_topk_mask")
+    return idx, bitmask
+
+
+SCORE_TOPK_MAX_TILES = 2048   # longest score row score_topk holds on chip
+
+
+def score_topk(feat_q: torch.Tensor, feat_k: torch.Tensor, geom: Geometry, k_per_head: Sequence[int],
+               k_max: Optional[int] = None, with_bitmask: bool = True, idx: Optional[torch.Tensor] = None,
+               bitmask: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Tile scores and head-aware Top-k in one pass, from the projections
+    (no score matrix): the idx and bitmask topk_mask gives for the scores
+    trippool_project_score writes, bit for bit. nT_max <= 2048."""
+    nT = geom.max_tiles()
+    if feat_q.dim() != 4:
+        raise ValueError("feat_q must be [B, heads, nT_max, r]")
+    r = feat_q.shape[3]
+    _need(feat_q, torch.bfloat16, (geom.B, geom.n_heads, nT, r), "feat_q")
+    _need(feat_k, torch.bfloat16, (geom.B, geom.n_heads, nT, r), "feat_k")
+    ks = list(k_per_head)
+    if len(ks) != geom.n_heads:
+        raise ValueError("need one k per head")
+    if k_max is None:
+        k_max = max(ks)
+    dev = feat_q.device
+    if idx is None:
+        idx = torch.empty((geom.B, geom.n_heads, nT, k_max), dtype=torch.int32, device=dev)
+    _need(idx, torch.int32, (geom.B, geom.n_heads, nT, k_max), "idx")
+    if with_bitmask and bitmask is None:
+        bitmask = torch.empty((geom.B, geom.n_heads, nT, (nT + 31) // 32), dtype=torch.uint32, device=dev)
+    if bitmask is not None:
+        _need(bitmask, torch.uint32, (geom.B, geom.n_heads, nT, (nT + 31) // 32), "bitmask")
+    _lib.check(_lib.lib.veda_score_topk(geom.c, feat_q.data_ptr(), feat_k.data_ptr(), int(r), _lib.int_array(ks),
+                                        int(k_max), idx.data_ptr(),
+                                        bitmask.data_ptr() if bitmask is not None else None, _stream(feat_q)),
+               "veda_score_topk")
     return idx, bitmask
 
 
@@ -480,16 +518,20 @@ def sparse_attn_fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, idx
 
 def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
                   geom: Geometry, k_per_head: Sequence[int], scale: Optional[float] = None,
-                  buffers: Optional[Dict[str, torch.Tensor]] = None, tiled_q: bool = False) -> Dict[str, torch.Tensor]:
+                  buffers: Optional[Dict[str, torch.Tensor]] = None, tiled_q: bool = False,
+                  keep_scores: bool = False) -> Dict[str, torch.Tensor]:
     """One Veda attention layer: the TripPool statistics of Q (a read-only
     pass), K permuted with its statistics in the same pass, V permuted,
-    projections and tile scores, Top-k mask, and tile-skipping attention
-    that reads Q and writes O in raster order. `buffers` (from a previous
-    call) reuses every output allocation. Returns all intermediates, `o` and
-    the attention's work-queue workspace `queue`; there is no tiled Q or O
-    (tile_permute, sparse_attn_fwd and tile_unpermute give the same `o`).
-    With `tiled_q` the layer tiles Q as well (output `q_t`) and the attention
-    reads that: the same bytes in every other output."""
+    projections, tile scores and their Top-k mask in one pass, and
+    tile-skipping attention that reads Q and writes O in raster order.
+    `buffers` (from a previous call) reuses every output allocation. Returns
+    all intermediates, `o` and the attention's work-queue workspace `queue`;
+    there is no tiled Q or O (tile_permute, sparse_attn_fwd and
+    tile_unpermute give the same `o`). With `tiled_q` the layer tiles Q as
+    well (output `q_t`) and the attention reads that. With `keep_scores`, or
+    when rows are longer than score_topk holds (SCORE_TOPK_MAX_TILES), the
+    score matrix is written (output `scores`) and topk_mask reads it. Every
+    other output is the same bytes on each route."""
     b = buffers if buffers is not None else {}
     if tiled_q:
         b["q_t"], b["stats_q"] = tile_permute_stats(q, geom, b.get("q_t"), b.get("stats_q"))
@@ -497,10 +539,18 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.
         b["stats_q"] = tile_stats(q, geom, b.get("stats_q"))
     b["k_t"], b["stats_k"] = tile_permute_stats(k, geom, b.get("k_t"), b.get("stats_k"))
     b["v_t"] = tile_permute(v, geom, b.get("v_t"), layout=CHANNEL_MAJOR)
+    fused = not keep_scores and geom.max_tiles() <= SCORE_TOPK_MAX_TILES
+    if fused:
+        b.pop("scores", None)
     est = trippool_project_score(b["stats_q"], b["stats_k"], w_q, w_k, geom,
-                                 {n: b[n] for n in ("feat_q", "feat_k", "scores")} if "scores" in b else None)
+                                 {n: b.get(n) for n in ("feat_q", "feat_k", "scores")}, with_scores=not fused)
     b.update(est)
-    b["idx"], b["bitmask"] = topk_mask(b["scores"], geom, k_per_head, idx=b.get("idx"), bitmask=b.get("bitmask"))
+    if fused:
+        b["idx"], b["bitmask"] = score_topk(b["feat_q"], b["feat_k"], geom, k_per_head, idx=b.get("idx"),
+                                            bitmask=b.get("bitmask"))
+    else:
+        b["idx"], b["bitmask"] = topk_mask(b["scores"], geom, k_per_head, idx=b.get("idx"),
+                                           bitmask=b.get("bitmask"))
     if b.get("queue") is None:
         b["queue"] = attn_queue(q.device)
     if tiled_q:

@@ -30,7 +30,7 @@ EXPORTS = ["veda_status_str", "veda_num_tiles", "veda_max_tiles", "veda_tile_per
            "veda_sparse_attn_fwd_raster", "veda_sparse_attn_fwd_raster_io", "veda_sparse_attn_fwd_raster_io_noalloc",
            "veda_avgpool_score", "veda_tile_recall", "veda_tile_search_select", "veda_k_from_keep",
            "veda_distill_mean_kl", "veda_candidate_tiles", "veda_dense_attn_fwd", "veda_dense_attn_fwd_raster",
-           "veda_tile_scores_mfma"]
+           "veda_tile_scores_mfma", "veda_score_topk"]
 
 
 class VedaGrid(ctypes.Structure):
@@ -83,6 +83,9 @@ def _load():
     lib.veda_avgpool_score.restype = ctypes.c_int
     lib.veda_tile_scores_mfma.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_int32, c_void_p, c_void_p]
     lib.veda_tile_scores_mfma.restype = ctypes.c_int
+    lib.veda_score_topk.argtypes = [POINTER(VedaGeom), c_void_p, c_void_p, c_int32, POINTER(c_int32), c_int32,
+                                    c_void_p, c_void_p, c_void_p]
+    lib.veda_score_topk.restype = ctypes.c_int
     lib.veda_topk_mask.argtypes = [POINTER(VedaGeom), c_void_p, POINTER(c_int32), c_int32, c_void_p, c_void_p,
                                    c_void_p]
     lib.veda_topk_mask.restype = ctypes.c_int

@@ -52,56 +52,19 @@ __device__ __forceinline__ uint32_t count_below(uint64_t mask) {  // set bits of
   return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
 }
 
-template <int NCH>
-__global__ __launch_bounds__(kThreads) void topk_kernel(GeoTable g, const float* __restrict__ scores, int32_t k_max,
-                                                       int32_t* __restrict__ idx, uint32_t* __restrict__ bitmask) {
-  constexpr bool kStaged = NCH <= 32;   // rows of up to 2048 scores go through LDS
-  // Each wave's area is whole 1-KiB pieces: a piece always writes all 64 lanes'
-  // 16 bytes (zeros past the row), so a shorter area would spill into the next.
-  constexpr int kRowWords = kStaged ? (NCH * 64 + 255) / 256 * 256 : 1;
-  __shared__ __attribute__((aligned(16))) uint32_t row_s[kRowsPerBlock][kRowWords];
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const int32_t tq = blockIdx.x * kRowsPerBlock + wave;
-  const int hd = blockIdx.y, b = blockIdx.z;
-  if (tq >= g.nT_max) return;
-  const HeadGeo hg = g.h[hd];
-  const int64_t row = (int64_t(b) * g.heads + hd) * g.nT_max + tq;
-  int32_t* out = idx + row * k_max;
-  const int n_words = (g.nT_max + 31) / 32;
-  uint32_t* bm = bitmask ? bitmask + row * n_words : nullptr;
+// A row with no such query tile for its head: every index -1, no bit set.
+__device__ __forceinline__ void empty_row(int32_t k_max, int n_words, int lane, int32_t* out, uint32_t* bm) {
+  for (int i = lane; i < k_max; i += 64) out[i] = -1;
+  if (bm)
+    for (int i = lane; i < n_words; i += 64) bm[i] = 0u;
+}
 
-  if (tq >= hg.nT) {  // no such query tile for this head
-    for (int i = lane; i < k_max; i += 64) out[i] = -1;
-    if (bm)
-      for (int i = lane; i < n_words; i += 64) bm[i] = 0u;
-    return;
-  }
-  const int n = hg.nT, k = hg.k;
-  const float* s = scores + row * g.nT_max;
-  uint32_t key[NCH];  // key of score j = 64 i + lane in key[i]; 0 (below every finite score's key) past the row
-  bool staged = false;
-  if constexpr (kStaged) staged = (reinterpret_cast<uintptr_t>(s) & 15u) == 0;   // wave-uniform
-  if (staged) {
-    typedef __attribute__((address_space(3))) uint32_t lds_u32;
-    lds_u32* dst = (lds_u32*)&row_s[wave][0];
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(s), 0, n * 4, 0x00020000);
-    const int pieces = (n * 4 + 1023) / 1024;
-    for (int c = 0; c < pieces; ++c)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst + c * 256, 16, 16 * lane, c * 1024, 0, 0);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's pieces have landed (only this wave reads them)
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int j = i * 64 + lane;
-      key[i] = j < n ? order_key(__uint_as_float(row_s[wave][j])) : 0u;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int j = i * 64 + lane;
-      key[i] = j < n ? order_key(__builtin_nontemporal_load(s + j)) : 0u;
-    }
-  }
+// The k largest of one row's keys (key of tile j = 64 i + lane in key[i]; 0,
+// below every finite score's key, past the row): ascending tile indices into
+// out[0..k), -1 in out[k..k_max), and the row's bitmask words when bm is set.
+template <int NCH>
+__device__ __forceinline__ void select_row(const uint32_t (&key)[NCH], int k, int32_t k_max, int n_words, int lane,
+                                           int32_t* out, uint32_t* bm) {
   // Largest t with #{key >= t} >= k: the k-th largest key. The search may
   // stop early at a t with exactly k keys >= t; those k keys are then the
   // k largest, and the selection below keeps exactly them.
@@ -150,6 +113,171 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(GeoTable g, const float*
 }
 
 template <int NCH>
+__global__ __launch_bounds__(kThreads) void topk_kernel(GeoTable g, const float* __restrict__ scores, int32_t k_max,
+                                                       int32_t* __restrict__ idx, uint32_t* __restrict__ bitmask) {
+  constexpr bool kStaged = NCH <= 32;   // rows of up to 2048 scores go through LDS
+  // Each wave's area is whole 1-KiB pieces: a piece always writes all 64 lanes'
+  // 16 bytes (zeros past the row), so a shorter area would spill into the next.
+  constexpr int kRowWords = kStaged ? (NCH * 64 + 255) / 256 * 256 : 1;
+  __shared__ __attribute__((aligned(16))) uint32_t row_s[kRowsPerBlock][kRowWords];
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int32_t tq = blockIdx.x * kRowsPerBlock + wave;
+  const int hd = blockIdx.y, b = blockIdx.z;
+  if (tq >= g.nT_max) return;
+  const HeadGeo hg = g.h[hd];
+  const int64_t row = (int64_t(b) * g.heads + hd) * g.nT_max + tq;
+  int32_t* out = idx + row * k_max;
+  const int n_words = (g.nT_max + 31) / 32;
+  uint32_t* bm = bitmask ? bitmask + row * n_words : nullptr;
+
+  if (tq >= hg.nT) {  // no such query tile for this head
+    empty_row(k_max, n_words, lane, out, bm);
+    return;
+  }
+  const int n = hg.nT;
+  const float* s = scores + row * g.nT_max;
+  uint32_t key[NCH];  // key of score j = 64 i + lane in key[i]; 0 (below every finite score's key) past the row
+  bool staged = false;
+  if constexpr (kStaged) staged = (reinterpret_cast<uintptr_t>(s) & 15u) == 0;   // wave-uniform
+  if (staged) {
+    typedef __attribute__((address_space(3))) uint32_t lds_u32;
+    lds_u32* dst = (lds_u32*)&row_s[wave][0];
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(s), 0, n * 4, 0x00020000);
+    const int pieces = (n * 4 + 1023) / 1024;
+    for (int c = 0; c < pieces; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst + c * 256, 16, 16 * lane, c * 1024, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's pieces have landed (only this wave reads them)
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int j = i * 64 + lane;
+      key[i] = j < n ? order_key(__uint_as_float(row_s[wave][j])) : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int j = i * 64 + lane;
+      key[i] = j < n ? order_key(__builtin_nontemporal_load(s + j)) : 0u;
+    }
+  }
+  select_row<NCH>(key, hg.k, k_max, n_words, lane, out, bm);
+}
+
+constexpr int kStRows = 8;                  // query tiles per workgroup, one wave each in the selection
+constexpr int kStThreads = 64 * kStRows;
+constexpr int kStWavesPerSimd = 4;          // two workgroups per CU (64 KiB of keys each): at most 128 VGPRs
+constexpr int kStFence = 8;                 // channels between scheduling fences (bounds the live LDS reads)
+
+// Scores and Top-k in one pass: the ordered scores of kStRows query tiles
+// against all key tiles of the head go to LDS as order keys, never to HBM,
+// and each wave then selects one row from there. Score (i, j) is the same
+// fp32 chain as the scores kernel's: FMA over the r channels in ascending
+// order from +0, products of bf16 values exact, so the keys, and with them
+// the lists and bitmasks, are the bytes of the two-kernel route.
+// Thread t scores key tiles t, t + kStThreads, ... for all kStRows rows; the
+// rows' features sit in LDS as fp32 [channel][row] and are read as broadcasts.
+template <int R, int NCH>
+__global__ __launch_bounds__(kStThreads, kStWavesPerSimd) void score_topk_kernel(GeoTable g, const uint16_t* __restrict__ feat_q,
+                                                                const uint16_t* __restrict__ feat_k, int32_t k_max,
+                                                                int32_t* __restrict__ idx,
+                                                                uint32_t* __restrict__ bitmask) {
+  __shared__ uint32_t key_s[kStRows][NCH * 64];
+  __shared__ __attribute__((aligned(16))) float fq_s[R][kStRows];
+  const int hd = blockIdx.y, b = blockIdx.z;
+  const HeadGeo hg = g.h[hd];
+  const int n = hg.nT;
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int i0 = blockIdx.x * kStRows;
+  const int64_t head_row = (int64_t(b) * g.heads + hd) * g.nT_max;
+  if (i0 < n) {  // workgroup-uniform
+    for (int e = threadIdx.x; e < kStRows * R; e += kStThreads) {
+      const int r = e % kStRows, c = e / kStRows;
+      fq_s[c][r] = i0 + r < n ? bf16_to_f32(feat_q[(head_row + i0 + r) * R + c]) : 0.0f;
+    }
+    __syncthreads();
+    // A thread's key-tile feature row (R bf16, R / 8 pieces of 16 bytes) is
+    // loaded whole, so its pieces come in back-to-back loads, and the next
+    // row's loads are in flight while this one is scored.
+    constexpr int kPieces = R / 8;
+    const uint16_t* fk_head = feat_k + head_row * R;
+    auto load_row = [&](int j, uint4 (&dst)[kPieces]) {
+#pragma unroll
+      for (int p = 0; p < kPieces; ++p)
+        dst[p] = j < n ? *reinterpret_cast<const uint4*>(fk_head + int64_t(j) * R + 8 * p) : make_uint4(0, 0, 0, 0);
+    };
+    uint4 kw[kPieces], kn[kPieces];
+    load_row(threadIdx.x, kw);
+    for (int j = threadIdx.x; j < n; j += kStThreads) {
+      load_row(j + kStThreads, kn);
+      float acc[kStRows];
+#pragma unroll
+      for (int r = 0; r < kStRows; ++r) acc[r] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < R; ++c) {
+        float qv[kStRows];
+#pragma unroll
+        for (int r4 = 0; r4 < kStRows / 4; ++r4) {
+          const float4 q4 = *reinterpret_cast<const float4*>(&fq_s[c][4 * r4]);
+          qv[4 * r4] = q4.x;
+          qv[4 * r4 + 1] = q4.y;
+          qv[4 * r4 + 2] = q4.z;
+          qv[4 * r4 + 3] = q4.w;
+        }
+        const uint4 pc = kw[c / 8];
+        const int e = c % 8;
+        const uint32_t wd = e / 2 == 0 ? pc.x : e / 2 == 1 ? pc.y : e / 2 == 2 ? pc.z : pc.w;
+        const float kv = __uint_as_float((e & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+#pragma unroll
+        for (int r = 0; r < kStRows; ++r) acc[r] = __builtin_fmaf(qv[r], kv, acc[r]);
+        if (c % kStFence == kStFence - 1) __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int r = 0; r < kStRows; ++r) key_s[r][j] = order_key(acc[r]);
+#pragma unroll
+      for (int p = 0; p < kPieces; ++p) kw[p] = kn[p];
+    }
+    __syncthreads();
+  }
+  const int32_t tq = i0 + wave;
+  if (tq >= g.nT_max) return;
+  const int64_t row = head_row + tq;
+  int32_t* out = idx + row * k_max;
+  const int n_words = (g.nT_max + 31) / 32;
+  uint32_t* bm = bitmask ? bitmask + row * n_words : nullptr;
+  if (tq >= n) {
+    empty_row(k_max, n_words, lane, out, bm);
+    return;
+  }
+  uint32_t key[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int j = i * 64 + lane;
+    key[i] = j < n ? key_s[wave][j] : 0u;
+  }
+  select_row<NCH>(key, hg.k, k_max, n_words, lane, out, bm);
+}
+
+template <int R, int NCH>
+hipError_t launch_st(const GeoTable& g, const uint16_t* feat_q, const uint16_t* feat_k, int32_t k_max, int32_t* idx,
+                     uint32_t* bitmask, hipStream_t s) {
+  const dim3 grid((g.nT_max + kStRows - 1) / kStRows, g.heads, g.B);
+  score_topk_kernel<R, NCH><<<grid, kStThreads, 0, s>>>(g, feat_q, feat_k, k_max, idx, bitmask);
+  return hipGetLastError();
+}
+
+template <int R>
+hipError_t launch_st_r(const GeoTable& g, const uint16_t* feat_q, const uint16_t* feat_k, int32_t k_max, int32_t* idx,
+                       uint32_t* bitmask, hipStream_t s) {
+  const int chunks = (g.nT_max + 63) / 64;
+  if (chunks <= 1) return launch_st<R, 1>(g, feat_q, feat_k, k_max, idx, bitmask, s);
+  if (chunks <= 2) return launch_st<R, 2>(g, feat_q, feat_k, k_max, idx, bitmask, s);
+  if (chunks <= 4) return launch_st<R, 4>(g, feat_q, feat_k, k_max, idx, bitmask, s);
+  if (chunks <= 8) return launch_st<R, 8>(g, feat_q, feat_k, k_max, idx, bitmask, s);
+  if (chunks <= 16) return launch_st<R, 16>(g, feat_q, feat_k, k_max, idx, bitmask, s);
+  return launch_st<R, 32>(g, feat_q, feat_k, k_max, idx, bitmask, s);
+}
+
+template <int NCH>
 hipError_t launch_nch(const GeoTable& g, const float* scores, int32_t k_max, int32_t* idx, uint32_t* bitmask,
                       hipStream_t s) {
   const dim3 grid((g.nT_max + kRowsPerBlock - 1) / kRowsPerBlock, g.heads, g.B);
@@ -170,6 +298,13 @@ hipError_t launch_topk(const GeoTable& g, const float* scores, int32_t k_max, in
   if (chunks <= 32) return launch_nch<32>(g, scores, k_max, idx, bitmask, s);
   if (chunks <= 64) return launch_nch<64>(g, scores, k_max, idx, bitmask, s);
   return launch_nch<128>(g, scores, k_max, idx, bitmask, s);
+}
+
+hipError_t launch_score_topk(const GeoTable& g, const uint16_t* feat_q, const uint16_t* feat_k, int32_t r,
+                             int32_t k_max, int32_t* idx, uint32_t* bitmask, hipStream_t s) {
+  if (g.nT_max > kScoreTopkMaxTiles) return hipErrorInvalidValue;
+  return r == 64 ? launch_st_r<64>(g, feat_q, feat_k, k_max, idx, bitmask, s)
+                 : launch_st_r<32>(g, feat_q, feat_k, k_max, idx, bitmask, s);
 }
 
 }  // namespace veda

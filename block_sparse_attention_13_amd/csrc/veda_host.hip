@@ -212,17 +212,19 @@ int veda_trippool_project_score(const veda_geom* g, const void* stats_q, const v
                                 void* stream) {
   GeoTable t;
   VEDA_TRY(build_table(g, &t));
-  if (!stats_q || !stats_k || !w_q || !w_k || !feat_q || !feat_k || !scores) return VEDA_ERR_NULL;
+  if (!stats_q || !stats_k || !w_q || !w_k || !feat_q || !feat_k) return VEDA_ERR_NULL;
   if (rank != 32 && rank != 64) return VEDA_ERR_SHAPE;
   for (const void* p : {stats_q, stats_k, w_q, w_k, static_cast<const void*>(feat_q),
-                        static_cast<const void*>(feat_k), static_cast<const void*>(scores)})
+                        static_cast<const void*>(feat_k)})
     if (!aligned16(p)) return VEDA_ERR_ALIGN;
+  if (scores && !aligned16(scores)) return VEDA_ERR_ALIGN;
   VEDA_TRY(check_device());
   const hipStream_t st = static_cast<hipStream_t>(stream);
   VEDA_TRY(launched(veda::launch_trippool_project(
       t, static_cast<const uint16_t*>(stats_q), static_cast<const uint16_t*>(stats_k),
       static_cast<const uint16_t*>(w_q), static_cast<const uint16_t*>(w_k), rank, static_cast<uint16_t*>(feat_q),
       static_cast<uint16_t*>(feat_k), st)));
+  if (!scores) return VEDA_OK;  // features only (the fused score + Top-k call takes them from here)
   return launched(veda::launch_tile_scores(t, static_cast<const uint16_t*>(feat_q),
                                            static_cast<const uint16_t*>(feat_k), rank, scores, st));
 }
@@ -262,6 +264,22 @@ int veda_topk_mask(const veda_geom* g, const float* scores, const int32_t* k_per
   if (!aligned16(scores) || !aligned16(idx) || (bitmask && !aligned16(bitmask))) return VEDA_ERR_ALIGN;
   VEDA_TRY(check_device());
   return launched(veda::launch_topk(t, scores, k_max, idx, bitmask, static_cast<hipStream_t>(stream)));
+}
+
+int veda_score_topk(const veda_geom* g, const void* feat_q, const void* feat_k, int32_t rank,
+                    const int32_t* k_per_head, int32_t k_max, int32_t* idx, uint32_t* bitmask, void* stream) {
+  GeoTable t;
+  VEDA_TRY(build_table(g, &t));
+  if (!feat_q || !feat_k || !idx) return VEDA_ERR_NULL;
+  if (rank != 32 && rank != 64) return VEDA_ERR_SHAPE;
+  if (t.nT_max > veda::kScoreTopkMaxTiles) return VEDA_ERR_SHAPE;
+  VEDA_TRY(set_k(k_per_head, k_max, &t));
+  if (!aligned16(feat_q) || !aligned16(feat_k) || !aligned16(idx) || (bitmask && !aligned16(bitmask)))
+    return VEDA_ERR_ALIGN;
+  VEDA_TRY(check_device());
+  return launched(veda::launch_score_topk(t, static_cast<const uint16_t*>(feat_q),
+                                          static_cast<const uint16_t*>(feat_k), rank, k_max, idx, bitmask,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int veda_sparse_attn_fwd(const veda_geom* g, const void* q_tiled, const void* k_tiled, const void* v_tiled,

@@ -134,6 +134,9 @@ hipError_t launch_tile_scores_mfma(const GeoTable& g, const uint16_t* feat_q, co
                                    float* scores, hipStream_t s);
 hipError_t launch_avgpool_scores(const GeoTable& g, const uint16_t* stats_q, const uint16_t* stats_k, float* scores,
                                  hipStream_t s);
+constexpr int kScoreTopkMaxTiles = 2048;   // key tiles per row the fused score + Top-k pass holds in LDS
+hipError_t launch_score_topk(const GeoTable& g, const uint16_t* feat_q, const uint16_t* feat_k, int32_t r,
+                             int32_t k_max, int32_t* idx, uint32_t* bitmask, hipStream_t s);
 hipError_t launch_topk(const GeoTable& g, const float* scores, int32_t k_max, int32_t* idx, uint32_t* bitmask,
                        hipStream_t s);
 hipError_t launch_teacher(const GeoTable& g, const uint16_t* q_t, const uint16_t* k_t, const float* lse, float scale,

@@ -14,6 +14,7 @@
  * The same layer in fewer passes over HBM, with identical results:
  *   veda_tile_permute_stats    x2  raster Q/K -> tiles and each tile's TripPool stats in one pass
  *   veda_trippool_project_score    stats -> head-specific projections -> tile scores
+ *   veda_score_topk            tile scores and Top-k in one pass, from the projections (no score matrix)
  *   veda_sparse_attn_fwd_raster    attention that writes raster O itself (no unpermute pass)
  *   (with veda_tile_permute of V and veda_topk_mask in between)
  * and with Q never tiled: veda_tile_permute_stats of Q with no tiled output (statistics
@@ -210,7 +211,9 @@ int veda_trippool_score(const veda_geom* g, const void* q_tiled, const void* k_t
  *   w_q, w_k          in   bf16 [heads, 3d, rank]
  *   rank              in   r: 32 or 64 (else VEDA_ERR_SHAPE)
  *   feat_q, feat_k    out  bf16 [B, heads, nT_max, rank], as veda_trippool_score
- *   scores            out  fp32 [B, heads, nT_max, nT_max], as veda_trippool_score
+ *   scores            out  fp32 [B, heads, nT_max, nT_max], as veda_trippool_score; may be NULL,
+ *                          and then only the features are computed (veda_score_topk takes the
+ *                          mask from them without a score matrix)
  * Given the statistics veda_trippool_score would compute, the outputs are
  * identical to its outputs, bit for bit.
  */
@@ -264,6 +267,22 @@ int veda_avgpool_score(const veda_geom* g, const void* stats_q, const void* stat
  */
 int veda_topk_mask(const veda_geom* g, const float* scores, const int32_t* k_per_head,
                    int32_t k_max, int32_t* idx, uint32_t* bitmask, void* stream);
+
+/*
+ * Tile scores and head-aware Top-k in one pass (Veda page, "Attention Structure Distillation",
+ * Estimator and Execution: the projections' products score the tile pairs, and Top-k per query
+ * tile of those scores is the tile mask). The scores of a group of query tiles are held on chip
+ * and selected there; no score matrix is written or read.
+ *   feat_q, feat_k    in   bf16 [B, heads, nT_max, rank], as veda_trippool_project_score writes them
+ *   rank              in   32 or 64 (else VEDA_ERR_SHAPE)
+ *   k_per_head, k_max, idx, bitmask   as veda_topk_mask
+ * The scores are those veda_trippool_project_score writes (fp32 FMA over the channels in ascending
+ * order from +0), so idx and bitmask are, bit for bit, what veda_topk_mask makes of them.
+ * nT_max must not exceed 2048 (else VEDA_ERR_SHAPE; use the two calls).
+ */
+int veda_score_topk(const veda_geom* g, const void* feat_q, const void* feat_k, int32_t rank,
+                    const int32_t* k_per_head, int32_t k_max, int32_t* idx, uint32_t* bitmask,
+                    void* stream);
 
 /*
  * Tile-skipping attention forward (Veda page, "Attention Structure

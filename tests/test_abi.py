@@ -21,7 +21,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     from block_sparse_attention_13_amd import _lib
     declared = _declared_functions()
-    assert len(declared) == 28, declared
+    assert len(declared) == 29, declared
     assert sorted(_lib.EXPORTS) == declared
     for name in declared:
         assert hasattr(_lib.lib, name), name
@@ -108,6 +108,16 @@ def test_call_errors_precede_any_device_work():
     assert L.veda_topk_mask(g.c, FAKE, _lib.int_array([5]), 4, FAKE, None, None) == -4
     assert L.veda_topk_mask(g.c, FAKE, None, 4, FAKE, None, None) == -1
     assert L.veda_topk_mask(g.c, FAKE, ks, 4, FAKE, FAKE + 4, None) == -5
+    st = L.veda_score_topk
+    assert st(g.c, FAKE, FAKE, 48, ks, 4, FAKE, None, None) == -2
+    assert st(g.c, FAKE, None, 64, ks, 4, FAKE, None, None) == -1
+    assert st(g.c, FAKE, FAKE, 64, ks, 4, None, None, None) == -1
+    assert st(g.c, FAKE, FAKE, 64, _lib.int_array([9]), 9, FAKE, None, None) == -4
+    assert st(g.c, FAKE, FAKE, 64, None, 4, FAKE, None, None) == -1
+    assert st(g.c, FAKE + 8, FAKE, 64, ks, 4, FAKE, None, None) == -5
+    assert st(g.c, FAKE, FAKE, 64, ks, 4, FAKE, FAKE + 4, None) == -5
+    # rows longer than the fused pass holds on chip (here 2,112 key tiles; at most 2,048) need the two calls
+    assert st(_geom(grid=(16, 64, 264)).c, FAKE, FAKE, 64, ks, 4, FAKE, None, None) == -2
     assert L.veda_sparse_attn_fwd(g.c, FAKE, FAKE, FAKE, FAKE, _lib.int_array([9]), 8, 0.0, FAKE, None, None,
                                   None) == -4
     assert L.veda_sparse_attn_fwd(g.c, FAKE, None, FAKE, FAKE, ks, 4, 0.0, FAKE, None, None, None) == -1

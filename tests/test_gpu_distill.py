@@ -37,7 +37,7 @@ def _setup(w):
     data = datagen.generate(w)
     g = geometry(w)
     q, k, v, wq, wk = (to_dev_bf16(data[n]) for n in ("q", "k", "v", "wq", "wk"))
-    out = V.layer_forward(q, k, v, wq, wk, g, w.k_per_head(), tiled_q=True)
+    out = V.layer_forward(q, k, v, wq, wk, g, w.k_per_head(), tiled_q=True, keep_scores=True)
     idx_d, ks_d = V.dense_index(g, q.device)
     _, lse = V.sparse_attn_fwd(out["q_t"], out["k_t"], out["v_t"], idx_d, g, ks_d)
     T = V.teacher_tile_max(out["q_t"], out["k_t"], lse, g)

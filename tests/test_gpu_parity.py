@@ -26,13 +26,13 @@ def _lib():
     return V
 
 
-def run_layer(w, data, k_per_head=None, buffers=None, tiled_q=False):
+def run_layer(w, data, k_per_head=None, buffers=None, tiled_q=False, keep_scores=False):
     V = _lib()
     geom = geometry(w)
     ks = k_per_head or w.k_per_head()
     q, k, v = (to_dev_bf16(data[n]) for n in ("q", "k", "v"))
     wq, wk = to_dev_bf16(data["wq"]), to_dev_bf16(data["wk"])
-    out = V.layer_forward(q, k, v, wq, wk, geom, ks, buffers=buffers, tiled_q=tiled_q)
+    out = V.layer_forward(q, k, v, wq, wk, geom, ks, buffers=buffers, tiled_q=tiled_q, keep_scores=keep_scores)
     torch.cuda.synchronize()
     return geom, out, (q, k, v, wq, wk)
 
@@ -48,6 +48,16 @@ def _sample_tiles(nT, count, seed):
     fixed = [0, 1, nT // 2, nT - 2, nT - 1]
     extra = rng.choice(nT, size=min(nT, count), replace=False).tolist()
     return sorted(set(t for t in fixed + extra if 0 <= t < nT))
+
+
+def _layer_scores(out, data, geom):
+    """The layer's tile scores: written by the layer (keep_scores, or rows
+    too long for the one-pass call), else recomputed from its statistics by
+    trippool_project_score, whose scores the one-pass Top-k selects from."""
+    if "scores" in out:
+        return out["scores"]
+    wq, wk = to_dev_bf16(data["wq"]), to_dev_bf16(data["wk"])
+    return _lib().trippool_project_score(out["stats_q"], out["stats_k"], wq, wk, geom)["scores"]
 
 
 def check_head(w, data, out, hd, ks, tiles, b=0, check_attention=True):
@@ -68,7 +78,7 @@ def check_head(w, data, out, hd, ks, tiles, b=0, check_attention=True):
         got = bits_of(out[name][b, hd])
         assert np.array_equal(got[:nT], O.float_to_bf16_bits(r[name])), (name, hd)
         assert not got[nT:].any(), (name, hd)
-    S = out["scores"][b, hd].cpu().numpy()
+    S = _layer_scores(out, data, geometry(w))[b, hd].cpu().numpy()
     assert np.array_equal(S[:nT, :nT].view(np.uint32), r["scores"].view(np.uint32)), ("scores", hd)
     assert np.all(np.isneginf(S[nT:, :])) and np.all(np.isneginf(S[:, nT:])), ("scores pad", hd)
     idx = out["idx"][b, hd].cpu().numpy()
@@ -181,7 +191,7 @@ def test_estimator_is_deterministic():
     V = _lib()
     w = W["480p"]
     data = datagen.generate(w)
-    geom, out, (q, k, v, wq, wk) = run_layer(w, data)
+    geom, out, (q, k, v, wq, wk) = run_layer(w, data, keep_scores=True)
     first = out["scores"].clone()
     q_t = V.tile_permute(q, geom)
     for _ in range(2):
@@ -245,9 +255,11 @@ def test_fused_layer_matches_unfused(wname, heads, B, custom):
     data = datagen.generate(w)
     geom, out, (q, k, v, wq, wk) = run_layer(w, data)
     _, out_t, _ = run_layer(w, data, tiled_q=True)
-    assert "q_t" not in out
-    for name in ("k_t", "v_t", "stats_q", "stats_k", "feat_q", "feat_k", "scores", "idx", "bitmask", "lse", "o"):
-        assert torch.equal(out[name].contiguous().view(torch.uint8), out_t[name].contiguous().view(torch.uint8)), name
+    _, out_s, _ = run_layer(w, data, keep_scores=True)   # scores written, then topk_mask
+    assert "q_t" not in out and "scores" not in out and "scores" in out_s
+    for name in ("k_t", "v_t", "stats_q", "stats_k", "feat_q", "feat_k", "idx", "bitmask", "lse", "o"):
+        for other in (out_t, out_s):
+            assert torch.equal(out[name].contiguous().view(torch.uint8), other[name].contiguous().view(torch.uint8)), name
     q_t, k_t = V.tile_permute(q, geom), V.tile_permute(k, geom)
     two = V.trippool_score(q_t, k_t, wq, wk, geom)
     torch.cuda.synchronize()
@@ -255,14 +267,15 @@ def test_fused_layer_matches_unfused(wname, heads, B, custom):
     assert torch.equal(out["k_t"].view(torch.int16), k_t.view(torch.int16))
     for name in ("stats_q", "stats_k", "feat_q", "feat_k"):
         assert torch.equal(out[name].view(torch.int16), two[name].view(torch.int16)), name
-    assert torch.equal(out["scores"].view(torch.int32), two["scores"].view(torch.int32))
+    assert torch.equal(out_s["scores"].view(torch.int32), two["scores"].view(torch.int32))
     ks = w.k_per_head()
-    idx, _ = V.topk_mask(two["scores"], geom, ks)
+    idx, bm = V.topk_mask(two["scores"], geom, ks)
     v_t = V.tile_permute(v, geom, layout=V.CHANNEL_MAJOR)
     o_t, lse = V.sparse_attn_fwd(q_t, k_t, v_t, idx, geom, ks)
     o = V.tile_unpermute(o_t, geom)
     torch.cuda.synchronize()
     assert torch.equal(out["idx"], idx)
+    assert torch.equal(out["bitmask"].view(torch.int32), bm.view(torch.int32))
     assert torch.equal(out["o"].view(torch.int16), o.view(torch.int16))
     real = torch.zeros(lse.shape, dtype=torch.bool, device=lse.device)
     for hd, tile in enumerate(w.head_tiles()):
@@ -550,7 +563,7 @@ def test_equal_scores_keep_the_lower_tile():
             data["k"][0, sel[np.argsort(pos[sel])], hd, :] = src[order0]
     ks = [2, 2]
     geom, out, _ = run_layer(w, data, k_per_head=ks)
-    S = out["scores"].cpu().numpy()
+    S = _layer_scores(out, data, geom).cpu().numpy()
     assert np.array_equal(S[0, 0, :, 0], S[0, 0, :, 3]) and np.array_equal(S[0, 0, :, 0], S[0, 0, :, 6])
     for hd in range(2):
         check_head(w, data, out, hd, ks, list(range(8)))
@@ -774,10 +787,15 @@ def test_outputs_stay_in_their_buffers(tiled_q):
     V.teacher_tile_max(q_t, out["k_t"], out["lse"], geom, out=teacher); checks.append(("teacher", b6))
     st, b7 = _guarded(shapes["stats_q"][0], torch.bfloat16)
     V.tile_stats(q, geom, st); checks.append(("tile_stats", b7))
+    i2, b8 = _guarded(*shapes["idx"])
+    m2, b9 = _guarded(*shapes["bitmask"])
+    V.topk_mask(est["scores"], geom, w.k_per_head(), idx=i2, bitmask=m2.view(torch.uint32))
+    checks += [("topk_mask idx", b8), ("topk_mask bitmask", b9)]
     torch.cuda.synchronize()
     for name, buf in checks:
         assert _guards_intact(buf), name
     assert torch.equal(o.view(torch.int16), out["o"].view(torch.int16))
+    assert torch.equal(i2, out["idx"]) and torch.equal(m2.view(torch.int32), out["bitmask"].view(torch.int32))
 
 
 def test_layer_replays_in_a_graph():
