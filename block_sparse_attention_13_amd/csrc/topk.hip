@@ -165,8 +165,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(GeoTable g, const float*
 
 constexpr int kStRows = 8;                  // query tiles per workgroup, one wave each in the selection
 constexpr int kStThreads = 64 * kStRows;
+constexpr int kStCols = 2;                  // key tiles a thread scores at once (each query read serves both)
 constexpr int kStWavesPerSimd = 4;          // two workgroups per CU (64 KiB of keys each): at most 128 VGPRs
-constexpr int kStFence = 8;                 // channels between scheduling fences (bounds the live LDS reads)
 
 // Scores and Top-k in one pass: the ordered scores of kStRows query tiles
 // against all key tiles of the head go to LDS as order keys, never to HBM,
@@ -174,14 +174,21 @@ constexpr int kStFence = 8;                 // channels between scheduling fence
 // fp32 chain as the scores kernel's: FMA over the r channels in ascending
 // order from +0, products of bf16 values exact, so the keys, and with them
 // the lists and bitmasks, are the bytes of the two-kernel route.
-// Thread t scores key tiles t, t + kStThreads, ... for all kStRows rows; the
-// rows' features sit in LDS as fp32 [channel][row] and are read as broadcasts.
+// Thread t scores key tiles t + kStThreads * (kStCols m + u), u < kStCols,
+// for all kStRows rows at once: the rows' features sit in LDS as fp32
+// [channel][row], and each 16-byte broadcast read of four rows' values feeds
+// 4 kStCols FMAs. The code avoids two things the compiler would otherwise
+// do with it: the query reads take an offset the compiler cannot see is 0,
+// so they are not hoisted out of the column loop (64 x 8 live values), and a
+// column past the row still stores its keys (to a spare word past the row),
+// so no branch sinks its FMA chain below the loop and keeps the query values
+// live until then.
 template <int R, int NCH>
-__global__ __launch_bounds__(kStThreads, kStWavesPerSimd) void score_topk_kernel(GeoTable g, const uint16_t* __restrict__ feat_q,
-                                                                const uint16_t* __restrict__ feat_k, int32_t k_max,
-                                                                int32_t* __restrict__ idx,
-                                                                uint32_t* __restrict__ bitmask) {
-  __shared__ uint32_t key_s[kStRows][NCH * 64];
+__global__ __launch_bounds__(kStThreads, kStWavesPerSimd) void score_topk_kernel(
+    GeoTable g, const uint16_t* __restrict__ feat_q, const uint16_t* __restrict__ feat_k, int32_t k_max,
+    int32_t* __restrict__ idx, uint32_t* __restrict__ bitmask) {
+  constexpr int kRowWords = NCH * 64;
+  __shared__ uint32_t key_s[kStRows][kRowWords + 1];   // word kRowWords: the spare
   __shared__ __attribute__((aligned(16))) float fq_s[R][kStRows];
   const int hd = blockIdx.y, b = blockIdx.z;
   const HeadGeo hg = g.h[hd];
@@ -195,46 +202,59 @@ __global__ __launch_bounds__(kStThreads, kStWavesPerSimd) void score_topk_kernel
       fq_s[c][r] = i0 + r < n ? bf16_to_f32(feat_q[(head_row + i0 + r) * R + c]) : 0.0f;
     }
     __syncthreads();
-    // A thread's key-tile feature row (R bf16, R / 8 pieces of 16 bytes) is
-    // loaded whole, so its pieces come in back-to-back loads, and the next
-    // row's loads are in flight while this one is scored.
+    // A key tile's feature row (R bf16, R / 8 pieces of 16 bytes) is loaded
+    // whole, in back-to-back loads; a column past the row loads the last
+    // row's features (a valid address) and its keys go to the spare word.
     constexpr int kPieces = R / 8;
     const uint16_t* fk_head = feat_k + head_row * R;
-    auto load_row = [&](int j, uint4 (&dst)[kPieces]) {
+    const float4* fq4 = reinterpret_cast<const float4*>(&fq_s[0][0]);
+    for (int jb = threadIdx.x; jb < n; jb += kStThreads * kStCols) {
+      int32_t hidden_zero;
+      asm volatile("s_mov_b32 %0, 0" : "=s"(hidden_zero));
+      uint4 kw[kStCols][kPieces];
 #pragma unroll
-      for (int p = 0; p < kPieces; ++p)
-        dst[p] = j < n ? *reinterpret_cast<const uint4*>(fk_head + int64_t(j) * R + 8 * p) : make_uint4(0, 0, 0, 0);
-    };
-    uint4 kw[kPieces], kn[kPieces];
-    load_row(threadIdx.x, kw);
-    for (int j = threadIdx.x; j < n; j += kStThreads) {
-      load_row(j + kStThreads, kn);
-      float acc[kStRows];
+      for (int u = 0; u < kStCols; ++u) {
+        const int64_t j = min(jb + u * kStThreads, n - 1);
 #pragma unroll
-      for (int r = 0; r < kStRows; ++r) acc[r] = 0.0f;
+        for (int p = 0; p < kPieces; ++p) kw[u][p] = *reinterpret_cast<const uint4*>(fk_head + j * R + 8 * p);
+      }
+      float acc[kStCols][kStRows];
 #pragma unroll
-      for (int c = 0; c < R; ++c) {
-        float qv[kStRows];
+      for (int u = 0; u < kStCols; ++u)
 #pragma unroll
-        for (int r4 = 0; r4 < kStRows / 4; ++r4) {
-          const float4 q4 = *reinterpret_cast<const float4*>(&fq_s[c][4 * r4]);
-          qv[4 * r4] = q4.x;
-          qv[4 * r4 + 1] = q4.y;
-          qv[4 * r4 + 2] = q4.z;
-          qv[4 * r4 + 3] = q4.w;
+        for (int r = 0; r < kStRows; ++r) acc[u][r] = 0.0f;
+#pragma unroll
+      for (int cb = 0; cb < kPieces; ++cb) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = 8 * cb + e;
+          float qv[kStRows];
+#pragma unroll
+          for (int r4 = 0; r4 < kStRows / 4; ++r4) {
+            const float4 q4 = fq4[hidden_zero + (c * kStRows + 4 * r4) / 4];
+            qv[4 * r4] = q4.x;
+            qv[4 * r4 + 1] = q4.y;
+            qv[4 * r4 + 2] = q4.z;
+            qv[4 * r4 + 3] = q4.w;
+          }
+#pragma unroll
+          for (int u = 0; u < kStCols; ++u) {
+            const uint4 pc = kw[u][cb];
+            const uint32_t wd = e / 2 == 0 ? pc.x : e / 2 == 1 ? pc.y : e / 2 == 2 ? pc.z : pc.w;
+            const float kv = __uint_as_float((e & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+#pragma unroll
+            for (int r = 0; r < kStRows; ++r) acc[u][r] = __builtin_fmaf(qv[r], kv, acc[u][r]);
+          }
         }
-        const uint4 pc = kw[c / 8];
-        const int e = c % 8;
-        const uint32_t wd = e / 2 == 0 ? pc.x : e / 2 == 1 ? pc.y : e / 2 == 2 ? pc.z : pc.w;
-        const float kv = __uint_as_float((e & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
-#pragma unroll
-        for (int r = 0; r < kStRows; ++r) acc[r] = __builtin_fmaf(qv[r], kv, acc[r]);
-        if (c % kStFence == kStFence - 1) __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);   // one 8-channel group at a time
       }
 #pragma unroll
-      for (int r = 0; r < kStRows; ++r) key_s[r][j] = order_key(acc[r]);
+      for (int u = 0; u < kStCols; ++u) {
+        const int j = jb + u * kStThreads;
+        const int js = j < n ? j : kRowWords;
 #pragma unroll
-      for (int p = 0; p < kPieces; ++p) kw[p] = kn[p];
+        for (int r = 0; r < kStRows; ++r) key_s[r][js] = order_key(acc[u][r]);
+      }
     }
     __syncthreads();
   }
