@@ -18,6 +18,11 @@
 // chunk's two bitmask words go into one lane each of a register, and the
 // row's words are stored together at the end, instead of one single-lane store
 // per word.
+//
+// score_topk_kernel runs the same selection on scores it computes itself
+// from the estimator's features (Estimator: the products of the head-specific
+// projections score each tile pair) and holds in LDS, so no score matrix goes
+// through HBM.
 #include "veda_internal.hpp"
 
 namespace veda {

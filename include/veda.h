@@ -13,10 +13,11 @@
  *
  * The same layer in fewer passes over HBM, with identical results:
  *   veda_tile_permute_stats    x2  raster Q/K -> tiles and each tile's TripPool stats in one pass
- *   veda_trippool_project_score    stats -> head-specific projections -> tile scores
- *   veda_score_topk            tile scores and Top-k in one pass, from the projections (no score matrix)
+ *   veda_trippool_project_score    stats -> head-specific projections (-> tile scores)
+ *   veda_score_topk            tile scores and Top-k in one pass, from the projections (no score
+ *                              matrix; or veda_topk_mask of the scores the call above writes)
  *   veda_sparse_attn_fwd_raster    attention that writes raster O itself (no unpermute pass)
- *   (with veda_tile_permute of V and veda_topk_mask in between)
+ *   (with veda_tile_permute of V in between)
  * and with Q never tiled: veda_tile_permute_stats of Q with no tiled output (statistics
  * only), then veda_sparse_attn_fwd_raster_io, which also reads Q in raster order.
  *
