@@ -35,7 +35,10 @@ gives the same bytes on every call, whatever the thread count.
 
 Random streams: numpy PCG64 seeded by SeedSequence([seed, tensor_id, b, hd])
 for tensor_id 0/1/2 = Q/K/V; [seed, 99, hd] for A_hd; [seed, 100, hd] and
-[seed, 101, hd] for W_q and W_k.
+[seed, 101, hd] for W_q and W_k. A workload with `noise_seed` set draws the
+noise from [noise_seed, tensor_id, b, hd] instead (the field, amplitudes and
+weights keep `seed`): the same positional structure with other content, the
+held-out sample of the distillation report.
 """
 
 from __future__ import annotations
@@ -66,6 +69,7 @@ class Workload:
     amp_uniform: bool                               # A_hd ~ U(0.5, 2) instead of 1
     seed: int
     description: str
+    noise_seed: Optional[int] = None                # noise from its own stream (the field keeps `seed`)
 
     @property
     def tokens(self) -> int:
@@ -156,6 +160,8 @@ def _fill_head(out: np.ndarray, w: Workload, tensor_id: int, b: int, hd: int,
     arg = pos[:, 0:1] * kf[:, 0] + pos[:, 1:2] * kf[:, 1] + pos[:, 2:3] * kf[:, 2]   # [N, 8]
     c = amp * np.cos(2.0 * math.pi * arg + phi)
     field = np.einsum("nf,fd->nd", c, a, optimize=False)                         # [N, d] float64
+    if w.noise_seed is not None:
+        rng = _rng(w.noise_seed, tensor_id, b, hd)
     noise = rng.standard_normal((pos.shape[0], w.d), dtype=np.float32)
     out[b, :, hd, :] = to_bf16_bits(field.astype(np.float32) + noise)
 
