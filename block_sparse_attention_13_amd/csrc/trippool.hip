@@ -148,11 +148,14 @@ __global__ __launch_bounds__(kThreads) void trippool_features_kernel(
 
 // Projections alone, from statistics already in HBM (written by the permute
 // that computes them on the fly). r/8 lanes share a tile; each owns 8 of its
-// r outputs and keeps their sums in registers, so 8 FMA chains run side by
-// side in every lane. All lanes walk the 3d channels in the same ascending
-// order and read their 16 bytes of W row c from LDS (the lanes of a wave
-// read one contiguous row, free of bank conflicts). Each sum still takes one
-// channel at a time in ascending order from +0, exactly as project_tile.
+// r outputs for kProjTiles tiles (kLaneSlots apart) and keeps their sums in
+// registers, so 8 kProjTiles FMA chains run side by side in every lane. All
+// lanes walk the 3d channels in the same ascending order and read their 16
+// bytes of W row c from LDS (the lanes of a wave read one contiguous row,
+// free of bank conflicts); each W value is converted from bf16 once and
+// serves all the lane's tiles. Each sum still takes one channel at a time in
+// ascending order from +0, exactly as project_tile.
+constexpr int kProjTiles = 4;   // tiles per lane: each W value, converted once, feeds kProjTiles FMAs
 template <int D, int R>
 __global__ __launch_bounds__(kThreads) void trippool_project_kernel(
     GeoTable g, const uint16_t* __restrict__ stats_q, const uint16_t* __restrict__ stats_k,
@@ -160,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void trippool_project_kernel(
     uint16_t* __restrict__ feat_k) {
   constexpr int C = 3 * D;
   constexpr int kGroups = R / 8;                     // lanes per tile
-  constexpr int kTilesPerBlock = kThreads / kGroups;
+  constexpr int kLaneSlots = kThreads / kGroups;     // tile slots per workgroup pass
   __shared__ __attribute__((aligned(16))) uint16_t w_s[C * R];
 
   const int hd = blockIdx.y;
@@ -178,37 +181,52 @@ __global__ __launch_bounds__(kThreads) void trippool_project_kernel(
   __syncthreads();
 
   const int grp = threadIdx.x % kGroups;
-  const int32_t tau = blockIdx.x * kTilesPerBlock + threadIdx.x / kGroups;
-  const bool real = tau < hg.nT;
-  // Lanes past the head's tiles read tile 0's statistics (in bounds) and
-  // store zeros.
   const int64_t head_row = (int64_t(b) * g.heads + hd) * g.nT_max;
-  const uint4* st = reinterpret_cast<const uint4*>(stats + (head_row + (real ? tau : 0)) * C);
-  const uint16_t* wcol = w_s + 8 * grp;
-  float acc[8];
+  int32_t tau[kProjTiles];
+  const uint4* st[kProjTiles];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int t = 0; t < kProjTiles; ++t) {
+    tau[t] = (blockIdx.x * kProjTiles + t) * kLaneSlots + threadIdx.x / kGroups;
+    st[t] = reinterpret_cast<const uint4*>(stats + (head_row + (tau[t] < hg.nT ? tau[t] : 0)) * C);
+  }
+  const uint16_t* wcol = w_s + 8 * grp;
+  float acc[kProjTiles][8];
+#pragma unroll
+  for (int t = 0; t < kProjTiles; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[t][e] = 0.0f;
   for (int c8 = 0; c8 < C / 8; ++c8) {
-    const uint4 sv = st[c8];
-    const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+    uint32_t sw[kProjTiles][4];
+#pragma unroll
+    for (int t = 0; t < kProjTiles; ++t) {
+      const uint4 sv = st[t][c8];
+      sw[t][0] = sv.x; sw[t][1] = sv.y; sw[t][2] = sv.z; sw[t][3] = sv.w;
+    }
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
-      const float x = __uint_as_float((cc & 1) ? (sw[cc / 2] & 0xFFFF0000u) : (sw[cc / 2] << 16));
       const uint4 wv = *reinterpret_cast<const uint4*>(wcol + (c8 * 8 + cc) * R);
       const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+      float wf[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float wf = __uint_as_float((e & 1) ? (ww[e / 2] & 0xFFFF0000u) : (ww[e / 2] << 16));
-        acc[e] = __builtin_fmaf(x, wf, acc[e]);
+      for (int e = 0; e < 8; ++e) wf[e] = __uint_as_float((e & 1) ? (ww[e / 2] & 0xFFFF0000u) : (ww[e / 2] << 16));
+#pragma unroll
+      for (int t = 0; t < kProjTiles; ++t) {
+        const float x = __uint_as_float((cc & 1) ? (sw[t][cc / 2] & 0xFFFF0000u) : (sw[t][cc / 2] << 16));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[t][e] = __builtin_fmaf(x, wf[e], acc[t][e]);
       }
     }
   }
-  if (tau >= g.nT_max) return;
-  uint32_t o[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    o[e] = real ? (uint32_t(f32_to_bf16_rne(acc[2 * e])) | (uint32_t(f32_to_bf16_rne(acc[2 * e + 1])) << 16)) : 0u;
-  *reinterpret_cast<uint4*>(feat + (head_row + tau) * R + 8 * grp) = make_uint4(o[0], o[1], o[2], o[3]);
+  for (int t = 0; t < kProjTiles; ++t) {
+    if (tau[t] >= g.nT_max) continue;
+    const bool real = tau[t] < hg.nT;
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = real ? (uint32_t(f32_to_bf16_rne(acc[t][2 * e])) | (uint32_t(f32_to_bf16_rne(acc[t][2 * e + 1])) << 16)) : 0u;
+    *reinterpret_cast<uint4*>(feat + (head_row + tau[t]) * R + 8 * grp) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
 }
 
 constexpr int kScoreTile = 128;   // scores per workgroup: 128 x 128, 8 x 8 per thread
@@ -362,7 +380,7 @@ hipError_t launch_trippool_features(const GeoTable& g, const uint16_t* q_t, cons
 hipError_t launch_trippool_project(const GeoTable& g, const uint16_t* stats_q, const uint16_t* stats_k,
                                    const uint16_t* wq, const uint16_t* wk, int32_t r, uint16_t* feat_q,
                                    uint16_t* feat_k, hipStream_t s) {
-  const int tiles_per_block = kThreads / (r / 8);
+  const int tiles_per_block = kThreads / (r / 8) * kProjTiles;
   const dim3 grid((g.nT_max + tiles_per_block - 1) / tiles_per_block, g.heads, 2 * g.B);
   if (g.d == 128 && r == 64)
     trippool_project_kernel<128, 64><<<grid, kThreads, 0, s>>>(g, stats_q, stats_k, wq, wk, feat_q, feat_k);
