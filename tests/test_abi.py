@@ -173,6 +173,9 @@ def test_valid_call_without_gpu_reports_device_error():
     assert _lib.lib.veda_tile_permute(g.c, FAKE, s, FAKE, _lib.VEDA_TILED_CHANNEL_MAJOR, None) == -6
     assert _lib.lib.veda_tile_permute_stats(g.c, FAKE, s, FAKE, FAKE, None) == -6
     assert _lib.lib.veda_trippool_project_score(g.c, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, None) == -6
+    # features only (no score matrix) is a valid call too
+    assert _lib.lib.veda_trippool_project_score(g.c, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, None, None) == -6
+    assert _lib.lib.veda_score_topk(g.c, FAKE, FAKE, 64, _lib.int_array([3]), 4, FAKE, FAKE, None) == -6
     assert _lib.lib.veda_sparse_attn_fwd_raster(g.c, FAKE, FAKE, FAKE, FAKE, _lib.int_array([3]), 4, 0.0, FAKE, s,
                                                 None, FAKE, None) == -6
 
@@ -183,3 +186,8 @@ def test_python_wrappers_validate_before_calling():
     g = _geom()
     with pytest.raises(ValueError):
         V.tile_permute(torch.zeros(1, 1024, 1, 128, dtype=torch.bfloat16), g)   # not a device tensor
+    f = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        V.score_topk(f, f, g, [3])                                               # not device tensors
+    with pytest.raises(ValueError):
+        V.score_topk(f[0], f[0], g, [3])                                         # not [B, heads, nT_max, r]
