@@ -124,7 +124,7 @@ def test_score_topk_longest_rows_and_beyond():
     assert bool((idx == 7).all())
 
 
-@pytest.mark.parametrize("name,heads,B", [("hc", 6, 2), ("long", 3, 1)])
+@pytest.mark.parametrize("name,heads,B", [("hc", 6, 2), ("long", 40, 1)])   # long: the benchmarked layer, every head
 def test_score_topk_equals_two_call_route(name, heads, B):
     """On the layer's own features, the one-pass call and the two calls
     (scores written by trippool_project_score, then topk_mask) give the
