@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+ATTN_TARGET_FRAC = 0.5          # aim: the sparse attention sustains half the bf16 MFMA peak on the selected tiles
 PEAK_FP32_VALU_TFLOPS = 157.3   # MI355X fp32 vector FMA (256 CUs x 2.4 GHz x 256 flop/clk)
 HIP_ATTR_CLOCK_KHZ = 5          # hipDeviceAttributeClockRate in the ROCm 7 HIP headers
 
@@ -753,6 +754,9 @@ def main():
                    "tiles_per_head": max(w.tiles_per_head()), "k": max(w.k_per_head()), "rank": w.r},
         "attn_tflops": round(achieved, 1),
         "attn_frac_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "attn_target": {"frac_bf16_peak_at_least": ATTN_TARGET_FRAC,
+                        "attn_ms_at_most": round(f_attn / (ATTN_TARGET_FRAC * PEAK_BF16_TFLOPS * 1e12) * 1e3, 2),
+                        "met": bool(achieved / PEAK_BF16_TFLOPS >= ATTN_TARGET_FRAC)},
         "ms_per_layer_median": round(r["ms_step_median"], 3),
         "ms_per_layer_min": round(r["ms_step_min"], 3),
         "ms_per_layer_graph": r["graph_ms_step"],
