@@ -67,3 +67,27 @@ def test_candidate_tiles_enumerate_the_budget():
         assert V.candidate_tiles(grid) == sorted(want), grid
     small = (_lib.VedaTile * 2)()
     assert _lib.lib.veda_candidate_tiles(_lib.VedaGrid(21, 45, 80), small, 2) == -2
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for more it exits with status 2 and a
+    message, before it touches a device."""
+    import sys
+    root = os.path.dirname(HERE)
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=300, cwd=root)
+    assert r.returncode == 2, (r.returncode, r.stderr[-500:])
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_bench_attention_target_is_half_the_peak_at_the_long_layer():
+    """The bench line's attention target: half the bf16 peak over the long
+    layer's 7,372,800 tile pairs, i.e. 49.48 ms."""
+    import sys
+    sys.path.insert(0, os.path.dirname(HERE))
+    import bench
+    import datagen
+    w = datagen.WORKLOADS["long"]
+    assert bench.attention_flops(w) == 4.0 * 128 * 128 * 128 * 1920 * 96 * 40
+    ms = bench.attention_flops(w) / (bench.ATTN_TARGET_FRAC * bench.PEAK_BF16_TFLOPS * 1e12) * 1e3
+    assert abs(ms - 49.48) < 0.01
